@@ -1,0 +1,266 @@
+"""Plain float64 implementation of 1.5-entmax and 1.5-entmax attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and obvious on
+purpose: one (batch, head) at a time, dense score matrices, numpy sort.
+
+Notation follows "ADASPLASH -- ROBERTA Benchmark Result", section 2:
+s is a row of scores, p = [(s - tau)/2]_+^2, g(tau) = sum_j p_j, tau the
+unique root of g(tau) = 1.
+"""
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Allowed-key sets (masking)
+# ---------------------------------------------------------------------------
+
+def allowed_mask(L, key_mask_row=None, causal=False, window=0):
+    """Boolean [L, L] matrix: entry (i, j) is True when query i may attend key j.
+
+    Follows "ADASPLASH -- ROBERTA Benchmark Result", section 3 (padding mask,
+    then causal tril for decoders, then the splash window for decoders), read
+    as follows:
+
+    * padding: key j is allowed only if key_mask_row[j] != 0 (padded keys are
+      removed from the simplex rather than filled with a large negative value);
+    * causal: j <= i;
+    * window W > 0 (decoders only, so it requires causal): i - W < j <= i,
+      i.e. W keys including the query itself.
+    """
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    ok = np.ones((L, L), dtype=bool)
+    if key_mask_row is not None:
+        ok &= (np.asarray(key_mask_row) != 0)[None, :]
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        if not causal:
+            raise ValueError("the splash window is only defined for causal attention")
+        ok &= j > i - window
+    return ok
+
+
+# ---------------------------------------------------------------------------
+# 1.5-entmax on rows
+# ---------------------------------------------------------------------------
+
+def entmax15_exact(s, allowed=None):
+    """Exact 1.5-entmax of each row of ``s`` over its allowed entries.
+
+    Theorem 1 ("ADASPLASH -- ROBERTA Benchmark Result", section 2.2): the
+    solution is p_j = ((s_j - tau)/2)^2 for s_j > tau and 0 otherwise, with
+    tau the unique value where the p sum to 1.  On a support made of the k
+    largest entries z_1 >= ... >= z_k this is sum_{i<=k} (z_i - tau)^2 = 4,
+    i.e. (mean_k - tau)^2 = 4/k - var_k, and the root below the mean is
+    tau_k = mean_k - sqrt(4/k - var_k).  The support is the largest k whose
+    tau_k exists and lies below z_k (KKT conditions of the same theorem).
+
+    Returns (p, tau).  Rows with no allowed entry get p = 0 and tau = +inf.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    squeeze = s.ndim == 1
+    s = np.atleast_2d(s)
+    R, N = s.shape
+    if allowed is None:
+        allowed = np.ones_like(s, dtype=bool)
+    allowed = np.broadcast_to(np.atleast_2d(np.asarray(allowed, dtype=bool)), s.shape)
+    if not np.all(np.isfinite(s[allowed])):
+        raise ValueError("scores must be finite")
+
+    n = allowed.sum(axis=1)
+    z = np.where(allowed, s, -np.inf)
+    z = -np.sort(-z, axis=1)                       # descending, disallowed last
+    top = np.where(n > 0, z[:, 0], 0.0)
+    k = np.arange(1, N + 1, dtype=np.float64)[None, :]
+    in_row = k <= n[:, None]
+    y = np.where(in_row, z - top[:, None], 0.0)    # shifted: largest is 0
+    mean = np.cumsum(y, axis=1) / k
+    var = np.maximum(np.cumsum(y * y, axis=1) / k - mean * mean, 0.0)
+    delta = 4.0 / k - var
+    tau_k = mean - np.sqrt(np.maximum(delta, 0.0))
+    ok = in_row & (delta >= 0.0) & (y > tau_k)
+    # largest admissible k (k = 1 is always admissible for a non-empty row)
+    kstar = np.where(ok.any(axis=1), N - 1 - np.argmax(ok[:, ::-1], axis=1), -1)
+
+    tau = np.full(R, np.inf)
+    has = n > 0
+    tau[has] = top[has] + tau_k[has, kstar[has]]
+
+    above = allowed & (s > tau[:, None])
+    p = np.where(above, ((s - tau[:, None]) / 2.0) ** 2, 0.0)
+
+    # KKT consistency: the support found equals {j : s_j > tau}
+    supp = above.sum(axis=1)
+    bad = has & (supp != kstar + 1)
+    if np.any(bad):
+        # ties exactly at tau may only shrink the strict support
+        if np.any(supp[bad] > kstar[bad] + 1):
+            raise AssertionError("support search inconsistent with KKT conditions")
+    if squeeze:
+        return p[0], tau[0]
+    return p, tau
+
+
+def entmax15_bisect(s, allowed=None, n_iter=25):
+    """1.5-entmax by bisection on g(tau) = sum_j [(s_j - tau)/2]_+^2.
+
+    Theorem 2 ("ADASPLASH -- ROBERTA Benchmark Result", section 2.3): g is
+    strictly decreasing where positive, so bisection converges.  Bracket from
+    "DistilBERT SST-2 with AdaSplash Attention", Mathematical Formulation 2:
+    [max - 2, max - 2/sqrt(n)] with n the number of allowed entries.  Update
+    rule: if g(mid) > 1 the root lies above mid (lo = mid), else hi = mid; the
+    answer is the midpoint of the final bracket.  No renormalisation.
+
+    Independent of ``entmax15_exact``: used by the tests to pin it.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    squeeze = s.ndim == 1
+    s = np.atleast_2d(s)
+    if allowed is None:
+        allowed = np.ones_like(s, dtype=bool)
+    allowed = np.broadcast_to(np.atleast_2d(np.asarray(allowed, dtype=bool)), s.shape)
+    n = allowed.sum(axis=1)
+    m = np.where(allowed, s, -np.inf).max(axis=1)
+    has = n > 0
+    m = np.where(has, m, 0.0)
+    lo = m - 2.0
+    hi = m - 2.0 / np.sqrt(np.maximum(n, 1))
+
+    def g(t):
+        d = np.where(allowed, np.maximum((s - t[:, None]) / 2.0, 0.0), 0.0)
+        return (d * d).sum(axis=1)
+
+    for _ in range(n_iter):
+        mid = 0.5 * (lo + hi)
+        up = g(mid) > 1.0
+        lo = np.where(up, mid, lo)
+        hi = np.where(up, hi, mid)
+    tau = 0.5 * (lo + hi)
+    tau = np.where(has, tau, np.inf)
+    p = np.where(allowed & (s > tau[:, None]), ((s - tau[:, None]) / 2.0) ** 2, 0.0)
+    if squeeze:
+        return p[0], tau[0]
+    return p, tau
+
+
+def tsallis15_objective(p, s):
+    """p.s + H_1.5(p), with H_1.5(p) = (4/3) sum (p - p^1.5).
+
+    "ADASPLASH -- ROBERTA Benchmark Result", section 2.1 (H_alpha with
+    alpha = 1.5, so 1/(alpha(alpha-1)) = 4/3); 1.5-entmax is its maximiser
+    over the simplex.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    return float(p @ s + (4.0 / 3.0) * np.sum(p - p ** 1.5))
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _as64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):            # torch tensor: exact upcast on the CPU
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _key_mask_row(key_mask, b):
+    if key_mask is None:
+        return None
+    km = key_mask
+    if hasattr(km, "detach"):
+        km = km.detach().to("cpu").numpy()
+    return np.asarray(km)[b]
+
+
+def _head_list(B, H, heads):
+    if heads is None:
+        return [(b, h) for b in range(B) for h in range(H)]
+    return [tuple(x) for x in heads]
+
+
+def attention_forward(q, k, v, key_mask=None, causal=False, window=0,
+                      heads=None, rows=None, return_probs=False):
+    """1.5-entmax attention forward for the selected (b, h) heads.
+
+    Scores s_ij = (q_i . k_j) / sqrt(d) ("ADASPLASH -- ROBERTA Benchmark
+    Result", sections 3-4: logits = q k^T * d^-1/2; the model cards write /8
+    for d = 64).  Row i takes 1.5-entmax over its allowed keys
+    (``allowed_mask``), and O_i = sum_j A_ij V_j ("RoBERTa Base with AdaSplash
+    Attention", Architecture Overview).
+
+    Arguments: q, k, v [B, H, L, d] (numpy or torch, any float dtype: upcast
+    exactly to float64), key_mask [B, L] (nonzero = valid key) or None.
+    ``rows`` optionally restricts the query rows computed (same for every
+    head).  Returns a dict with 'out' [nh, r, d], 'tau' [nh, r] and, when
+    asked, 'probs' [nh, r, L]; 'heads' lists the (b, h) pairs in order.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    hl = _head_list(B, H, heads)
+    r_idx = np.arange(L) if rows is None else np.asarray(rows)
+    outs, taus, probs = [], [], []
+    for (b, h) in hl:
+        ok = allowed_mask(L, _key_mask_row(key_mask, b), causal, window)[r_idx]
+        s = (q[b, h, r_idx] @ k[b, h].T) * scale
+        p, tau = entmax15_exact(s, ok)
+        outs.append(p @ v[b, h])
+        taus.append(tau)
+        if return_probs:
+            probs.append(p)
+    res = {"out": np.stack(outs), "tau": np.stack(taus), "heads": hl, "rows": r_idx}
+    if return_probs:
+        res["probs"] = np.stack(probs)
+    return res
+
+
+def attention_backward(q, k, v, dout, key_mask=None, causal=False, window=0,
+                       heads=None, row_chunk=1024):
+    """Gradients of 1.5-entmax attention w.r.t. q, k and v.
+
+    Jacobian from "ADASPLASH -- ROBERTA Benchmark Result", section 2.4 (also
+    "RoBERTa Base with AdaSplash Attention", Mathematical Formulation 2):
+    for a row with p = entmax15(s) and incoming gradient g = dL/dp,
+        dL/ds_j = sqrt(p_j) * (g_j - sum_k sqrt(p_k) g_k / sum_k sqrt(p_k)),
+    which is zero off the support.  With O = A V: dL/dA = dO V^T, dV = A^T dO,
+    and through s = q k^T / sqrt(d): dq = dS k / sqrt(d), dk = dS^T q / sqrt(d).
+
+    Rows are processed in chunks of ``row_chunk`` to bound memory; the sums
+    over rows for dk and dv are plain accumulations.  Returns a dict with
+    'dq', 'dk', 'dv' [nh, L, d] and 'heads'.
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, L, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    hl = _head_list(B, H, heads)
+    dqs, dks, dvs = [], [], []
+    for (b, h) in hl:
+        kmr = _key_mask_row(key_mask, b)
+        dq = np.zeros((L, d))
+        dk = np.zeros((L, d))
+        dv = np.zeros((L, d))
+        for r0 in range(0, L, row_chunk):
+            r = np.arange(r0, min(L, r0 + row_chunk))
+            ok = allowed_mask(L, kmr, causal, window)[r]
+            s = (q[b, h, r] @ k[b, h].T) * scale
+            p, _ = entmax15_exact(s, ok)
+            w = np.sqrt(p)                                  # sqrt(p), 0 off support
+            gp = dout[b, h, r] @ v[b, h].T                  # dL/dA
+            den = w.sum(axis=1, keepdims=True)
+            c = np.where(den > 0, (w * gp).sum(axis=1, keepdims=True) / np.where(den > 0, den, 1.0), 0.0)
+            ds = w * (gp - c)
+            dq[r] = (ds @ k[b, h]) * scale
+            dk += (ds.T @ q[b, h, r]) * scale
+            dv += p.T @ dout[b, h, r]
+        dqs.append(dq)
+        dks.append(dk)
+        dvs.append(dv)
+    return {"dq": np.stack(dqs), "dk": np.stack(dks), "dv": np.stack(dvs), "heads": hl}
