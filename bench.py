@@ -1,0 +1,263 @@
+"""Throughput of 1.5-entmax attention on one MI355X, against its roofline.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole path over one batch of synthetic input:
+the forward (scores, masks, row max, tau by bisection, P, O = P V) for the
+forward workloads, forward + backward for ``longctx``.  Inputs are already
+resident in HBM when the timed region starts; the timed steps rotate over
+enough copies of the input/output buffers (> 256 MB in total) that no step is
+served from the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``value`` is effective TFLOP/s: 4 d FLOPs per allowed
+(query, key) pair for the forward (two products of d multiply-adds; zeros of
+A count as done), plus 6 d per pair for the backward.  ``roofline`` reports
+the dominant kernel: its algorithmic bytes (HBM-bound workloads) or
+algorithmic MFMA FLOPs (MFMA-bound ones) per launch over its average launch
+time, measured with HIP events on the launch stream inside the timed region.
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "1.5-entmax attn fwd: effective TFLOP/s + % MFMA/HBM roofline, L=128..8192"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+MFMA_F32_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 * 2 ** 20
+
+BOUND = {"tiny": "hbm", "encoder": "hbm", "long": "mfma", "decoder": "hbm", "longctx": "mfma"}
+
+
+def allowed_pairs_per_head(w, key_mask):
+    """Number of allowed (query, key) pairs for each batch entry (list)."""
+    import numpy as np
+    L = w.L
+    if key_mask is not None:
+        lens = key_mask.sum(dim=1).tolist()
+        return [L * int(n) for n in lens]
+    if w.causal and w.window > 0:
+        i = np.arange(L)
+        n = int(np.minimum(i + 1, w.window).sum())
+    elif w.causal:
+        n = L * (L + 1) // 2
+    else:
+        n = L * L
+    return [n] * w.B
+
+
+def algorithmic_bytes(w, key_mask):
+    """HBM bytes one forward launch must move at least: Q, K and V rows that
+    some query may attend (valid keys only), O (fp32), tau (fp32), mask."""
+    esz = 4 if w.dtype == "f32" else 2
+    row = w.d * esz
+    q = w.B * w.H * w.L * row
+    if key_mask is not None:
+        kv_rows = int(key_mask.sum().item()) * w.H
+    else:
+        kv_rows = w.B * w.H * w.L
+    o = w.B * w.H * w.L * w.d * 4
+    tau = w.B * w.H * w.L * 4
+    mask = 0 if key_mask is None else w.B * w.L
+    return q + 2 * kv_rows * row + o + tau + mask
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from entmax_amd.workloads import WORKLOADS, make_inputs
+    from oracle import attention_backward, attention_forward
+
+    w = WORKLOADS[name]
+    inp = make_inputs(name)
+    pairs = allowed_pairs_per_head(w, inp["key_mask"])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    flop_per_pair = 4 * w.d + (6 * w.d if w.backward else 0)
+    done_flop = 0.0
+    n_heads = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            b, h = heads[n_heads % len(heads)]
+            attention_forward(inp["q"], inp["k"], inp["v"], inp["key_mask"], w.causal, w.window, heads=[(b, h)])
+            if w.backward:
+                attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], inp["key_mask"], w.causal,
+                                   w.window, heads=[(b, h)])
+            done_flop += flop_per_pair * pairs[b]
+            n_heads += 1
+            if time.perf_counter() - t0 > budget_s and n_heads >= 1:
+                break
+    dt = time.perf_counter() - t0
+    return {
+        "value": done_flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n_heads} (batch, head) slices of the {name} workload "
+                  f"({'forward+backward' if w.backward else 'forward'}, float64 numpy, one thread), "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="encoder",
+                    choices=["tiny", "encoder", "long", "decoder", "longctx"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): every (batch, head) is independent, "
+              "so the path shards by heads with no communication; run it once per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    # The CPU baseline runs first, before anything touches the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
+
+    import torch
+    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd
+    from entmax_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    km_cpu = inp["key_mask"]
+    pairs = sum(allowed_pairs_per_head(w, km_cpu)) * w.H
+    fwd_flop = 4.0 * w.d * pairs
+    bwd_flop = 6.0 * w.d * pairs if w.backward else 0.0
+
+    # rotating buffer sets, > 256 MB in total
+    esz = 4 if w.dtype == "f32" else 2
+    n_el = w.B * w.H * w.L * w.d
+    set_bytes = n_el * (3 * esz + 4) + w.B * w.H * w.L * 4
+    if w.backward:
+        set_bytes += n_el * (esz + 12)
+    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for _ in range(nsets):
+        s = {x: inp[x].to(dev) for x in ("q", "k", "v")}
+        s["key_mask"] = None if km_cpu is None else km_cpu.to(dev)
+        s["out"] = torch.empty((w.B, w.H, w.L, w.d), dtype=torch.float32, device=dev)
+        s["tau"] = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+        if w.backward:
+            s["dout"] = inp["dout"].to(dev)
+            s["grads"] = [torch.empty((w.B, w.H, w.L, w.d), dtype=torch.float32, device=dev) for _ in range(3)]
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        entmax_attn_fwd(s["q"], s["k"], s["v"], s["key_mask"], w.causal, w.window, out=s["out"], tau_out=s["tau"])
+        if ev is not None:
+            ev[1].record()
+        if w.backward:
+            if ev is not None:
+                ev[2].record()
+            entmax_attn_bwd(s["q"], s["k"], s["v"], s["tau"], s["dout"], s["key_mask"], w.causal, w.window,
+                            dq=s["grads"][0], dk=s["grads"][1], dv=s["grads"][2])
+            if ev is not None:
+                ev[3].record()
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # nonzeros of A (outside the timed region), for the algorithmic FLOPs
+    nnz = None
+    if BOUND[args.workload] == "mfma":
+        from entmax_amd import entmax_attn_probs
+        s0 = sets[0]
+        nnz = 0
+        hb = max(1, (2 ** 31) // (w.L * w.L * 4))      # heads per probs call (<= 2 GiB)
+        for h0 in range(0, w.H, hb):
+            sl = slice(h0, min(w.H, h0 + hb))
+            q_, k_ = s0["q"][:, sl].contiguous(), s0["k"][:, sl].contiguous()
+            t_ = s0["tau"][:, sl].contiguous()
+            pr = entmax_attn_probs(q_, k_, t_, s0["key_mask"], w.causal, w.window)
+            nnz += int((pr > 0).sum().item())
+            del pr
+        torch.cuda.synchronize()
+
+    nev = 4 if w.backward else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps if w.backward else 0.0
+
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel
+    bound = BOUND[args.workload]
+    if bound == "hbm":
+        bytes_per_launch = algorithmic_bytes(w, km_cpu)
+        achieved = bytes_per_launch / (fwd_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "fwd", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_per_launch,
+                "launch_ms": fwd_ms}
+    else:
+        peak = MFMA_F32_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        if w.backward and bwd_ms > fwd_ms:
+            # S recomputed for every allowed pair; dP, dQ, dK, dV on the support
+            kname, kms = "bwd", bwd_ms
+            flop = 2.0 * w.d * pairs + 8.0 * w.d * nnz
+        else:
+            # Q K^T for every allowed pair; P V on the support
+            kname, kms = "fwd", fwd_ms
+            flop = 2.0 * w.d * pairs + 2.0 * w.d * nnz
+        achieved = flop / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "flop_per_launch": flop, "launch_ms": kms}
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "causal": w.causal,
+                   "window": w.window, "padding": w.padding, "backward": w.backward,
+                   "allowed_pairs": pairs, "buffer_sets": nsets,
+                   "zero_fraction": None if nnz is None else 1.0 - nnz / pairs},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if w.backward:
+        res["fwd_ms"] = fwd_ms
+        res["bwd_ms"] = bwd_ms
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""1.5-entmax (AdaSplash-style) attention on MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``libentmax_attn.so`` (``include/entmax_attn.h``); this package is the thin
+Python binding plus the seeded input generators.  Build with
+``__graft_entry__.build()`` (or ``python -m entmax_amd.build``).
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    EntmaxError,
+    entmax_attn_bwd,
+    entmax_attn_fwd,
+    entmax_attn_probs,
+    load_library,
+)

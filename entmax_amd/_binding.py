@@ -1,0 +1,168 @@
+"""ctypes binding of libentmax_attn.so: argument marshalling only.
+
+Every function here checks shapes, dtypes and devices, allocates outputs
+with torch when the caller gives none, and calls the C ABI declared in
+``include/entmax_attn.h`` with raw device pointers and torch's current HIP
+stream.  No step of the computation runs in Python, and there is no CPU
+fallback: without the built library every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_NAME = "libentmax_attn.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+ENTMAX_F32 = 0
+ENTMAX_BF16 = 1
+
+EXPORTS = (
+    "entmax_attn_fwd",
+    "entmax_attn_bwd",
+    "entmax_attn_probs",
+    "entmax_attn_status_string",
+    "entmax_attn_last_error",
+    "entmax_attn_version",
+)
+
+_lib = None
+
+
+class EntmaxError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, code, message):
+        super().__init__(message)
+        self.code = code
+
+
+def load_library(path=LIB_PATH):
+    """Load the shared library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{LIB_NAME} is not built ({path}); run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    vp, i32, u8p, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_fwd.restype = i32
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_bwd.restype = i32
+    lib.entmax_attn_probs.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_probs.restype = i32
+    lib.entmax_attn_status_string.argtypes = [i32]
+    lib.entmax_attn_status_string.restype = ctypes.c_char_p
+    lib.entmax_attn_last_error.argtypes = []
+    lib.entmax_attn_last_error.restype = ctypes.c_char_p
+    lib.entmax_attn_version.argtypes = []
+    lib.entmax_attn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(lib, rc):
+    if rc != 0:
+        status = lib.entmax_attn_status_string(rc).decode()
+        msg = lib.entmax_attn_last_error().decode()
+        raise EntmaxError(rc, f"{status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ENTMAX_F32
+    if t.dtype == torch.bfloat16:
+        return ENTMAX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_qkv(q, k, v=None):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    for name, t in (("k", k), ("v", v)):
+        if t is None:
+            continue
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    for t in (q, k, v):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("q, k, v must be contiguous GPU tensors")
+
+
+def _check_mask(key_mask, q):
+    if key_mask is None:
+        return None
+    B, _, L, _ = q.shape
+    if key_mask.shape != (B, L) or key_mask.dtype != torch.uint8 or key_mask.device != q.device:
+        raise ValueError("key_mask must be a [B, L] uint8 tensor on q's device")
+    return key_mask.contiguous()
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, tau_out=None, want_tau=True):
+    """O = entmax_1.5(Q K^T / sqrt(d)) V and the row thresholds tau.
+
+    Returns (out [B, H, L, d] float32, tau [B, H, L] float32 or None).
+    """
+    lib = load_library()
+    _check_qkv(q, k, v)
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    if tau_out is None and want_tau:
+        tau_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    rc = lib.entmax_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window),
+                             _ptr(out), _ptr(tau_out), B, H, L, d, _dtype_code(q), _stream(q))
+    _check(lib, rc)
+    return out, tau_out
+
+
+def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) float32 [B, H, L, d] from the forward's tau."""
+    lib = load_library()
+    _check_qkv(q, k, v)
+    _check_qkv(q, dout)
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    if tau.shape != (B, H, L) or tau.dtype != torch.float32 or not tau.is_contiguous():
+        raise ValueError("tau must be a contiguous [B, H, L] float32 tensor")
+    mk = lambda: torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)  # noqa: E731
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    rc = lib.entmax_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                             _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, L, d, _dtype_code(q), _stream(q))
+    _check(lib, rc)
+    return dq, dk, dv
+
+
+def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=None):
+    """Dense attention weights [B, H, L, L] float32 recomputed from tau."""
+    lib = load_library()
+    _check_qkv(q, k)
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    if probs is None:
+        probs = torch.empty((B, H, L, L), dtype=torch.float32, device=q.device)
+    rc = lib.entmax_attn_probs(_ptr(q), _ptr(k), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                               _ptr(probs), B, H, L, d, _dtype_code(q), _stream(q))
+    _check(lib, rc)
+    return probs
+
+
+def raw_call(name, *args):
+    """Call an exported symbol with raw ctypes arguments; returns its result.
+
+    For tests of the boundary itself (error codes on bad arguments)."""
+    lib = load_library()
+    return getattr(lib, name)(*args)

@@ -1,0 +1,157 @@
+// Device helpers shared by the gfx950 1.5-entmax attention kernels.
+//
+// MFMA lane layouts used throughout (wave of 64 lanes, g = lane / 16,
+// c = lane % 16):
+//   v_mfma_f32_16x16x32_bf16: lane (g, c) supplies A[c][8g .. 8g+7] and
+//     B[8g .. 8g+7][c]; the result D[4g + i][c] sits in element i.
+//   v_mfma_f32_16x16x4_f32:   lane (g, c) supplies A[c][g] and B[g][c];
+//     the result layout is the same as above.
+// Only the pairing of A and B slots matters for the contraction, so each
+// helper picks the contraction index of slot (g, i) to make its loads
+// contiguous, and uses the same choice for both operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ea {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;     // threads per workgroup (4 waves)
+constexpr int kBN = 64;           // keys per KV tile
+constexpr int kIters = 25;        // bisection steps
+constexpr float kInf = __builtin_huge_valf();
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+    u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Sums / maxima over groups of N consecutive lanes (N a power of two <= 64).
+// Butterfly order: every lane of the group ends with a bitwise-identical
+// value (floating-point addition is commutative).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = N / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = N / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ int group_sum_int(int v) {
+#pragma unroll
+    for (int o = N / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Score tiles: S[16 queries x 16 keys] = Q K^T (unscaled), fp32 accumulate.
+// ---------------------------------------------------------------------------
+
+template <int DT, int D> struct QFrag;
+
+// bf16: slot (g, i) of k-step ks holds feature 32*ks + 8*g + i.
+template <int D> struct QFrag<DT_BF16, D> {
+    bf16x8 a[D / 32];
+    __device__ __forceinline__ void load(const uint16_t* qh, int row, int L, int g) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            a[ks] = row < L ? ld_bf16x8(qh + static_cast<size_t>(row) * D + 32 * ks + 8 * g) : zero_bf16x8();
+    }
+    // key: this lane's key (column c); the lane's K row is read 16 B at a time
+    __device__ __forceinline__ f32x4 tile(const uint16_t* kh, int key, int L, int g) const {
+        bf16x8 b[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            b[ks] = key < L ? ld_bf16x8(kh + static_cast<size_t>(key) * D + 32 * ks + 8 * g) : zero_bf16x8();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(a[ks], b[ks], acc);
+        return acc;
+    }
+};
+
+// f32: step (u, s) gives slot g the feature 16*u + 4*g + s.
+template <int D> struct QFrag<DT_F32, D> {
+    f32x4 a[D / 16];
+    __device__ __forceinline__ void load(const float* qh, int row, int L, int g) {
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            a[u] = row < L ? *reinterpret_cast<const f32x4*>(qh + static_cast<size_t>(row) * D + 16 * u + 4 * g) : z;
+        }
+    }
+    __device__ __forceinline__ f32x4 tile(const float* kh, int key, int L, int g) const {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 b = key < L ? *reinterpret_cast<const f32x4*>(kh + static_cast<size_t>(key) * D + 16 * u + 4 * g) : z;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_f32(a[u][s], b[s], acc);
+        }
+        return acc;
+    }
+};
+
+template <int DT> struct InT;
+template <> struct InT<DT_F32> { typedef float type; };
+template <> struct InT<DT_BF16> { typedef uint16_t type; };
+
+// ---------------------------------------------------------------------------
+// Masking: key j allowed for query i (both already known to be < L).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool allowed_ij(int i, int j, int causal, int window) {
+    return (!causal || j <= i) && (window <= 0 || j > i - window);
+}
+
+// Key range [lo, hi) that rows [q0, q0 + bm) may attend.
+__host__ __device__ __forceinline__ void key_range(int q0, int bm, int L, int causal, int window,
+                                                   int* lo, int* hi) {
+    int h = L;
+    if (causal) h = q0 + bm < L ? q0 + bm : L;
+    int l = 0;
+    if (window > 0) l = q0 - window + 1 > 0 ? q0 - window + 1 : 0;
+    *lo = l;
+    *hi = h;
+}
+
+// Workgroup -> work item: consecutive work items (the Q tiles of one head)
+// land on the same XCD, whose L2 then serves the head's K and V.
+// Workgroups are dealt round-robin to the 8 XCDs.
+__device__ __forceinline__ int xcd_swizzle(int bid, int total) {
+    const int nx = 8;
+    const int per = total / nx;
+    if (bid < per * nx) return (bid % nx) * per + bid / nx;
+    return bid;
+}
+
+}  // namespace ea

@@ -1,0 +1,227 @@
+// C ABI of the gfx950 1.5-entmax attention library: argument validation,
+// kernel selection and launch on the caller's stream.  See
+// include/entmax_attn.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "entmax_attn.h"
+#include "fwd_dense.hpp"
+#include "fwd_short.hpp"
+#include "fwd_stream.hpp"
+#include "probs.hpp"
+#include "bwd.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ENTMAX_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    g_err[0] = '\0';
+    return ENTMAX_OK;
+}
+
+// Common argument checks; returns ENTMAX_OK or an error code.
+int check_common(int B, int H, int L, int d, int dtype, int causal, int window) {
+    if (B <= 0 || H <= 0 || L <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, L must be positive (got %d, %d, %d)", B, H, L);
+    if (window < 0) return fail(ENTMAX_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal) return fail(ENTMAX_ERR_INVALID_ARG, "window > 0 requires causal attention");
+    if (d != 64 && d != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (L > 65536) return fail(ENTMAX_ERR_UNSUPPORTED, "L = %d exceeds 65536", L);
+    if (static_cast<long long>(B) * H * ((L + 15) / 16) > (1LL << 30))
+        return fail(ENTMAX_ERR_UNSUPPORTED, "B*H*L too large for one launch");
+    return ENTMAX_OK;
+}
+
+// Largest key span (in 64-key tiles x 64) over the query tiles of height bm.
+int max_span(int L, int bm, int causal, int window) {
+    int best = 0;
+    for (int q0 = 0; q0 < L; q0 += bm) {
+        int lo, hi;
+        ea::key_range(q0, bm, L, causal, window, &lo, &hi);
+        const int span = (hi > lo) ? ((hi + ea::kBN - 1) / ea::kBN - lo / ea::kBN) * ea::kBN : 0;
+        if (span > best) best = span;
+    }
+    return best;
+}
+
+template <typename K>
+int set_lds(K kernel, size_t bytes) {
+    if (bytes <= 65536) return ENTMAX_OK;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+    if (e != hipSuccess) return fail(ENTMAX_ERR_HIP, "hipFuncSetAttribute(%zu B LDS): %s", bytes, hipGetErrorString(e));
+    return ENTMAX_OK;
+}
+
+template <int DT, int D, int BM, int LSPAN>
+int launch_dense(const ea::FwdArgs& a, hipStream_t st) {
+    typedef ea::DenseCfg<D, BM, LSPAN> C;
+    auto kern = ea::fwd_dense_kernel<DT, D, BM, LSPAN>;
+    int rc = set_lds(kern, C::lds_bytes);
+    if (rc) return rc;
+    const int grid = a.B * a.H * a.nqt;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_dense");
+}
+
+template <int DT, int D, int NKT>
+int launch_short(const ea::FwdArgs& a, hipStream_t st) {
+    typedef ea::ShortCfg<DT, D, NKT> C;
+    auto kern = ea::fwd_short_kernel<DT, D, NKT>;
+    int rc = set_lds(kern, C::lds_bytes);
+    if (rc) return rc;
+    const int grid = a.B * a.H * a.nqt;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_short");
+}
+
+template <int DT, int D>
+int launch_stream(const ea::FwdArgs& a, hipStream_t st) {
+    constexpr int CAP = 128;
+    typedef ea::StreamCfg<D, CAP> C;
+    auto kern = ea::fwd_stream_kernel<DT, D, CAP>;
+    int rc = set_lds(kern, C::lds_bytes);
+    if (rc) return rc;
+    const int grid = a.B * a.H * a.nqt;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_stream");
+}
+
+template <int DT, int D>
+int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
+    const int L = a.L;
+    const int s64 = max_span(L, 64, a.causal, a.window);
+    if (s64 <= 64) {
+        a.nqt = (L + 63) / 64;
+        return launch_short<DT, D, 1>(a, st);
+    }
+    if (s64 <= 128) {
+        a.nqt = (L + 63) / 64;
+        return launch_short<DT, D, 2>(a, st);
+    }
+    if (max_span(L, 32, a.causal, a.window) <= 256) {
+        a.nqt = (L + 31) / 32;
+        return launch_dense<DT, D, 32, 256>(a, st);
+    }
+    const int s16 = max_span(L, 16, a.causal, a.window);
+    if (s16 <= 512) {
+        a.nqt = (L + 15) / 16;
+        return launch_dense<DT, D, 16, 512>(a, st);
+    }
+    if (s16 <= 1024) {
+        a.nqt = (L + 15) / 16;
+        return launch_dense<DT, D, 16, 1024>(a, st);
+    }
+    a.nqt = (L + 63) / 64;
+    return launch_stream<DT, D>(a, st);
+}
+
+template <int DT, int D>
+int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
+    constexpr int CAP = 128;
+    auto kern = ea::bwd_kernel<DT, D, CAP>;
+    const size_t lds = ea::BwdCfg<CAP>::lds_bytes;
+    int rc = set_lds(kern, lds);
+    if (rc) return rc;
+    const size_t n = static_cast<size_t>(a.B) * a.H * a.L * D;
+    const unsigned fill_blocks = static_cast<unsigned>((n / 4 + 255) / 256 + 1);
+    hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dk, n);
+    hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dv, n);
+    hipLaunchKernelGGL(kern, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), lds, st, a);
+    return check_launch("bwd");
+}
+
+}  // namespace
+
+extern "C" {
+
+int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                    float* out, float* tau_out, int B, int H, int L, int d, int dtype, void* stream) {
+    if (!q || !k || !v || !out) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+    int rc = check_common(B, H, L, d, dtype, causal, window);
+    if (rc) return rc;
+    ea::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.key_mask = key_mask;
+    a.out = out; a.tau = tau_out;
+    a.B = B; a.H = H; a.L = L;
+    a.causal = causal ? 1 : 0; a.window = window;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    a.nqt = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16)
+        return d == 64 ? dispatch_fwd<ea::DT_BF16, 64>(a, st) : dispatch_fwd<ea::DT_BF16, 128>(a, st);
+    return d == 64 ? dispatch_fwd<ea::DT_F32, 64>(a, st) : dispatch_fwd<ea::DT_F32, 128>(a, st);
+}
+
+int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
+                      const float* tau, float* probs, int B, int H, int L, int d, int dtype, void* stream) {
+    if (!q || !k || !tau || !probs) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, tau and probs must not be NULL");
+    int rc = check_common(B, H, L, d, dtype, causal, window);
+    if (rc) return rc;
+    ea::ProbsArgs a;
+    a.q = q; a.k = k; a.key_mask = key_mask; a.tau = tau; a.probs = probs;
+    a.B = B; a.H = H; a.L = L; a.causal = causal ? 1 : 0; a.window = window;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    a.nrt = (L + 15) / 16;
+    a.nkt = (L + ea::kBN - 1) / ea::kBN;
+    const long long items = static_cast<long long>(B) * H * a.nrt * a.nkt;
+    if ((items + 3) / 4 > (1LL << 31) - 1) return fail(ENTMAX_ERR_UNSUPPORTED, "probs grid too large");
+    const dim3 grid(static_cast<unsigned>((items + 3) / 4));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16) {
+        if (d == 64) hipLaunchKernelGGL((ea::probs_kernel<ea::DT_BF16, 64>), grid, dim3(ea::kThreads), 0, st, a);
+        else hipLaunchKernelGGL((ea::probs_kernel<ea::DT_BF16, 128>), grid, dim3(ea::kThreads), 0, st, a);
+    } else {
+        if (d == 64) hipLaunchKernelGGL((ea::probs_kernel<ea::DT_F32, 64>), grid, dim3(ea::kThreads), 0, st, a);
+        else hipLaunchKernelGGL((ea::probs_kernel<ea::DT_F32, 128>), grid, dim3(ea::kThreads), 0, st, a);
+    }
+    return check_launch("probs");
+}
+
+int entmax_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                    const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                    int B, int H, int L, int d, int dtype, void* stream) {
+    if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv)
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk and dv must not be NULL");
+    int rc = check_common(B, H, L, d, dtype, causal, window);
+    if (rc) return rc;
+    ea::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.H = H; a.L = L; a.causal = causal ? 1 : 0; a.window = window;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    a.nqt = (L + 63) / 64;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16) return d == 64 ? launch_bwd<ea::DT_BF16, 64>(a, st) : launch_bwd<ea::DT_BF16, 128>(a, st);
+    return d == 64 ? launch_bwd<ea::DT_F32, 64>(a, st) : launch_bwd<ea::DT_F32, 128>(a, st);
+}
+
+const char* entmax_attn_status_string(int status) {
+    switch (status) {
+        case ENTMAX_OK: return "ok";
+        case ENTMAX_ERR_INVALID_ARG: return "invalid argument";
+        case ENTMAX_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ENTMAX_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* entmax_attn_last_error(void) { return g_err; }
+
+int entmax_attn_version(void) { return 1; }
+
+}  // extern "C"

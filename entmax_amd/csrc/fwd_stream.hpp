@@ -1,0 +1,342 @@
+// Forward kernel for rows whose key span does not fit in LDS (> 1024 keys).
+//
+// One workgroup = 4 independent waves, each owning 16 query rows of one
+// (batch, head).  The score row is never stored whole:
+//   1. one pass over the KV tiles computes S = Q K^T / sqrt(d) on MFMA with
+//      the masks folded in, keeps the running row max m and the allowed count
+//      n, and appends every score above m - 2 (with its key) to the row's
+//      candidate list in LDS.  tau >= max - 2 ("DistilBERT SST-2 with
+//      AdaSplash Attention" model card, Mathematical Formulation 2), so every
+//      key of the final support is in the list; lists that would fill up are
+//      compacted with the current threshold.
+//   2. tau by 25 bisection steps over the list (tau_solver.hpp), 4 lanes/row.
+//   3. O_i = sum over list entries with s > tau of p * V_key, gathering V rows
+//      (sparse aggregation, "RoBERTa Base with AdaSplash Attention" model
+//      card, Architecture Overview).
+// A row whose candidates still overflow its list falls back to bisection with
+// S recomputed from the K tiles at every step, then a recompute pass that
+// streams its support into the list and flushes it into O when full.
+#pragma once
+
+#include "common.hpp"
+#include "fwd_dense.hpp"
+#include "tau_solver.hpp"
+
+namespace ea {
+
+template <int D, int CAP>
+struct StreamCfg {
+    static constexpr int BM = 64;
+    static constexpr int TPR = kThreads / BM;   // 4 lanes per row in the solve
+    static constexpr size_t lds_bytes =
+        static_cast<size_t>(BM) * CAP * (sizeof(float) + sizeof(uint16_t)) +
+        sizeof(float) * 3 * BM + sizeof(int) * 2 * BM;
+    static_assert(CAP / TPR <= 64, "at most 64 list entries per lane in the solve");
+};
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Rank of this lane among the set lanes of its 16-lane group in `mask`.
+__device__ __forceinline__ void group_rank(unsigned long long mask, int g, int c, int* rank, int* total) {
+    const unsigned gm = static_cast<unsigned>((mask >> (16 * g)) & 0xFFFFull);
+    *rank = __popc(gm & ((1u << c) - 1u));
+    *total = __popc(gm);
+}
+
+template <int DT, int D, int CAP>
+__global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
+    typedef typename InT<DT>::type T;
+    typedef StreamCfg<D, CAP> C;
+    constexpr int BM = C::BM, TPR = C::TPR;
+    extern __shared__ float lds[];
+    float* lv = lds;                                   // [BM][CAP] candidate scores
+    float* rowm = lv + BM * CAP;                       // [BM] row max
+    float* rowts = rowm + BM;                          // [BM] shifted tau
+    int* rown = reinterpret_cast<int*>(rowts + BM + BM);            // [BM] allowed count
+    int* rowc = rown + BM;                             // [BM] list length, -1 = overflow
+    uint16_t* lk = reinterpret_cast<uint16_t*>(rowc + BM);         // [BM][CAP] keys
+
+    const int total = a.B * a.H * a.nqt;
+    const int w = xcd_swizzle(blockIdx.x, total);
+    const int bh = w / a.nqt;
+    const int qt = w - bh * a.nqt;
+    const int b = bh / a.H;
+    const int q0 = qt * BM;
+    const int L = a.L;
+    const size_t head_off = static_cast<size_t>(bh) * L * D;
+    const T* qh = static_cast<const T*>(a.q) + head_off;
+    const T* kh = static_cast<const T*>(a.k) + head_off;
+    const T* vh = static_cast<const T*>(a.v) + head_off;
+    const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wv = tid / kWave;
+    const int g = lane / 16, c = lane % 16;
+    const int r0 = 16 * wv;            // this wave's first row (tile-local)
+
+    // key span of this wave's rows
+    int klo, khi;
+    key_range(q0 + r0, 16, L, a.causal, a.window, &klo, &khi);
+    const int kt0 = klo / kBN;
+    const int ntile = khi > klo ? (khi + kBN - 1) / kBN - kt0 : 0;
+
+    QFrag<DT, D> qf;
+    qf.load(qh, q0 + r0 + c, L, g);
+
+    auto score = [&](int key, const f32x4& acc, int i) {
+        const int row = q0 + r0 + 4 * g + i;
+        const bool ok = key < L && row < L && (km == nullptr || km[key] != 0) &&
+                        allowed_ij(row, key, a.causal, a.window);
+        return ok ? acc[i] * a.scale : -kInf;
+    };
+
+    // ---- 1. scores, row max, candidate lists --------------------------------
+    float m[4];
+    int n[4], cnt[4];
+    bool ovf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m[i] = -kInf; n[i] = 0; cnt[i] = 0; ovf[i] = false; }
+
+    for (int t = 0; t < ntile; ++t) {
+        const int kbase = (kt0 + t) * kBN;
+        float s[4][4];
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16) {
+            const int key = kbase + 16 * c16 + c;
+            const f32x4 acc = qf.tile(kh, key, L, g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, acc, i);
+        }
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float tm = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
+            int tn = (s[0][i] > -kInf) + (s[1][i] > -kInf) + (s[2][i] > -kInf) + (s[3][i] > -kInf);
+            tm = row_max<16>(tm);
+            tn = static_cast<int>(row_sum<16>(static_cast<float>(tn)));
+            m[i] = fmaxf(m[i], tm);
+            n[i] += tn;
+            const float thr = m[i] - 2.f;
+#pragma unroll
+            for (int c16 = 0; c16 < 4; ++c16) any |= s[c16][i] > thr;
+        }
+        if (!__any(any)) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = r0 + 4 * g + i;
+            const float thr = m[i] - 2.f;
+            // make room: drop entries that fell below the current threshold
+            const bool need = !ovf[i] && cnt[i] + kBN > CAP;
+            if (__any(need)) {
+                int wr = 0;
+                const int tot = need ? cnt[i] : 0;
+                int nch = (tot + 15) / 16;
+                int maxch = nch;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) maxch = max(maxch, __shfl_xor(maxch, o, kWave));
+                for (int ch = 0; ch < maxch; ++ch) {
+                    const int idx = 16 * ch + c;
+                    const bool in = idx < tot;
+                    const float v = in ? lv[rl * CAP + idx] : -kInf;
+                    const uint16_t kk = in ? lk[rl * CAP + idx] : static_cast<uint16_t>(0);
+                    const bool keep = in && v > thr;
+                    int rank, tot2;
+                    group_rank(__ballot(keep), g, c, &rank, &tot2);
+                    wave_sync();
+                    if (keep) {
+                        lv[rl * CAP + wr + rank] = v;
+                        lk[rl * CAP + wr + rank] = kk;
+                    }
+                    wave_sync();
+                    wr += tot2;
+                }
+                if (need) cnt[i] = wr;
+            }
+#pragma unroll
+            for (int c16 = 0; c16 < 4; ++c16) {
+                const bool pred = !ovf[i] && s[c16][i] > thr;
+                int rank, tot2;
+                group_rank(__ballot(pred), g, c, &rank, &tot2);
+                const int slot = cnt[i] + rank;
+                if (pred && slot < CAP) {
+                    lv[rl * CAP + slot] = s[c16][i];
+                    lk[rl * CAP + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
+                }
+                cnt[i] += tot2;
+            }
+            if (cnt[i] > CAP) ovf[i] = true;
+        }
+    }
+    if (c == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = r0 + 4 * g + i;
+            rowm[rl] = n[i] > 0 ? m[i] : 0.f;
+            rown[rl] = n[i];
+            rowc[rl] = ovf[i] ? -1 : cnt[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. tau over the candidate lists (4 lanes per row) -------------------
+    {
+        const int r = tid / TPR, sub = tid % TPR;
+        const int nr = rown[r];
+        const int len = rowc[r];
+        const float mm = rowm[r];
+        const float* vrow = lv + r * CAP;
+        const int nel = len > 0 ? (len + TPR - 1) / TPR : 0;
+        auto get = [&](int i) {
+            const int idx = sub + TPR * i;
+            return idx < len ? vrow[idx] - mm : -kInf;
+        };
+        float ts = solve_tau_shifted<TPR>(get, nel, nr > 0 ? nr : 1);
+        if (nr == 0) ts = kInf;
+        if (sub == 0) rowts[r] = ts;
+    }
+    __syncthreads();
+
+    // ---- 3. O = sum p V over the support -------------------------------------
+    constexpr int DPL = D / 16;        // output columns per lane
+    float o[4][DPL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[i][j] = 0.f;
+
+    auto flush = [&](int i, int len, float mm, float ts) {
+        const int rl = r0 + 4 * g + i;
+        for (int e = 0; e < len; ++e) {
+            const float x = (lv[rl * CAP + e] - mm) - ts;
+            if (x > 0.f) {
+                const float p = 0.25f * x * x;
+                const int key = lk[rl * CAP + e];
+                const T* vr = vh + static_cast<size_t>(key) * D + DPL * c;
+                if constexpr (DT == DT_BF16) {
+#pragma unroll
+                    for (int j = 0; j < DPL; j += 4) {
+                        const uint2 u = *reinterpret_cast<const uint2*>(vr + j);
+                        o[i][j + 0] = fmaf(p, __uint_as_float(u.x << 16), o[i][j + 0]);
+                        o[i][j + 1] = fmaf(p, __uint_as_float(u.x & 0xFFFF0000u), o[i][j + 1]);
+                        o[i][j + 2] = fmaf(p, __uint_as_float(u.y << 16), o[i][j + 2]);
+                        o[i][j + 3] = fmaf(p, __uint_as_float(u.y & 0xFFFF0000u), o[i][j + 3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < DPL; j += 4) {
+                        const f32x4 u = *reinterpret_cast<const f32x4*>(vr + j);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o[i][j + q] = fmaf(p, u[q], o[i][j + q]);
+                    }
+                }
+            }
+        }
+    };
+
+    float mrow[4], tsrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = r0 + 4 * g + i;
+        mrow[i] = rowm[rl];
+        tsrow[i] = rowts[rl];
+        if (!ovf[i]) flush(i, cnt[i], mrow[i], tsrow[i]);
+    }
+
+    // ---- overflow fallback (this wave only) ----------------------------------
+    bool my_ovf = ovf[0] || ovf[1] || ovf[2] || ovf[3];
+    if (__any(my_ovf)) {
+        float lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = -2.f;
+            hi[i] = -2.f / sqrtf(static_cast<float>(n[i] > 0 ? n[i] : 1));
+        }
+        for (int it = 0; it < kIters; ++it) {
+            float mid[4], acc4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { mid[i] = 0.5f * (lo[i] + hi[i]); acc4[i] = 0.f; }
+            for (int t = 0; t < ntile; ++t) {
+                const int kbase = (kt0 + t) * kBN;
+#pragma unroll
+                for (int c16 = 0; c16 < 4; ++c16) {
+                    const int key = kbase + 16 * c16 + c;
+                    const f32x4 acc = qf.tile(kh, key, L, g);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float dx = (score(key, acc, i) - mrow[i]) - mid[i];
+                        acc4[i] = dx > 0.f ? fmaf(dx, dx, acc4[i]) : acc4[i];
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g4 = row_sum<16>(acc4[i]);
+                if (g4 > 4.f) lo[i] = mid[i];
+                else hi[i] = mid[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (ovf[i]) {
+                tsrow[i] = n[i] > 0 ? 0.5f * (lo[i] + hi[i]) : kInf;
+                cnt[i] = 0;
+            }
+        }
+        // stream the support of overflowing rows through their lists
+        for (int t = 0; t < ntile; ++t) {
+            const int kbase = (kt0 + t) * kBN;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool full = ovf[i] && cnt[i] + kBN > CAP;
+                if (full) {
+                    wave_sync();
+                    flush(i, cnt[i], mrow[i], tsrow[i]);
+                    cnt[i] = 0;
+                }
+            }
+            wave_sync();
+#pragma unroll
+            for (int c16 = 0; c16 < 4; ++c16) {
+                const int key = kbase + 16 * c16 + c;
+                const f32x4 acc = qf.tile(kh, key, L, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rl = r0 + 4 * g + i;
+                    const float sc = score(key, acc, i);
+                    const bool pred = ovf[i] && (sc - mrow[i]) - tsrow[i] > 0.f;
+                    int rank, tot2;
+                    group_rank(__ballot(pred), g, c, &rank, &tot2);
+                    if (pred) {
+                        lv[rl * CAP + cnt[i] + rank] = sc;
+                        lk[rl * CAP + cnt[i] + rank] = static_cast<uint16_t>(key);
+                    }
+                    cnt[i] += tot2;
+                }
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (ovf[i]) flush(i, cnt[i], mrow[i], tsrow[i]);
+    }
+
+    // ---- write O and tau -------------------------------------------------------
+    float* outh = a.out + head_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = q0 + r0 + 4 * g + i;
+        if (row < L) {
+            float* orow = outh + static_cast<size_t>(row) * D + DPL * c;
+#pragma unroll
+            for (int j = 0; j < DPL; j += 4)
+                *reinterpret_cast<f32x4*>(orow + j) = f32x4{o[i][j], o[i][j + 1], o[i][j + 2], o[i][j + 3]};
+            if (a.tau != nullptr && c == 0)
+                a.tau[static_cast<size_t>(bh) * L + row] = n[i] > 0 ? mrow[i] + tsrow[i] : kInf;
+        }
+    }
+}
+
+}  // namespace ea

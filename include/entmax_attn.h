@@ -1,0 +1,112 @@
+/*
+ * entmax_attn.h -- C ABI of the MI355X (gfx950) 1.5-entmax attention library.
+ *
+ * Method: "ADASPLASH -- ROBERTA Benchmark Result" (AdaSplash Attention module
+ * specification), section 2.2 Theorem 1: each row of scores
+ * s_ij = q_i . k_j / sqrt(d) is mapped to p_ij = [(s_ij - tau_i)/2]_+^2 with
+ * the row threshold tau_i fixed by sum_j p_ij = 1; the attention output is
+ * O_i = sum_j p_ij v_j ("RoBERTa Base with AdaSplash Attention" model card,
+ * Architecture Overview).  tau_i is found by 25 bisection steps on the
+ * bracket [max_j s_ij - 2, max_j s_ij - 2/sqrt(n_i)] ("DistilBERT SST-2 with
+ * AdaSplash Attention" model card, Mathematical Formulation 2), n_i being
+ * the number of keys row i may attend.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE memory, allocated and owned by the
+ *    caller, contiguous, row-major.  q, k, v, dout: [B, H, L, d] of `dtype`;
+ *    out, dq, dk, dv: [B, H, L, d] float32; tau: [B, H, L] float32;
+ *    key_mask: [B, L] uint8 (nonzero = the key may be attended), or NULL for
+ *    "all keys valid".  Pointers to [.., d] rows must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is only enqueued; nothing synchronises.  The library allocates and
+ *    frees no memory and keeps no state between calls; calls on different
+ *    streams may run concurrently as long as their outputs do not overlap.
+ *  - Masking ("ADASPLASH -- ROBERTA Benchmark Result", section 3): key j is
+ *    allowed for query i iff key_mask[b][j] != 0, and, when causal != 0,
+ *    j <= i, and, when window > 0, j > i - window (the splash window, which
+ *    the pages use for causal decoders only: window > 0 requires causal).
+ *    Disallowed keys are removed from the simplex (p = 0 exactly).
+ *  - A query row with no allowed key gets O = 0 and tau = +inf.  Padded
+ *    query rows are computed like any other row.
+ *  - Inputs must be finite (not checked).  Scale is fixed to 1/sqrt(d),
+ *    alpha to 1.5 and the bisection to 25 steps.
+ *  - Supported: d in {64, 128}; dtype ENTMAX_F32 or ENTMAX_BF16;
+ *    1 <= L <= 65536.  Other values return ENTMAX_ERR_UNSUPPORTED.
+ *  - Errors: integer status codes; nothing is launched when the arguments
+ *    are rejected.  ENTMAX_ERR_HIP means a launch failed (see
+ *    entmax_attn_last_error()); faults inside a kernel surface at the
+ *    caller's next synchronisation.
+ */
+#ifndef ENTMAX_ATTN_H
+#define ENTMAX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum entmax_status {
+    ENTMAX_OK = 0,
+    ENTMAX_ERR_INVALID_ARG = 1,   /* NULL required pointer, size <= 0, window < 0, window without causal */
+    ENTMAX_ERR_UNSUPPORTED = 2,   /* d, dtype or L outside the supported set */
+    ENTMAX_ERR_HIP = 3            /* a HIP launch failed */
+};
+
+enum entmax_dtype {
+    ENTMAX_F32 = 0,
+    ENTMAX_BF16 = 1
+};
+
+/*
+ * Forward pass.  Writes out[b,h,i,:] = sum_j p_ij v[b,h,j,:] (float32) and,
+ * when tau_out is not NULL, tau_out[b,h,i] = tau_i in score units (so that
+ * p_ij = [(s_ij - tau_i)/2]_+^2).
+ * Required: q, k, v, out.  Optional: key_mask, tau_out.
+ */
+int entmax_attn_fwd(const void *q, const void *k, const void *v,
+                    const uint8_t *key_mask, int causal, int window,
+                    float *out, float *tau_out,
+                    int B, int H, int L, int d, int dtype, void *stream);
+
+/*
+ * Backward pass from the forward's tau ("ADASPLASH -- ROBERTA Benchmark
+ * Result", section 2.4 Jacobian): with w_ij = sqrt(p_ij),
+ * dp_ij = dout_i . v_j, c_i = sum_j w_ij dp_ij / sum_j w_ij and
+ * dS_ij = w_ij (dp_ij - c_i):  dq = dS k / sqrt(d), dk = dS^T q / sqrt(d),
+ * dv = p^T dout.  dq, dk, dv are overwritten (float32).
+ * Required: q, k, v, tau, dout, dq, dk, dv.  Optional: key_mask.
+ */
+int entmax_attn_bwd(const void *q, const void *k, const void *v,
+                    const uint8_t *key_mask, int causal, int window,
+                    const float *tau, const void *dout,
+                    float *dq, float *dk, float *dv,
+                    int B, int H, int L, int d, int dtype, void *stream);
+
+/*
+ * Dense attention weights for inspection and tests: probs[b,h,i,j] =
+ * [(s_ij - tau[b,h,i])/2]_+^2 for allowed (i, j), 0 otherwise
+ * ([B, H, L, L] float32), recomputing s from q and k exactly as the forward
+ * does.  Required: q, k, tau, probs.  Optional: key_mask.
+ */
+int entmax_attn_probs(const void *q, const void *k,
+                      const uint8_t *key_mask, int causal, int window,
+                      const float *tau, float *probs,
+                      int B, int H, int L, int d, int dtype, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *entmax_attn_status_string(int status);
+
+/* Message describing the most recent failure on the calling thread
+ * (thread-local storage, valid until the next call on that thread). */
+const char *entmax_attn_last_error(void);
+
+/* Library ABI version (incremented on incompatible changes). */
+int entmax_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAX_ATTN_H */

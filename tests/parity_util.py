@@ -1,0 +1,117 @@
+"""Helpers for GPU-vs-oracle parity checks (test code only)."""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import allowed_mask, attention_backward, attention_forward
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}     # absolute, on A, O and tau
+NEAR_TAU = 1e-6                       # zero-pattern exemption band around tau
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dtype_name(t):
+    return "f32" if t.dtype == torch.float32 else "bf16"
+
+
+def to_gpu(inp):
+    out = dict(inp)
+    for k in ("q", "k", "v", "dout", "key_mask"):
+        if out.get(k) is not None:
+            out[k] = out[k].cuda()
+    return out
+
+
+def scores64(q, k, b, h, rows):
+    q64 = q[b, h].to(torch.float64).cpu().numpy()
+    k64 = k[b, h].to(torch.float64).cpu().numpy()
+    return (q64[rows] @ k64.T) / math.sqrt(q.shape[-1])
+
+
+def check_forward(inp, heads=None, rows=None, check_probs=True, label=""):
+    """Run the HIP forward on `inp` (CPU tensors) and compare with the oracle
+    on the selected heads / rows.  Returns a dict of max errors."""
+    from entmax_amd import entmax_attn_fwd, entmax_attn_probs
+    g = to_gpu(inp)
+    q, k, v, km = g["q"], g["k"], g["v"], g["key_mask"]
+    causal, window = bool(inp["causal"]), int(inp["window"])
+    B, H, L, d = q.shape
+    tol = TOL[dtype_name(q)]
+    log(f"[parity] fwd {label} B{B} H{H} L{L} d{d} {dtype_name(q)} causal={causal} window={window}")
+    out, tau = entmax_attn_fwd(q, k, v, km, causal, window)
+    probs = None
+    if check_probs:
+        probs = entmax_attn_probs(q, k, tau, km, causal, window)
+    torch.cuda.synchronize()
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    r_idx = np.arange(L) if rows is None else np.asarray(rows)
+    ref = attention_forward(inp["q"], inp["k"], inp["v"], inp["key_mask"], causal, window,
+                            heads=heads, rows=r_idx, return_probs=check_probs)
+    out_c = out.cpu().numpy()
+    tau_c = tau.cpu().numpy()
+    errs = {"out": 0.0, "tau": 0.0, "probs": 0.0, "pattern_bad": 0}
+    km_np = None if inp["key_mask"] is None else inp["key_mask"].numpy()
+    for n, (b, h) in enumerate(heads):
+        o_gpu = out_c[b, h][r_idx]
+        t_gpu = tau_c[b, h][r_idx]
+        t_ref = ref["tau"][n]
+        inf_ref = np.isinf(t_ref)
+        assert np.array_equal(np.isinf(t_gpu), inf_ref), f"empty-row pattern differs at head {(b, h)}"
+        errs["out"] = max(errs["out"], float(np.abs(o_gpu - ref["out"][n]).max()))
+        if (~inf_ref).any():
+            errs["tau"] = max(errs["tau"], float(np.abs(t_gpu[~inf_ref] - t_ref[~inf_ref]).max()))
+        if check_probs:
+            a_gpu = probs[b, h].cpu().numpy()[r_idx]
+            a_ref = ref["probs"][n]
+            errs["probs"] = max(errs["probs"], float(np.abs(a_gpu - a_ref).max()))
+            s = scores64(inp["q"], inp["k"], b, h, r_idx)
+            ok = allowed_mask(L, None if km_np is None else km_np[b], causal, window)[r_idx]
+            near = np.abs(s - t_ref[:, None]) <= NEAR_TAU
+            differ = ((a_gpu == 0) != (a_ref == 0)) & ok & ~near
+            errs["pattern_bad"] += int(differ.sum())
+            assert not np.any((a_gpu != 0) & ~ok), "nonzero weight on a disallowed key"
+    log(f"[parity]   max err out={errs['out']:.3g} tau={errs['tau']:.3g} probs={errs['probs']:.3g} "
+        f"pattern_bad={errs['pattern_bad']} (tol {tol})")
+    assert errs["out"] <= tol, errs
+    assert errs["tau"] <= tol, errs
+    assert errs["probs"] <= tol, errs
+    assert errs["pattern_bad"] == 0, errs
+    return errs, out, tau
+
+
+def check_backward(inp, heads=None, label="", tau=None):
+    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd
+    g = to_gpu(inp)
+    q, k, v, do, km = g["q"], g["k"], g["v"], g["dout"], g["key_mask"]
+    causal, window = bool(inp["causal"]), int(inp["window"])
+    B, H, L, d = q.shape
+    tol = TOL[dtype_name(q)]
+    log(f"[parity] bwd {label} B{B} H{H} L{L} d{d} {dtype_name(q)} causal={causal} window={window}")
+    if tau is None:
+        _, tau = entmax_attn_fwd(q, k, v, km, causal, window)
+    dq, dk, dv = entmax_attn_bwd(q, k, v, tau, do, km, causal, window)
+    torch.cuda.synchronize()
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], inp["key_mask"], causal, window, heads=heads)
+    errs = {}
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        got_c = got.cpu().numpy()
+        worst = 0.0
+        for n, (b, h) in enumerate(heads):
+            r = ref[name][n]
+            scale = max(1.0, float(np.abs(r).max()))
+            worst = max(worst, float(np.abs(got_c[b, h] - r).max()) / scale)
+        errs[name] = worst
+    log(f"[parity]   max scaled err dq={errs['dq']:.3g} dk={errs['dk']:.3g} dv={errs['dv']:.3g} (tol {tol})")
+    for name in ("dq", "dk", "dv"):
+        assert errs[name] <= tol, errs
+    return errs

@@ -1,0 +1,93 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol
+the header declares, and rejects bad arguments with the documented status
+codes before touching the GPU (argument checks run before any HIP call)."""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(entmax_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from entmax_amd import load_library
+    return load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_probs"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from entmax_amd import LIB_PATH, EXPORTS
+    declared = _declared_functions()
+    dyn = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", dyn, flags=re.M))
+    for n in declared:
+        assert n in exported, n
+        assert hasattr(lib, n), n
+    assert sorted(EXPORTS) == declared
+
+
+def test_status_strings(lib):
+    assert lib.entmax_attn_status_string(0) == b"ok"
+    assert lib.entmax_attn_status_string(1) == b"invalid argument"
+    assert lib.entmax_attn_status_string(2) == b"unsupported configuration"
+    assert lib.entmax_attn_status_string(3) == b"HIP error"
+    assert lib.entmax_attn_version() == 1
+
+
+P = ctypes.c_void_p(16)   # never dereferenced: every call below is rejected first
+
+
+def _fwd(lib, q=P, k=P, v=P, mask=None, causal=0, window=0, out=P, tau=None, B=1, H=1, L=8, d=64, dtype=1):
+    return lib.entmax_attn_fwd(q, k, v, mask, causal, window, out, tau, B, H, L, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, 1), ({"k": None}, 1), ({"v": None}, 1), ({"out": None}, 1),
+    ({"B": 0}, 1), ({"H": -1}, 1), ({"L": 0}, 1),
+    ({"window": -1, "causal": 1}, 1), ({"window": 32, "causal": 0}, 1),
+    ({"d": 96}, 2), ({"d": 256}, 2), ({"dtype": 7}, 2), ({"L": 65537}, 2),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert lib.entmax_attn_last_error() != b""
+
+
+def test_bwd_and_probs_reject_null(lib):
+    args = [P, P, P, None, 0, 0, P, P, P, P, P, 1, 1, 8, 64, 1, None]
+    for i in (0, 1, 2, 6, 7, 8, 9, 10):
+        a = list(args)
+        a[i] = None
+        assert lib.entmax_attn_bwd(*a) == 1
+    assert lib.entmax_attn_bwd(*args[:4], 0, 5, *args[6:]) == 1         # window without causal
+    assert lib.entmax_attn_probs(P, P, None, 0, 0, None, P, 1, 1, 8, 64, 1, None) == 1
+    assert lib.entmax_attn_probs(P, P, None, 0, 0, P, P, 1, 1, 8, 32, 1, None) == 2
+
+
+def test_binding_validates_before_calling():
+    import torch
+    from entmax_amd import entmax_attn_fwd
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        entmax_attn_fwd(q, q, q)          # CPU tensors are refused by the binding
+    with pytest.raises(TypeError):
+        from entmax_amd._binding import _dtype_code
+        _dtype_code(torch.zeros(1, dtype=torch.float16))

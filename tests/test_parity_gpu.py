@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar (fixed by the method's target): absolute error <= 1e-5 for float32
+inputs and <= 2e-3 for bfloat16 inputs on A, O and tau; the exact-zero
+pattern of A must agree except for entries within 1e-6 of tau; backward
+errors are scaled by max(1, |reference|_inf) with the same tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from entmax_amd.workloads import WORKLOADS, make_inputs, random_inputs
+from tests.parity_util import check_backward, check_forward, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from entmax_amd import load_library
+    load_library()
+
+
+# ---- the named workloads ------------------------------------------------------
+
+def test_tiny_full():
+    check_forward(make_inputs("tiny"), label="tiny")
+
+
+def test_encoder_full():
+    check_forward(make_inputs("encoder"), label="encoder")
+
+
+def test_long_subset_heads_full_rows():
+    inp = make_inputs("long")
+    # one head of every temperature (h = 0..11) for batch 0, all rows
+    check_forward(inp, heads=[(0, h) for h in range(12)], label="long")
+
+
+def test_long_sampled_rows_all_heads():
+    inp = make_inputs("long")
+    rows = np.array([0, 1, 511, 777, 1023])
+    check_forward(inp, rows=rows, label="long/rows", check_probs=False)
+
+
+def test_decoder_subset():
+    inp = make_inputs("decoder")
+    check_forward(inp, heads=[(0, 0), (3, 5), (7, 11)], label="decoder")
+
+
+def test_decoder_sampled_rows_all_heads():
+    inp = make_inputs("decoder")
+    rows = np.array([0, 1, 31, 32, 33, 1000, 2047])
+    check_forward(inp, rows=rows, label="decoder/rows", check_probs=False)
+
+
+def test_longctx_forward_two_heads():
+    inp = make_inputs("longctx")
+    check_forward(inp, heads=[(0, 0), (0, 31)], label="longctx", check_probs=False)
+
+
+def test_longctx_forward_sampled_rows():
+    inp = make_inputs("longctx")
+    rows = np.array([0, 4095, 8191])
+    check_forward(inp, heads=[(0, h) for h in range(0, 32, 3)], rows=rows, label="longctx/rows",
+                  check_probs=False)
+
+
+def test_longctx_backward_two_heads():
+    inp = make_inputs("longctx")
+    check_backward(inp, heads=[(0, 0), (0, 17)], label="longctx")
+
+
+# ---- ragged shapes, masks, both dtypes and head dims ---------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L", [1, 7, 64, 100, 257])
+def test_ragged_bidirectional(dtype, d, L):
+    inp = random_inputs(2, 3, L, d, dtype, seed=L * 7 + d)
+    check_forward(inp, label=f"ragged L{L}")
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 1), (True, 5), (True, 32), (True, 100)])
+@pytest.mark.parametrize("L", [50, 300, 1100])
+def test_causal_and_window(causal, window, L):
+    inp = random_inputs(1, 2, L, 64, "bf16", seed=L + window)
+    inp["causal"], inp["window"] = causal, window
+    check_forward(inp, label=f"causal w{window} L{L}", check_probs=L <= 300)
+
+
+def test_padding_with_empty_sequences():
+    inp = random_inputs(4, 2, 96, 64, "bf16", seed=5, key_lengths=[0, 1, 50, 96])
+    errs, out, tau = check_forward(inp, label="padding")
+    assert torch.all(out[0] == 0) and torch.all(torch.isinf(tau[0]))
+
+
+def test_scattered_key_mask_causal():
+    inp = random_inputs(2, 2, 200, 128, "f32", seed=6, key_mask_density=0.5)
+    inp["causal"] = True
+    check_forward(inp, label="scattered mask")
+
+
+# ---- the streaming path (key span > 1024) and its overflow fallback -------------
+
+def test_stream_path_bidirectional():
+    inp = random_inputs(1, 2, 2000, 64, "bf16", seed=7)
+    check_forward(inp, label="stream", check_probs=False)
+
+
+def test_stream_path_masked_f32():
+    inp = random_inputs(2, 1, 1500, 128, "f32", seed=8, key_lengths=[1500, 1203])
+    check_forward(inp, label="stream f32", check_probs=False)
+
+
+def test_stream_overflow_fallback():
+    # near-uniform rows: every key is a candidate, far more than a list holds
+    inp = random_inputs(1, 2, 1300, 64, "bf16", seed=9, qk_gain=0.2)
+    check_forward(inp, label="stream overflow", check_probs=False)
+
+
+# ---- determinism and streams ----------------------------------------------------
+
+def test_forward_is_deterministic():
+    from entmax_amd import entmax_attn_fwd
+    inp = make_inputs("encoder")
+    q, k, v, km = (inp[x].cuda() for x in ("q", "k", "v", "key_mask"))
+    o1, t1 = entmax_attn_fwd(q, k, v, km)
+    o2, t2 = entmax_attn_fwd(q, k, v, km)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(t1, t2)
+
+
+def test_runs_on_a_side_stream():
+    from entmax_amd import entmax_attn_fwd
+    inp = random_inputs(2, 2, 256, 64, "bf16", seed=10)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    ref, _ = entmax_attn_fwd(q, k, v)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, _ = entmax_attn_fwd(q, k, v)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+# ---- backward on small cases ------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_small(dtype):
+    inp = random_inputs(2, 2, 77, 64, dtype, seed=11, qk_gain=1.5)
+    check_backward(inp, label="small")
+
+
+def test_backward_masked_causal_window():
+    inp = random_inputs(2, 2, 150, 128, "bf16", seed=12, key_lengths=[150, 90])
+    inp["causal"], inp["window"] = True, 32
+    check_backward(inp, label="masked causal window")
+
+
+def test_backward_dense_support_overflow():
+    # supports of hundreds of keys: the per-row list overflows
+    inp = random_inputs(1, 2, 600, 64, "f32", seed=13, qk_gain=0.3)
+    check_backward(inp, label="dense support")
