@@ -136,10 +136,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
         ovf[i] = false;
     }
 
-    auto score = [&](int key, const f32x4& acc, int i) {
+    // key validity without a branch around the mask load (see common.hpp)
+    auto key_ok = [&](int key) {
+        const bool in = key < L;
+        if (km == nullptr) return in;
+        const uint8_t mb = km[clamp_row(key, L)];   // unconditional load
+        return in && mb != 0;
+    };
+    auto score = [&](int key, bool kv, const f32x4& acc, int i) {
         const int row = q0 + r0 + 4 * g + i;
-        const bool ok = key < L && row < L && (km == nullptr || km[key] != 0) &&
-                        allowed_ij(row, key, a.causal, a.window);
+        const bool ok = kv && row < L && allowed_ij(row, key, a.causal, a.window);
         return ok ? acc[i] * a.scale : -kInf;
     };
     auto dot_dp = [&](int i, int key) {
@@ -176,9 +182,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int c16 = 0; c16 < 4; ++c16) {
             const int key = kbase + 16 * c16 + c;
+            const bool kv = key_ok(key);
             const f32x4 acc = qf.tile(kh, key, L, g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, acc, i);
+            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
         }
         int from[4];
 #pragma unroll
@@ -257,9 +264,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int c16 = 0; c16 < 4; ++c16) {
                 const int key = kbase + 16 * c16 + c;
+                const bool kv = key_ok(key);
                 const f32x4 acc = qf.tile(kh, key, L, g);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[c16][i] = score(key, acc, i);
+                for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
             }
             int n_in[4];
 #pragma unroll

@@ -79,19 +79,35 @@ __device__ __forceinline__ int group_sum_int(int v) {
 template <int DT, int D> struct QFrag;
 
 // bf16: slot (g, i) of k-step ks holds feature 32*ks + 8*g + i.
+// Loads below never branch on their predicate: a branch around a load makes
+// the compiler wait for that load before the branches join, which
+// serialises independent loads.  Out-of-range rows are read from a clamped
+// (valid, usually cache-resident) address and replaced by zero afterwards.
+__device__ __forceinline__ bf16x8 ld_bf16x8_or_zero(const uint16_t* p, bool ok) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8, ok ? u : z);
+}
+__device__ __forceinline__ f32x4 ld_f32x4_or_zero(const float* p, bool ok) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    return ok ? u : z;
+}
+__device__ __forceinline__ int clamp_row(int r, int L) { return r < L ? r : L - 1; }
+
 template <int D> struct QFrag<DT_BF16, D> {
     bf16x8 a[D / 32];
     __device__ __forceinline__ void load(const uint16_t* qh, int row, int L, int g) {
+        const uint16_t* p = qh + static_cast<size_t>(clamp_row(row, L)) * D + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            a[ks] = row < L ? ld_bf16x8(qh + static_cast<size_t>(row) * D + 32 * ks + 8 * g) : zero_bf16x8();
+        for (int ks = 0; ks < D / 32; ++ks) a[ks] = ld_bf16x8_or_zero(p + 32 * ks, row < L);
     }
     // key: this lane's key (column c); the lane's K row is read 16 B at a time
     __device__ __forceinline__ f32x4 tile(const uint16_t* kh, int key, int L, int g) const {
         bf16x8 b[D / 32];
+        const uint16_t* p = kh + static_cast<size_t>(clamp_row(key, L)) * D + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            b[ks] = key < L ? ld_bf16x8(kh + static_cast<size_t>(key) * D + 32 * ks + 8 * g) : zero_bf16x8();
+        for (int ks = 0; ks < D / 32; ++ks) b[ks] = ld_bf16x8_or_zero(p + 32 * ks, key < L);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(a[ks], b[ks], acc);
@@ -103,18 +119,16 @@ template <int D> struct QFrag<DT_BF16, D> {
 template <int D> struct QFrag<DT_F32, D> {
     f32x4 a[D / 16];
     __device__ __forceinline__ void load(const float* qh, int row, int L, int g) {
+        const float* p = qh + static_cast<size_t>(clamp_row(row, L)) * D + 4 * g;
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            a[u] = row < L ? *reinterpret_cast<const f32x4*>(qh + static_cast<size_t>(row) * D + 16 * u + 4 * g) : z;
-        }
+        for (int u = 0; u < D / 16; ++u) a[u] = ld_f32x4_or_zero(p + 16 * u, row < L);
     }
     __device__ __forceinline__ f32x4 tile(const float* kh, int key, int L, int g) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float* p = kh + static_cast<size_t>(clamp_row(key, L)) * D + 4 * g;
 #pragma unroll
         for (int u = 0; u < D / 16; ++u) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 b = key < L ? *reinterpret_cast<const f32x4*>(kh + static_cast<size_t>(key) * D + 16 * u + 4 * g) : z;
+            const f32x4 b = ld_f32x4_or_zero(p + 16 * u, key < L);
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc = mfma_f32(a[u][s], b[s], acc);
         }

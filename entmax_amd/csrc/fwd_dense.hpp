@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kThreads) void fwd_dense_kernel(FwdArgs a) {
 #pragma unroll
             for (int c16 = 0; c16 < kBN / 16; ++c16) {
                 const int key = (kt0 + t) * kBN + 16 * c16 + c;
+                const uint8_t mb = km == nullptr ? static_cast<uint8_t>(1) : km[clamp_row(key, L)];
+                const bool kv = key < L && mb != 0;
                 const f32x4 acc = qf.tile(kh, key, L, g);
-                const bool kv = key < L && (km == nullptr || km[key] != 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rl = 16 * rg + 4 * g + i;

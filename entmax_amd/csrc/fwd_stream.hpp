@@ -86,10 +86,16 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
     QFrag<DT, D> qf;
     qf.load(qh, q0 + r0 + c, L, g);
 
-    auto score = [&](int key, const f32x4& acc, int i) {
+    // key validity without a branch around the mask load (see common.hpp)
+    auto key_ok = [&](int key) {
+        const bool in = key < L;
+        if (km == nullptr) return in;
+        const uint8_t mb = km[clamp_row(key, L)];   // unconditional load
+        return in && mb != 0;
+    };
+    auto score = [&](int key, bool kv, const f32x4& acc, int i) {
         const int row = q0 + r0 + 4 * g + i;
-        const bool ok = key < L && row < L && (km == nullptr || km[key] != 0) &&
-                        allowed_ij(row, key, a.causal, a.window);
+        const bool ok = kv && row < L && allowed_ij(row, key, a.causal, a.window);
         return ok ? acc[i] * a.scale : -kInf;
     };
 
@@ -106,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
 #pragma unroll
         for (int c16 = 0; c16 < 4; ++c16) {
             const int key = kbase + 16 * c16 + c;
+            const bool kv = key_ok(key);
             const f32x4 acc = qf.tile(kh, key, L, g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, acc, i);
+            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
         }
         bool any = false;
 #pragma unroll
@@ -263,10 +270,11 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
                     const int key = kbase + 16 * c16 + c;
+                    const bool kv = key_ok(key);
                     const f32x4 acc = qf.tile(kh, key, L, g);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float dx = (score(key, acc, i) - mrow[i]) - mid[i];
+                        const float dx = (score(key, kv, acc, i) - mrow[i]) - mid[i];
                         acc4[i] = dx > 0.f ? fmaf(dx, dx, acc4[i]) : acc4[i];
                     }
                 }
@@ -301,11 +309,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
 #pragma unroll
             for (int c16 = 0; c16 < 4; ++c16) {
                 const int key = kbase + 16 * c16 + c;
+                const bool kv = key_ok(key);
                 const f32x4 acc = qf.tile(kh, key, L, g);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rl = r0 + 4 * g + i;
-                    const float sc = score(key, acc, i);
+                    const float sc = score(key, kv, acc, i);
                     const bool pred = ovf[i] && (sc - mrow[i]) - tsrow[i] > 0.f;
                     int rank, tot2;
                     group_rank(__ballot(pred), g, c, &rank, &tot2);

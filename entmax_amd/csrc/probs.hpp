@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kThreads) void probs_kernel(ProbsArgs a) {
     for (int c16 = 0; c16 < 4; ++c16) {
         const int key = kt * kBN + 16 * c16 + c;
         const f32x4 acc = qf.tile(kh, key, L, g);
-        const bool kv = key < L && (km == nullptr || km[key] != 0);
+        const uint8_t mb = km == nullptr ? static_cast<uint8_t>(1) : km[clamp_row(key, L)];
+                const bool kv = key < L && mb != 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rt + 4 * g + i;

@@ -36,8 +36,8 @@ template <int D> struct PVTile<DT_BF16, D> {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int key = key_lane + i;
-                const uint16_t raw = key < L ? vh[static_cast<size_t>(key) * D + 16 * ct + c] : static_cast<uint16_t>(0);
-                b[i] = __builtin_bit_cast(__bf16, raw);
+                const uint16_t raw = vh[static_cast<size_t>(clamp_row(key, L)) * D + 16 * ct + c];
+                b[i] = __builtin_bit_cast(__bf16, key < L ? raw : static_cast<uint16_t>(0));
             }
             o[ct] = mfma_bf16(phi, b, o[ct]);
             o[ct] = mfma_bf16(plo, b, o[ct]);
@@ -72,7 +72,8 @@ template <int D> struct PVTile<DT_F32, D> {
 #pragma unroll
             for (int s = 0; s < kPer; ++s) {
                 const int key = key_lane + s;
-                const float b = key < L ? vh[static_cast<size_t>(key) * D + 16 * ct + c] : 0.f;
+                const float raw = vh[static_cast<size_t>(clamp_row(key, L)) * D + 16 * ct + c];
+                const float b = key < L ? raw : 0.f;
                 o[ct] = mfma_f32(p[s], b, o[ct]);
             }
         }
