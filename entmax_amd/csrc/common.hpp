@@ -95,6 +95,16 @@ __device__ __forceinline__ f32x4 ld_f32x4_or_zero(const float* p, bool ok) {
 }
 __device__ __forceinline__ int clamp_row(int r, int L) { return r < L ? r : L - 1; }
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
+// element k (k < 4) of the 4 x 16-bit row that lane 4k + j/4 points at, so
+// a 16 x 4 block is read transposed.  p: LDS address, 8-byte aligned.
+__device__ __forceinline__ s16x4 ds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
 template <int D> struct QFrag<DT_BF16, D> {
     bf16x8 a[D / 32];
     __device__ __forceinline__ void load(const uint16_t* qh, int row, int L, int g) {

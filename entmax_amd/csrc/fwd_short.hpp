@@ -3,29 +3,33 @@
 //
 // One workgroup (4 waves) per (batch, head, 64 query rows); wave w owns rows
 // 16w .. 16w+15 and lane (g, c) = (lane / 16, lane % 16) serves query row c.
-//   0. All global loads are issued at once, none behind a branch: key-mask
-//      bytes first, then the Q fragments, the K fragments of every 16-key
-//      tile of the span (kept in registers for both products if they fit)
-//      and the V rows,
-//      which are stored transposed into LDS.  Key rows that are masked out or
-//      past L are redirected to an already-fetched row and zeroed.
+// Apart from the V^T staging area every step is private to a wave: one
+// barrier in total.
+//   0. All global loads are issued at once, none behind a branch: the Q
+//      fragments and the K fragments of every 16-key tile of the span (rows
+//      clamped to L; masked keys are dropped after the product), the
+//      key-mask bytes, then the V rows (masked rows are redirected to an
+//      already-fetched row and zeroed).  V waits in registers and is stored
+//      transposed into LDS only after step 2, so that steps 1 and 2 run
+//      while it arrives.
 //   1. S^T = K Q^T on MFMA (operands swapped, so each lane holds 4
-//      consecutive keys of one query), scaled by 1/sqrt(d), masked
-//      (padding / causal / window as -inf), written row-major to LDS with one
-//      128-bit store per tile; row max and allowed count reduced across the 4
-//      lanes of each query.  16-key tiles past the last valid key are
-//      skipped by the later steps.
-//   2. Two lanes per row (waves 0 and 1) find tau (25 bisection steps,
-//      solve_lane.hpp); the row of S in LDS is their workspace.
-//   3. S^T is recomputed on MFMA from the register fragments, P =
-//      [(S - tau)/2]_+^2 formed in registers directly in the A-operand layout,
-//      and O = P V on MFMA with V^T from LDS; 32-key chunks where P vanishes
-//      for the whole wave are skipped.  O is written in fp32.
+//      consecutive keys of one query in each 16-key tile), masked (padding /
+//      causal / window as -inf) and kept in registers: the four lanes
+//      c, c + 16, c + 32, c + 48 hold the whole row.  Tiles outside the
+//      wave's key range are skipped.  Row max and allowed count by
+//      cross-lane swaps.
+//   2. tau by 25 bisection steps on the registers (col_solve.hpp), with a
+//      per-lane scratch column in LDS for the shrinking band.
+//   3. P = [(S - tau)/2]_+^2 formed from the same registers directly in the
+//      A-operand layout of the P V MFMA (keys 4g + i of tiles 2h, 2h + 1
+//      give 32-key chunk h), V^T from LDS; O is written in fp32.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "fwd_dense.hpp"
-#include "solve_lane.hpp"
+#include "col_solve.hpp"
 
 namespace ea {
 
@@ -38,12 +42,19 @@ struct ShortCfg {
     static constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
     static constexpr int CPR = D / EPC;               // chunks per V row
     static constexpr int NCH = SPAN * CPR / kThreads; // V chunks per thread
-    static constexpr int SSTR = SPAN + 4;             // S row stride (floats)
-    static constexpr int VSTR = SPAN + EPC;           // V^T row stride (elements)
-    static constexpr int s_bytes = BM * SSTR * 4;
-    static constexpr int v_bytes = D * VSTR * ESZ;
-    static constexpr size_t lds_bytes = static_cast<size_t>(s_bytes) + v_bytes + 3 * BM * 4;
-    static_assert(NCH >= 2 && NCH % 2 == 0, "whole chunk pairs per thread");
+    static constexpr int VSTR = SPAN + EPC;           // fp32: V^T row stride (elements)
+    // bf16: V row-major, row stride D*2 + 32 bytes (conflict-free transpose
+    // reads); fp32: V^T
+    static constexpr int VRS = D * 2 + 32;
+    static constexpr int v_bytes = DT == DT_BF16 ? SPAN * VRS : D * VSTR * ESZ;
+    static constexpr int scr_bytes = 4 * NT * 4 * kWave * 4;   // per wave: NT*4 rows x 64 lanes
+    static constexpr int KSTR = D * ESZ + 16;                   // K row stride in LDS (bytes)
+    static constexpr int k_bytes = SPAN * KSTR;
+    static constexpr int NKC = SPAN * CPR / kThreads;           // K chunks per thread
+    // K staging (step 0-1) and the solve's scratch (step 2) share one region
+    static constexpr int ks_bytes = k_bytes > scr_bytes ? k_bytes : scr_bytes;
+    static constexpr size_t lds_bytes = static_cast<size_t>(ks_bytes) + v_bytes;
+    static_assert(NCH >= 1 && SPAN <= 2 * kWave, "whole chunks per thread; mask bits in two ballots");
     // waves per SIMD to aim for: 3 workgroups per CU where the register
     // budget allows it (168 registers), else whatever fits
     static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? 3 : 1;
@@ -53,6 +64,12 @@ struct ShortCfg {
 template <int DT, int D> struct KFrag;
 template <int D> struct KFrag<DT_BF16, D> {
     bf16x8 a[D / 32];
+    // from a row-major LDS copy (row = this lane's key)
+    __device__ __forceinline__ void load_lds(const char* row, int g) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 2 * (32 * ks + 8 * g)));
+    }
     // key must be a valid row index; ok = false loads it but yields zeros
     __device__ __forceinline__ void load(const uint16_t* kh, int key, bool ok, int g) {
 #pragma unroll
@@ -65,9 +82,21 @@ template <int D> struct KFrag<DT_BF16, D> {
         for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(a[ks], q.a[ks], acc);
         return acc;
     }
+    // Same, plus bias(key) for every query: one more k-step whose only
+    // nonzero entries are bias(key c) (slot g = 0, i = 0 on the K side) and
+    // 1 (the same slot on the Q side).  bias_bits: bf16 bits in the low half.
+    __device__ __forceinline__ f32x4 st_bias(const QFrag<DT_BF16, D>& q, unsigned bias_bits, int g) const {
+        const u32x4 ub = {g == 0 ? bias_bits : 0u, 0u, 0u, 0u};
+        const u32x4 uq = {g == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};   // bf16 1.0
+        return mfma_bf16(__builtin_bit_cast(bf16x8, ub), __builtin_bit_cast(bf16x8, uq), st(q));
+    }
 };
 template <int D> struct KFrag<DT_F32, D> {
     f32x4 a[D / 16];
+    __device__ __forceinline__ void load_lds(const char* row, int g) {
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) a[u] = *reinterpret_cast<const f32x4*>(row + 4 * (16 * u + 4 * g));
+    }
     __device__ __forceinline__ void load(const float* kh, int key, bool ok, int g) {
 #pragma unroll
         for (int u = 0; u < D / 16; ++u) a[u] = ld_f32x4_or_zero(kh + static_cast<size_t>(key) * D + 16 * u + 4 * g, ok);
@@ -80,20 +109,21 @@ template <int D> struct KFrag<DT_F32, D> {
             for (int s = 0; s < 4; ++s) acc = mfma_f32(a[u][s], q.a[u][s], acc);
         return acc;
     }
+    // bias_bits: fp32 bits of bias(key c)
+    __device__ __forceinline__ f32x4 st_bias(const QFrag<DT_F32, D>& q, unsigned bias_bits, int g) const {
+        return mfma_f32(g == 0 ? __uint_as_float(bias_bits) : 0.f, g == 0 ? 1.f : 0.f, st(q));
+    }
 };
 
 template <int DT, int D, int NKT>
 __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_short_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef ShortCfg<DT, D, NKT> C;
-    constexpr int BM = C::BM, SPAN = C::SPAN, NT = C::NT, EPC = C::EPC, CPR = C::CPR, NCH = C::NCH;
-    constexpr int SSTR = C::SSTR, VSTR = C::VSTR;
+    constexpr int BM = C::BM, NT = C::NT, EPC = C::EPC, CPR = C::CPR, NCH = C::NCH, VSTR = C::VSTR;
     extern __shared__ float lds[];
-    float* S = lds;
-    T* VT = reinterpret_cast<T*>(reinterpret_cast<char*>(lds) + C::s_bytes);
-    float* rowm = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + C::s_bytes + C::v_bytes);
-    float* rown = rowm + BM;
-    float* rowts = rown + BM;
+    char* Ks = reinterpret_cast<char*>(lds);              // K rows (steps 0-1)
+    float* scratch = lds;                                  // the solve's scratch (step 2), same region
+    char* Vs = reinterpret_cast<char*>(lds) + C::ks_bytes;   // V (bf16: row-major; fp32: V^T)
 
     const int total = a.B * a.H * a.nqt;
     const int w = xcd_swizzle(blockIdx.x, total);
@@ -113,222 +143,221 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     const int kbase = (klo / kBN) * kBN;   // first key of the span
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wv = tid / kWave;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: scalar branches below
     const int g = lane / 16, c = lane % 16;
-    const int qrow = q0 + 16 * wv + c;        // this lane's query (as S^T column)
+    const int qrow = q0 + 16 * wv + c;        // this lane's query (S^T column)
 
     // ---- 0. loads ----------------------------------------------------------------
-    // Mask bytes first: the K and V loads depend on them.  Every load is
-    // unconditional (clamped address) so that none waits for another.
-    // Lane (g, c) owns S^T keys kbase + 16t + 4g + i (t < NT, i < 4): their
-    // validity becomes the bitmask kbits (bit 4t + i).
-    bool okv[NCH], okk[NT];
-    int keyv[NCH];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const int itv = tid + kThreads * (j / 2);
-        keyv[j] = kbase + 2 * (itv / CPR) + (j % 2);
-    }
-    if (km != nullptr) {
-        uint8_t mv[NCH], mk[NT];
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) mv[j] = km[clamp_row(keyv[j], L)];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) mk[t] = km[clamp_row(kbase + 16 * t + c, L)];
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) okv[j] = keyv[j] < L && mv[j] != 0;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) okk[t] = kbase + 16 * t + c < L && mk[t] != 0;
-    } else {
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) okv[j] = keyv[j] < L;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) okk[t] = kbase + 16 * t + c < L;
-    }
-    // okk[t] of lanes c = 0..15 (g = 0) covers the 16 keys of tile t: a
-    // ballot hands lane (g, c) the validity of its S^T keys 4g .. 4g + 3
-    unsigned kbits = 0u;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const unsigned long long bal = __ballot(okk[t]);
-        kbits |= static_cast<unsigned>((bal >> (4 * g)) & 0xFull) << (4 * t);
-    }
+    // Issue order matters: a wait on a load also waits for every load issued
+    // before it.  The key-mask bytes go first (two per lane: keys kbase + lane
+    // and kbase + 64 + lane); Q, K and V do not depend on the mask (rows past
+    // L are clamped to valid ones; masked keys are dropped through their
+    // scores, and their V rows meet p = 0), so they are in flight together.
+    // No branch around any load: without a mask the byte loads read a byte
+    // of Q and ignore it.
+    const bool hasm = km != nullptr;
+    const uint8_t* kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+    const int mkey0 = kbase + lane, mkey1 = kbase + kWave + lane;
+    const uint8_t mb0 = kmp[hasm ? clamp_row(mkey0, L) : 0];
+    const uint8_t mb1 = C::SPAN > kWave ? kmp[hasm ? clamp_row(mkey1, L) : 0] : uint8_t(0);
+    // compiler-only fence: the mask loads are issued here, ahead of the
+    // rest (no wait is implied; it only stops the compiler from moving them)
+    asm volatile("" ::: "memory");
     QFrag<DT, D> qf;
     qf.load(qh, qrow, L, g);
-    // K fragments: kept in registers for both products when they fit in 64
-    // registers per lane, else fetched again for step 3 (from L2).  Rows that
-    // are masked out or past L are read from the span's first key row
-    // instead (valid, and fetched anyway), then zeroed: no branch, no extra
-    // HBM traffic.
-    constexpr bool kKeepK = NT * D * C::ESZ / 16 <= 64;
-    KFrag<DT, D> kf[kKeepK ? NT : 1];
-    auto ktile = [&](int t) {
-        KFrag<DT, D> f;
-        f.load(kh, okk[t] ? kbase + 16 * t + c : kbase, okk[t], g);
-        return f;
-    };
-    if constexpr (kKeepK) {
+    // K and V rows of the span, once per workgroup: 16-byte chunks,
+    // consecutive threads on consecutive chunks
+    u32x4 kreg[C::NKC], vreg[NCH];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) kf[t] = ktile(t);
+    for (int j = 0; j < C::NKC; ++j) {
+        const int ch = tid + kThreads * j;
+        kreg[j] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(clamp_row(kbase + ch / CPR, L)) * D + (ch % CPR) * EPC);
     }
-    auto kfrag = [&](int t) -> KFrag<DT, D> {
-        if constexpr (kKeepK) return kf[t];
-        else return ktile(t);
-    };
-    u32x4 vreg[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const int chv = (tid + kThreads * (j / 2)) % CPR;
-        const u32x4 u = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(okv[j] ? keyv[j] : kbase) * D + chv * EPC);
-        vreg[j] = okv[j] ? u : z;
+        const int ch = tid + kThreads * j;
+        vreg[j] = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(clamp_row(kbase + ch / CPR, L)) * D + (ch % CPR) * EPC);
     }
-    // live 16-key tiles: up to the last tile holding a valid key (the same
-    // keys are seen by every wave, so a wave-wide vote suffices)
-    int ntl = 0;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ntl = __any(((kbits >> (4 * t)) & 0xFu) != 0u) ? t + 1 : ntl;
-    // V^T: pairs of keys (2p, 2p + 1) packed per element; read only after
-    // the barrier that ends step 1
-#pragma unroll
-    for (int j = 0; j < NCH; j += 2) {
-        const int itv = tid + kThreads * (j / 2);
-        const int key0 = 2 * (itv / CPR);
-        const int d0 = (itv % CPR) * EPC;
-        if constexpr (DT == DT_BF16) {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                const unsigned w0 = vreg[j][e / 2], w1 = vreg[j + 1][e / 2];
-                const unsigned lo16 = (e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-                const unsigned hi16 = (e & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16);
-                *reinterpret_cast<unsigned*>(VT + (d0 + e) * VSTR + key0) = lo16 | hi16;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                uint2 pr;
-                pr.x = vreg[j][e];
-                pr.y = vreg[j + 1][e];
-                *reinterpret_cast<uint2*>(VT + (d0 + e) * VSTR + key0) = pr;
-            }
-        }
+    for (int j = 0; j < C::NKC; ++j) {
+        const int ch = tid + kThreads * j;
+        *reinterpret_cast<u32x4*>(Ks + (ch / CPR) * C::KSTR + (ch % CPR) * 16) = kreg[j];
+    }
+    __syncthreads();   // K staged
+
+    // valid keys of the span as two 64-bit masks (bit k <-> key kbase + k,
+    // resp. kbase + 64 + k), uniform over the wave
+    const unsigned long long M0 = __ballot((mkey0 < L) & (!hasm | (mb0 != 0)));
+    const unsigned long long M1 = C::SPAN > kWave ? __ballot((mkey1 < L) & (!hasm | (mb1 != 0))) : 0ull;
+    auto mbits16 = [&](int t) -> unsigned {   // the 16 key bits of tile t
+        return static_cast<unsigned>(((t < 4 ? M0 : M1) >> (16 * (t & 3))) & 0xFFFFull);
+    };
+
+    // tiles this wave's 16 rows may attend (causal / window; the mask is
+    // applied below): [t0, tc1), uniform over the wave
+    int t0, tc1;
+    {
+        int wlo, whi;
+        key_range(q0 + 16 * wv, 16, L, a.causal, a.window, &wlo, &whi);
+        t0 = wlo > kbase ? (wlo - kbase) / 16 : 0;
+        tc1 = (whi - kbase + 15) / 16;
+        tc1 = tc1 < NT ? tc1 : NT;
     }
 
-    // ---- 1. S^T tiles, row max and count ----------------------------------------------
-    // (no branches per tile, so that tiles overlap; masked entries are -inf)
-    auto masked = [&](const f32x4& acc, int t, f32x4& sv) {
+    // ---- 1. S^T tiles in registers ----------------------------------------------------
+    // lane (g, c) owns S^T keys kbase + 16t + 4g + i: their validity is bit
+    // 4t + i of kbits; okk(t): validity of this lane's K row (key 16t + c)
+    unsigned kbits = 0u;
+    unsigned full = 0u;   // bit t: every key of tile t valid (uniform)
+    int ntl = 0;          // tiles up to the last one holding a valid key (uniform)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = kbase + 16 * t + 4 * g + i;
-            const bool ok = ((kbits >> (4 * t + i)) & 1u) != 0u && qrow < L && allowed_ij(qrow, key, a.causal, a.window);
-            sv[i] = ok ? acc[i] * a.scale : -kInf;
-        }
-    };
-    {
-        float mx = -kInf, nf = 0.f;
-        float* srow = S + (16 * wv + c) * SSTR;
+    for (int t = 0; t < NT; ++t) {
+        const unsigned mb = mbits16(t);
+        kbits |= ((mb >> (4 * g)) & 0xFu) << (4 * t);
+        ntl = mb != 0u ? t + 1 : ntl;
+        full |= mb == 0xFFFFu ? (1u << t) : 0u;
+    }
+    const int t1 = tc1 < ntl ? tc1 : ntl;
+
+    // Products for the wave's tiles [t0, t1) only (uniform).  In a tile with
+    // keys that may not be attended (masked, or past L) the mask is folded
+    // into the product: such a key gets a bias of -1e30 (finite, so no NaN
+    // can arise), far below every candidate threshold.
+    constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30 (bf16 / fp32)
+    f32x4 sv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        sv[t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+        if (t < t0 || t >= t1) continue;
+        KFrag<DT, D> kf;
+        kf.load_lds(Ks + (16 * t + c) * C::KSTR, g);
+        sv[t] = ((full >> t) & 1u) ? kf.st(qf) : kf.st_bias(qf, ((mbits16(t) >> c) & 1u) ? 0u : kMaskedBits, g);
+    }
+
+    // causal / window masks, row max and count
+    float mraw = -kInf, nl = 0.f;
+    const bool rowok = qrow < L;
+    // allowed keys of this lane's query: (klo_i, khi_i] for causal / window
+    const int khi_i = qrow;
+    const int klo_i = a.window > 0 ? qrow - a.window : -1;
+    auto tiles = [&](auto causal_tag) {
+        constexpr bool CAUSAL = decltype(causal_tag)::value;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            f32x4 sv;
-            masked(kfrag(t).st(qf), t, sv);
+            if (t < t0 || t >= t1) continue;    // uniform: outside the wave's keys (-inf)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                mx = fmaxf(mx, sv[i]);
-                nf += sv[i] > -kInf ? 1.f : 0.f;
+                if constexpr (CAUSAL) {
+                    const int key = kbase + 16 * t + 4 * g + i;
+                    const bool ok = (((kbits >> (4 * t + i)) & 1u) != 0u) & (key <= khi_i) & (key > klo_i);
+                    nl += ok ? 1.f : 0.f;
+                    sv[t][i] = ok ? sv[t][i] : -kInf;
+                }
+                mraw = fmaxf(mraw, sv[t][i]);
             }
-            *reinterpret_cast<f32x4*>(srow + 16 * t + 4 * g) = sv;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        nf += __shfl_xor(nf, 16, kWave);
-        nf += __shfl_xor(nf, 32, kWave);
-        if (g == 0) {
-            rowm[16 * wv + c] = mx;
-            rown[16 * wv + c] = nf;
+        if constexpr (!CAUSAL) {
+            // every key of tiles [t0, t1) with its bit set
+            const unsigned long long lo = (1ull << (4 * t0)) - 1ull, hi = (1ull << (4 * t1)) - 1ull;
+            nl = static_cast<float>(__popc(kbits & static_cast<unsigned>(hi & ~lo)));
         }
+    };
+    if (a.causal) tiles(std::true_type{});
+    else tiles(std::false_type{});
+    if (!rowok) {
+        // query rows past L: nothing allowed
+        nl = 0.f;
+        mraw = -kInf;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sv[t] = f32x4{-kInf, -kInf, -kInf, -kInf};
     }
-    __syncthreads();
+    const float mlane = mraw;   // this lane's maximum
+    mraw = col4_max(mraw);
+    const float n = col4_sum(nl);
+    const bool empty = n == 0.f;
 
-    // ---- 2. tau, two lanes per row (waves 0 and 1) ---------------------------------------
-    if (wv < 2) {
-        const int r = tid / 2, sub = tid % 2;
-        const int n = static_cast<int>(rown[r]);
-        const bool empty = n == 0;
-        const float mm = empty ? 0.f : rowm[r];
-        // this row's own key range inside the span, widened to 4-entry groups
-        int rlo_k, rhi_k;
-        key_range(q0 + r, 1, L, a.causal, a.window, &rlo_k, &rhi_k);
-        const int e0 = ((rlo_k > kbase ? rlo_k - kbase : 0) / 4) * 4;
-        int e1 = rhi_k - kbase;
-        e1 = e1 < 16 * ntl ? e1 : 16 * ntl;
-        e1 = e1 > e0 ? ((e1 + 3) / 4) * 4 : e0;
-        float ts = solve_row_lane<2>(S + r * SSTR, e0, e1, mm, empty ? 1 : n, sub);
-        if (empty) ts = kInf;
-        if (sub == 0) {
-            rowm[r] = mm;
-            rowts[r] = ts;
-            const int row = q0 + r;
-            if (a.tau != nullptr && row < L) a.tau[static_cast<size_t>(bh) * L + row] = empty ? kInf : mm + ts;
+    __syncthreads();   // every wave has its K fragments: the region becomes scratch
+
+    // ---- 2. tau ----------------------------------------------------------------------------
+    const float c2 = 0.5f * a.scale;
+    const float mc2 = empty ? 0.f : mraw * c2;
+    float* col = scratch + wv * (NT * 4 * kWave) + lane;
+    float tr = col_solve<NT>(sv, t0, t1, c2, mc2, empty ? 1.f : n, fmaf(mlane, c2, -mc2), col);
+    if (a.tau != nullptr && g == 0 && rowok) a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tr);
+    const float sh = empty ? 0.f : mc2 + tr;   // p = clamp(acc c2 - sh)^2; empty rows have acc = -inf
+
+    // V into LDS, only now, so that steps 1 and 2 ran while it arrived.
+    // bf16: row-major (the P V operand is read back with transpose loads);
+    // fp32: transposed, one element at a time.
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int ch = tid + kThreads * j;
+        const int key = ch / CPR, d0 = (ch % CPR) * EPC;
+        if constexpr (DT == DT_BF16) {
+            *reinterpret_cast<u32x4*>(Vs + key * C::VRS + d0 * 2) = vreg[j];
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) reinterpret_cast<float*>(Vs)[(d0 + e) * VSTR + key] = __uint_as_float(vreg[j][e]);
         }
     }
-    __syncthreads();
+    __syncthreads();   // V staged
 
     // ---- 3. O = P V --------------------------------------------------------------------------
     f32x4 o[D / 16];
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-        const float mr = rowm[16 * wv + c], tr = rowts[16 * wv + c];
-        auto probs = [&](int t, f32x4& p) {
-            f32x4 sv;
-            masked(kfrag(t).st(qf), t, sv);
+    auto probs = [&](int t, f32x4& p) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = (sv[i] - mr) - tr;
-                p[i] = x > 0.f ? 0.25f * x * x : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const float y = relu1(fmaf(sv[t][i], c2, -sh));
+            p[i] = y * y;
+        }
+    };
+    if constexpr (DT == DT_BF16) {
+        // chunks of 32 keys = tiles (2h, 2h + 1): slot (g, i) holds key
+        // 32h + 4g + i for i < 4 and 32h + 16 + 4g + i - 4 for i >= 4
+#pragma unroll
+        for (int h = 0; h < NT / 2; ++h) {
+            if (2 * h + 1 < t0 || 2 * h >= t1) continue;   // uniform
+            f32x4 p0, p1;
+            probs(2 * h, p0);
+            probs(2 * h + 1, p1);
+            bf16x8 phi, plo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float pv = i < 4 ? p0[i] : p1[i - 4];
+                const __bf16 hb = static_cast<__bf16>(pv);
+                phi[i] = hb;
+                plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
             }
-        };
-        if constexpr (DT == DT_BF16) {
-            // chunks of 32 keys = tiles (2h, 2h + 1): slot (g, i) holds key
-            // 32h + 4g + i for i < 4 and 32h + 16 + 4g + i - 4 for i >= 4
 #pragma unroll
-            for (int h = 0; h < NT / 2; ++h) {
-                if (2 * h >= ntl) break;   // uniform: no valid key from here on
-                f32x4 p0, p1;
-                probs(2 * h, p0);
-                probs(2 * h + 1, p1);
-                bf16x8 phi, plo;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pv = i < 4 ? p0[i] : p1[i - 4];
-                    const __bf16 hb = static_cast<__bf16>(pv);
-                    phi[i] = hb;
-                    plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
-                }
-#pragma unroll
-                for (int ct = 0; ct < D / 16; ++ct) {
-                    const T* vrow = VT + (16 * ct + c) * VSTR + 32 * h + 4 * g;
-                    const uint2 u0 = *reinterpret_cast<const uint2*>(vrow);
-                    const uint2 u1 = *reinterpret_cast<const uint2*>(vrow + 16);
-                    const u32x4 u = {u0.x, u0.y, u1.x, u1.y};
-                    const bf16x8 bv = __builtin_bit_cast(bf16x8, u);
-                    o[ct] = mfma_bf16(phi, bv, o[ct]);
-                    o[ct] = mfma_bf16(plo, bv, o[ct]);
-                }
+            for (int ct = 0; ct < D / 16; ++ct) {
+                // B operand: lane (g, c) needs V[key 32h + 4g + k][16ct + c]
+                // (k < 4) and the same 16 keys on.  A transpose load hands
+                // lane j of a 16-lane group element k of the 4 x b16 row read
+                // by lane 4k + j/4, so lane (g, c) points at row
+                // 32h + 4g + c/4, columns 16ct + 4(c%4) .. + 3.
+                const char* src = Vs + (32 * h + 4 * g + (c >> 2)) * C::VRS + (16 * ct + 4 * (c & 3)) * 2;
+                const s16x4 r0 = ds_read_tr16(src);
+                const s16x4 r1 = ds_read_tr16(src + 16 * C::VRS);
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, s16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]});
+                o[ct] = mfma_bf16(phi, bv, o[ct]);
+                o[ct] = mfma_bf16(plo, bv, o[ct]);
             }
-        } else {
-            // fp32: step s of tile t gives slot g the key 16t + 4g + s
+        }
+    } else {
+        // fp32: step s of tile t gives slot g the key 16t + 4g + s
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t >= ntl) break;       // uniform: no valid key from here on
-                f32x4 p;
-                probs(t, p);
+        for (int t = 0; t < NT; ++t) {
+            if (t < t0 || t >= t1) continue;   // uniform
+            f32x4 p;
+            probs(t, p);
 #pragma unroll
-                for (int ct = 0; ct < D / 16; ++ct) {
-                    const f32x4 bv = *reinterpret_cast<const f32x4*>(VT + (16 * ct + c) * VSTR + 16 * t + 4 * g);
+            for (int ct = 0; ct < D / 16; ++ct) {
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Vs) + (16 * ct + c) * VSTR + 16 * t + 4 * g);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) o[ct] = mfma_f32(p[s], bv[s], o[ct]);
-                }
+                for (int s = 0; s < 4; ++s) o[ct] = mfma_f32(p[s], bv[s], o[ct]);
             }
         }
     }
