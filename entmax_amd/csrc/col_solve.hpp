@@ -210,6 +210,9 @@ __device__ __forceinline__ float col_exact_from(const float* col, int len, const
     return col_exact<K>(sl, s, K * 4 + 3);
 }
 
+template <int KMAX>
+__device__ __forceinline__ float col_finish(float* col, int len, ColState& s);
+
 // Exact root over the row's four lane maxima (xl: this lane's maximum in
 // the half-scaled shifted domain): a subset of the row, so by Theorem 1 its
 // root is at most the row's.  Sort and support search as for the full row,
@@ -270,9 +273,16 @@ __device__ __forceinline__ float col_solve(const f32x4 (&sv)[NT], int t0, int t1
             len += x > s.lb ? 1 : 0;
         }
     }
-    // one stage of bisection steps on the candidates, then the exact finish
-    // on what is left of the band
-    constexpr int KMAX = NT * 4;
+    return col_finish<NT * 4>(col, len, s);
+}
+
+// From a state whose band (entries in (lo, hi] above lb, at most KMAX per
+// lane) sits in the scratch column: one stage of bisection steps, then the
+// exact finish on what is left of the band.  Returns t (half-scaled,
+// shifted), equal in the four lanes of a row.
+template <int KMAX>
+__device__ __forceinline__ float col_finish(float* col, int len, ColState& s) {
+    if (s.it >= kIters) return 0.5f * (s.lo + s.hi);
     if (KMAX > 16 && __any(len > 16)) col_stage<(KMAX > 16 ? 32 : 16), 3>(col, len, s);
     else if (__any(len > 8)) col_stage<16, 3>(col, len, s);
     else if (__any(len > 4)) col_stage<8, 3>(col, len, s);

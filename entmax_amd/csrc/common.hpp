@@ -146,6 +146,20 @@ template <int D> struct QFrag<DT_F32, D> {
     }
 };
 
+// Forward launch arguments (device pointers; see the C header for layouts).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const uint8_t* key_mask;
+    float* out;
+    float* tau;
+    int B, H, L;
+    int causal, window;
+    float scale;
+    int nqt;   // query tiles per head
+};
+
 template <int DT> struct InT;
 template <> struct InT<DT_F32> { typedef float type; };
 template <> struct InT<DT_BF16> { typedef uint16_t type; };

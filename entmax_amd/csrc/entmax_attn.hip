@@ -8,7 +8,7 @@
 #include <cstdio>
 
 #include "entmax_attn.h"
-#include "fwd_dense.hpp"
+#include "fwd_long.hpp"
 #include "fwd_short.hpp"
 #include "fwd_stream.hpp"
 #include "probs.hpp"
@@ -67,17 +67,6 @@ int set_lds(K kernel, size_t bytes) {
     return ENTMAX_OK;
 }
 
-template <int DT, int D, int BM, int LSPAN>
-int launch_dense(const ea::FwdArgs& a, hipStream_t st) {
-    typedef ea::DenseCfg<D, BM, LSPAN> C;
-    auto kern = ea::fwd_dense_kernel<DT, D, BM, LSPAN>;
-    int rc = set_lds(kern, C::lds_bytes);
-    if (rc) return rc;
-    const int grid = a.B * a.H * a.nqt;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), C::lds_bytes, st, a);
-    return check_launch("fwd_dense");
-}
-
 template <int DT, int D, int NKT>
 int launch_short(const ea::FwdArgs& a, hipStream_t st) {
     typedef ea::ShortCfg<DT, D, NKT> C;
@@ -102,6 +91,18 @@ int launch_stream(const ea::FwdArgs& a, hipStream_t st) {
 }
 
 template <int DT, int D>
+int launch_long(ea::FwdArgs a, hipStream_t st) {
+    typedef ea::LongCfg<DT, D> C;
+    auto kern = ea::fwd_long_kernel<DT, D>;
+    int rc = set_lds(kern, C::lds_bytes);
+    if (rc) return rc;
+    a.nqt = (a.L + C::BM - 1) / C::BM;
+    const long long grid = static_cast<long long>(a.B) * a.H * a.nqt;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_long");
+}
+
+template <int DT, int D>
 int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
     const int L = a.L;
     const int s64 = max_span(L, 64, a.causal, a.window);
@@ -113,21 +114,14 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
         a.nqt = (L + 63) / 64;
         return launch_short<DT, D, 2>(a, st);
     }
-    if (max_span(L, 32, a.causal, a.window) <= 256) {
-        a.nqt = (L + 31) / 32;
-        return launch_dense<DT, D, 32, 256>(a, st);
+    // spans beyond 2048 keys: one pass over K with candidate lists and a
+    // gather over the support (the multi-pass streaming kernel re-reads K
+    // and V more than it saves there)
+    if (s64 > 2048) {
+        a.nqt = (L + 63) / 64;
+        return launch_stream<DT, D>(a, st);
     }
-    const int s16 = max_span(L, 16, a.causal, a.window);
-    if (s16 <= 512) {
-        a.nqt = (L + 15) / 16;
-        return launch_dense<DT, D, 16, 512>(a, st);
-    }
-    if (s16 <= 1024) {
-        a.nqt = (L + 15) / 16;
-        return launch_dense<DT, D, 16, 1024>(a, st);
-    }
-    a.nqt = (L + 63) / 64;
-    return launch_stream<DT, D>(a, st);
+    return launch_long<DT, D>(a, st);
 }
 
 template <int DT, int D>

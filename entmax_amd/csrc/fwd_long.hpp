@@ -1,0 +1,439 @@
+// Forward kernel for query tiles whose key span exceeds 128 keys.
+//
+// One workgroup (4 waves) per (batch, head, 64 query rows); wave w owns rows
+// 16w .. 16w+15 and lane (g, c) serves query row c, as in the short-span
+// kernel: the 16-key S^T tiles give lane (g, c) keys 4g .. 4g + 3 of each
+// tile for query c, so the four lanes c, c + 16, c + 32, c + 48 hold a row.
+//
+// The key span is streamed in chunks of 64 keys, each staged once per
+// workgroup in LDS (two buffers; a chunk's loads are issued two chunks ahead)
+// and shared by the four waves; S is recomputed on MFMA in every pass
+// instead of being stored.
+//   A. row max and allowed count, and a rough count of candidates;
+//   C. (only when some lane has too many candidates for its list) three
+//      bisection levels at once: g at the seven midpoints of the next three
+//      levels of the bisection tree ("ADASPLASH -- ROBERTA Benchmark
+//      Result", section 2.3 Theorem 2; bracket of the "DistilBERT SST-2
+//      with AdaSplash Attention" model card, Mathematical Formulation 2);
+//   B. the band: scores in the current bracket (lo, hi] go to a per-lane
+//      list in LDS, those above hi are folded into exact sums (U); if a
+//      list overflows, C runs again and B is repeated;
+//   then tau from the list and U as in the short-span kernel
+//      (col_solve.hpp);
+//   D. P = [(S - tau)/2]_+^2 and O = P V on MFMA, V staged per chunk
+//      (bf16: row-major, read back with transpose loads), chunks where a
+//      wave has no nonzero P skipped for that wave.  O is written in fp32.
+// Every pass decision is uniform over the workgroup (the chunk loop and its
+// barriers are shared).
+#pragma once
+
+#include <type_traits>
+
+#include "col_solve.hpp"
+#include "common.hpp"
+#include "fwd_short.hpp"
+
+namespace ea {
+
+template <int DT, int D>
+struct LongCfg {
+    static constexpr int BM = 64;
+    static constexpr int CK = 64;                     // keys per chunk
+    static constexpr int NTC = CK / 16;               // 16-key tiles per chunk
+    static constexpr int ESZ = DT == DT_BF16 ? 2 : 4;
+    static constexpr int EPC = 16 / ESZ;              // elements per 16-byte piece
+    static constexpr int CPR = D / EPC;               // pieces per row
+    static constexpr int NPC = CK * CPR / kThreads;   // pieces per thread per chunk (K or V)
+    static constexpr int KSTR = D * ESZ + 16;         // K row stride in LDS (bytes)
+    static constexpr int k_bytes = CK * KSTR;         // one K buffer
+    static constexpr int VRS = D * 2 + 32;            // bf16: V row stride (bytes)
+    static constexpr int VSTR = CK + EPC;             // fp32: V^T row stride (elements)
+    static constexpr int v_bytes = DT == DT_BF16 ? CK * VRS : D * VSTR * 4;   // one V buffer
+    static constexpr int CAP = 32;                    // band entries per lane
+    // one more row: where the branch-free appends land once a list is full
+    static constexpr int list_bytes = 4 * (CAP + 1) * kWave * 4;
+    // the band lists (passes B, solve) and the V buffers (pass D) share a region
+    static constexpr int vl_bytes = 2 * v_bytes > list_bytes ? 2 * v_bytes : list_bytes;
+    static constexpr size_t lds_bytes = static_cast<size_t>(2 * k_bytes) + vl_bytes + 64;
+    static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? 3 : (DT == DT_F32 && D == 128) ? 1 : 2;
+    static_assert(NPC >= 1 && CK == kWave, "whole pieces per thread; one mask byte per lane and chunk");
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_kernel(FwdArgs a) {
+    typedef typename InT<DT>::type T;
+    typedef LongCfg<DT, D> C;
+    constexpr int BM = C::BM, CK = C::CK, NTC = C::NTC, EPC = C::EPC, CPR = C::CPR, NPC = C::NPC;
+    constexpr int CAP = C::CAP;
+    extern __shared__ float lds[];
+    char* Kb = reinterpret_cast<char*>(lds);                           // 2 K buffers
+    char* Vb = Kb + 2 * C::k_bytes;                                    // 2 V buffers (pass D)
+    float* lists = reinterpret_cast<float*>(Vb);                       // band lists (B, solve)
+    int* flag = reinterpret_cast<int*>(Vb + C::vl_bytes);              // workgroup-wide vote
+
+    const int total = a.B * a.H * a.nqt;
+    const int w = xcd_swizzle(blockIdx.x, total);
+    const int bh = w / a.nqt;
+    const int qt = w - bh * a.nqt;
+    const int b = bh / a.H;
+    const int q0 = qt * BM;
+    const int L = a.L;
+    const size_t head_off = static_cast<size_t>(bh) * L * D;
+    const T* qh = static_cast<const T*>(a.q) + head_off;
+    const T* kh = static_cast<const T*>(a.k) + head_off;
+    const T* vh = static_cast<const T*>(a.v) + head_off;
+    const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
+    const bool hasm = km != nullptr;
+    const uint8_t* kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane / 16, c = lane % 16;
+    const int qrow = q0 + 16 * wv + c;
+    const bool rowok = qrow < L;
+
+    // chunks of the workgroup's key span, and the keys this wave's rows may attend
+    int klo, khi;
+    key_range(q0, BM, L, a.causal, a.window, &klo, &khi);
+    const int ch0 = klo / CK, ch1 = (khi + CK - 1) / CK;
+    int wlo, whi;
+    key_range(q0 + 16 * wv, 16, L, a.causal, a.window, &wlo, &whi);
+    const int khi_i = qrow;                                   // causal: key <= query
+    const int klo_i = a.window > 0 ? qrow - a.window : -1;    // window: key > query - W
+
+    QFrag<DT, D> qf;
+    qf.load(qh, qrow, L, g);
+
+    // ---- chunk streaming ----------------------------------------------------------
+    struct Pre {
+        u32x4 k[NPC];
+        u32x4 v[NPC];
+        uint8_t mb;
+    };
+    auto prefetch = [&](int ch, bool withv, Pre& p) {
+        const int cb = ch * CK;
+        p.mb = kmp[hasm ? clamp_row(cb + lane, L) : 0];   // no branch around the load
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int pc = tid + kThreads * j;
+            const size_t off = static_cast<size_t>(clamp_row(cb + pc / CPR, L)) * D + (pc % CPR) * EPC;
+            p.k[j] = *reinterpret_cast<const u32x4*>(kh + off);
+            if (withv) p.v[j] = *reinterpret_cast<const u32x4*>(vh + off);
+        }
+    };
+    auto stage = [&](int buf, bool withv, const Pre& p) {
+        char* kb = Kb + buf * C::k_bytes;
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int pc = tid + kThreads * j;
+            *reinterpret_cast<u32x4*>(kb + (pc / CPR) * C::KSTR + (pc % CPR) * 16) = p.k[j];
+        }
+        if (withv) {
+            char* vb = Vb + buf * C::v_bytes;
+#pragma unroll
+            for (int j = 0; j < NPC; ++j) {
+                const int pc = tid + kThreads * j;
+                const int key = pc / CPR, d0 = (pc % CPR) * EPC;
+                if constexpr (DT == DT_BF16) {
+                    *reinterpret_cast<u32x4*>(vb + key * C::VRS + d0 * 2) = p.v[j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e)
+                        reinterpret_cast<float*>(vb)[(d0 + e) * C::VSTR + key] = __uint_as_float(p.v[j][e]);
+                }
+            }
+        }
+    };
+    // One pass over the span: fn(ch, kbuf, vbuf, M) for every chunk, M = the
+    // chunk's valid-key bits (uniform).  The loads of a chunk are issued two
+    // chunks ahead (register sets pa / pb, used alternately with the two LDS
+    // buffers), so that two chunks of work cover their latency.  The
+    // workgroup stays in step: one barrier per chunk.
+    auto valid_bits = [&](int ch, const Pre& p) {
+        return __ballot((ch * CK + lane < L) & (!hasm | (p.mb != 0)));
+    };
+    auto stream = [&](bool withv, auto&& fn) {
+        if (ch0 >= ch1) return;
+        Pre pa, pb;
+        prefetch(ch0, withv, pa);
+        if (ch0 + 1 < ch1) prefetch(ch0 + 1, withv, pb);
+        stage(0, withv, pa);
+        unsigned long long Ma = valid_bits(ch0, pa), Mb = 0ull;
+        __syncthreads();
+        for (int ch = ch0; ch < ch1; ch += 2) {
+            // chunk ch sits in buffer 0; chunk ch + 1 is in flight in pb
+            if (ch + 2 < ch1) prefetch(ch + 2, withv, pa);
+            fn(ch, Kb, Vb, Ma);
+            if (ch + 1 < ch1) {
+                stage(1, withv, pb);
+                Mb = valid_bits(ch + 1, pb);
+            }
+            __syncthreads();
+            if (ch + 1 >= ch1) break;
+            // chunk ch + 1 sits in buffer 1; chunk ch + 2 is in flight in pa
+            if (ch + 3 < ch1) prefetch(ch + 3, withv, pb);
+            fn(ch + 1, Kb + C::k_bytes, Vb + C::v_bytes, Mb);
+            if (ch + 2 < ch1) {
+                stage(0, withv, pa);
+                Ma = valid_bits(ch + 2, pa);
+            }
+            __syncthreads();
+        }
+    };
+    // S^T tiles of one chunk for this wave (raw accumulators, masked keys
+    // -1e30 through the bias step, causal / window entries -inf), or -inf
+    // for tiles outside the wave's keys.  ok(t): tile computed.
+    constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
+    auto tiles = [&](int ch, const char* kb, unsigned long long M, f32x4 (&sv)[NTC], bool (&ok)[NTC]) {
+        const int cb = ch * CK;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            sv[t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+            const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
+            ok[t] = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
+            if (!ok[t]) continue;
+            KFrag<DT, D> kf;
+            kf.load_lds(kb + (16 * t + c) * C::KSTR, g);
+            sv[t] = mb == 0xFFFFu ? kf.st(qf) : kf.st_bias(qf, ((mb >> c) & 1u) ? 0u : kMaskedBits, g);
+            if (a.causal) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = cb + 16 * t + 4 * g + i;
+                    sv[t][i] = (key <= khi_i) & (key > klo_i) ? sv[t][i] : -kInf;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[t][i] = rowok ? sv[t][i] : -kInf;
+        }
+    };
+
+    const float c2 = 0.5f * a.scale;
+
+    // ---- A. row max, allowed count, candidate estimate ---------------------------
+    // cand: entries above (running row max - 2) in score units, i.e. x > -1
+    // against the row max seen so far -- an over-count of the final one
+    float mlane = -kInf, nl = 0.f, cand = 0.f, mrun = -kInf;
+    const float thr_raw = 2.f / a.scale;
+    stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+        f32x4 sv[NTC];
+        bool ok[NTC];
+        tiles(ch, kb, M, sv, ok);
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            if (!ok[t]) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mlane = fmaxf(mlane, sv[t][i]);
+        }
+        mrun = col4_max(mlane);
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            if (!ok[t]) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = sv[t][i];
+                nl += s > -1e29f ? 1.f : 0.f;
+                cand += s > mrun - thr_raw ? 1.f : 0.f;
+            }
+        }
+    });
+    const float mrow = col4_max(mlane);
+    const float n = col4_sum(nl);
+    const bool empty = n == 0.f;
+    const float mc2 = empty ? 0.f : mrow * c2;
+
+    ColState s;
+    s.lb = fmaxf(col_lower_bound(fmaf(mlane, c2, -mc2)), -1.f);
+    s.lo = -1.f;
+    s.hi = -__builtin_amdgcn_rsqf(empty ? 1.f : n);
+    s.it = 0;
+
+    // workgroup-wide vote (uniform result)
+    auto vote_any = [&](bool v) {
+        if (tid == 0) *flag = 0;
+        __syncthreads();
+        if (__any(v) && lane == 0) atomicOr(flag, 1);
+        __syncthreads();
+        const int r = *flag;
+        __syncthreads();
+        return r != 0;
+    };
+
+    // ---- C. three bisection levels per pass -------------------------------------
+    auto pass_c = [&]() -> int {
+        // the seven midpoints of the next three levels, as the steps would form them
+        const float lo = s.lo, hi = s.hi;
+        const float p4 = 0.5f * (lo + hi);
+        const float p2 = 0.5f * (lo + p4), p6 = 0.5f * (p4 + hi);
+        const float p1 = 0.5f * (lo + p2), p3 = 0.5f * (p2 + p4), p5 = 0.5f * (p4 + p6), p7 = 0.5f * (p6 + hi);
+        const float pts[7] = {p1, p2, p3, p4, p5, p6, p7};
+        // per lane: g parts and the number of entries above each point
+        float acc[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int cnt[7] = {0, 0, 0, 0, 0, 0, 0};
+        const float lo_eff = fmaxf(lo, s.lb);   // entries at or below it are never listed
+        int cnt_lo = 0, cnt_hi = 0;
+        stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+            f32x4 sv[NTC];
+            bool ok[NTC];
+            tiles(ch, kb, M, sv, ok);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                if (!ok[t]) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = fmaf(sv[t][i], c2, -mc2);
+#pragma unroll
+                    for (int k = 0; k < 7; ++k) {
+                        const float y = relu1(x - pts[k]);
+                        acc[k] = fmaf(y, y, acc[k]);
+                        cnt[k] += x > pts[k] ? 1 : 0;
+                    }
+                    cnt_lo += x > lo_eff ? 1 : 0;
+                    cnt_hi += x > hi ? 1 : 0;
+                }
+            }
+        });
+        float gk[7];
+#pragma unroll
+        for (int k = 0; k < 7; ++k) gk[k] = col4_sum(acc[k]);
+        // walk the tree: g > 1 (or a midpoint below lb) moves the lower end;
+        // track this lane's entries in the final cell (lo, hi]
+        int node = 3;   // p4
+        int above_lo = cnt_lo, above_hi = cnt_hi;   // entries above lo / above hi (this lane)
+#pragma unroll
+        for (int lev = 0; lev < 3; ++lev) {
+            if (s.it >= kIters) break;
+            const float mid = pts[node];
+            const bool up = gk[node] > 1.f || mid < s.lb;
+            if (up) {
+                s.lo = mid;
+                above_lo = cnt[node];
+            } else {
+                s.hi = mid;
+                above_hi = cnt[node];
+            }
+            ++s.it;
+            const int step = lev == 0 ? 2 : 1;
+            node = up ? node + step : node - step;
+        }
+        return above_lo - above_hi;   // band entries of this lane (an over-count while lo < lb)
+    };
+
+    // ---- B. band lists and U ---------------------------------------------------------
+    float* col = lists + wv * ((CAP + 1) * kWave) + lane;
+    int len = 0;
+    auto pass_b = [&]() {
+        s.hc = s.hi;
+        s.cnt = 0.f;
+        s.a1 = 0.f;
+        s.a2 = 0.f;
+        len = 0;
+        stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+            f32x4 sv[NTC];
+            bool ok[NTC];
+            tiles(ch, kb, M, sv, ok);
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+                if (!ok[t]) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = fmaf(sv[t][i], c2, -mc2);
+                    const float y = relu1(x - s.hi);
+                    s.cnt += x > s.hi ? 1.f : 0.f;
+                    s.a1 += y;
+                    s.a2 = fmaf(y, y, s.a2);
+                    col[(len < CAP ? len : CAP) * kWave] = x;   // row CAP: overflow dump
+                    len += (x > s.lo) & (x > s.lb) & (x <= s.hi) ? 1 : 0;
+                }
+            }
+        });
+    };
+
+    // ---- tau -----------------------------------------------------------------------------
+    // lists alias the V buffers, which pass D rewrites only after this
+    {
+        // pass C until the band of every lane fits its list (known from the
+        // counts), then pass B; a list that still overflows (the candidate
+        // estimate was used) sends the workgroup back to pass C
+        bool need_c = vote_any(cand > static_cast<float>(CAP));
+        for (;;) {
+            while (need_c && s.it < kIters) need_c = vote_any(pass_c() > CAP);
+            if (s.it >= kIters) break;   // uniform: every row has taken all steps
+            pass_b();
+            if (!vote_any(len > CAP)) break;
+            need_c = true;
+        }
+    }
+    float tr;
+    if (s.it >= kIters) tr = 0.5f * (s.lo + s.hi);
+    else tr = col_finish<CAP>(col, len, s);
+    if (a.tau != nullptr && g == 0 && rowok) a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tr);
+    const float sh = empty ? 0.f : mc2 + tr;
+    __syncthreads();   // lists done: the region holds V from now on
+
+    // ---- D. O = P V ----------------------------------------------------------------------
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream(true, [&](int ch, const char* kb, const char* vb, unsigned long long M) {
+        f32x4 sv[NTC];
+        bool ok[NTC];
+        tiles(ch, kb, M, sv, ok);
+        f32x4 p[NTC];
+        bool nz = false;
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y = relu1(fmaf(sv[t][i], c2, -sh));
+                p[t][i] = y * y;
+                nz |= y > 0.f;
+            }
+        }
+        if (!__any(nz)) return;   // uniform: nothing of this chunk reaches the wave's rows
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+            for (int h = 0; h < NTC / 2; ++h) {
+                bf16x8 phi, plo;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float pv = i < 4 ? p[2 * h][i] : p[2 * h + 1][i - 4];
+                    const __bf16 hb = static_cast<__bf16>(pv);
+                    phi[i] = hb;
+                    plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
+                }
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    // B operand through transpose loads (see the short-span kernel)
+                    const char* src = vb + (32 * h + 4 * g + (c >> 2)) * C::VRS + (16 * ct + 4 * (c & 3)) * 2;
+                    const s16x4 r0 = ds_read_tr16(src);
+                    const s16x4 r1 = ds_read_tr16(src + 16 * C::VRS);
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, s16x8{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]});
+                    o[ct] = mfma_bf16(phi, bv, o[ct]);
+                    o[ct] = mfma_bf16(plo, bv, o[ct]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NTC; ++t) {
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    const f32x4 bv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(vb) + (16 * ct + c) * C::VSTR + 16 * t + 4 * g);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[ct] = mfma_f32(p[t][q], bv[q], o[ct]);
+                }
+            }
+        }
+    });
+
+    float* outh = a.out + head_off;
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = q0 + 16 * wv + 4 * g + i;
+            if (row < L) outh[static_cast<size_t>(row) * D + 16 * ct + c] = o[ct][i];
+        }
+}
+
+}  // namespace ea

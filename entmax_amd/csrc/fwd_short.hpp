@@ -28,7 +28,6 @@
 #include <type_traits>
 
 #include "common.hpp"
-#include "fwd_dense.hpp"
 #include "col_solve.hpp"
 
 namespace ea {

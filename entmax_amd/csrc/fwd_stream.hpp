@@ -19,7 +19,6 @@
 #pragma once
 
 #include "common.hpp"
-#include "fwd_dense.hpp"
 #include "tau_solver.hpp"
 
 namespace ea {

@@ -84,6 +84,16 @@ def test_ragged_bidirectional(dtype, d, L):
     check_forward(inp, label=f"ragged L{L}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gain", [0.05, 0.2, 0.3, 0.5])
+@pytest.mark.parametrize("L", [300, 600])
+def test_dense_supports_long(dtype, gain, L):
+    # low-variance rows: hundreds of keys in the support, band lists near and
+    # over capacity on the long-span path
+    inp = random_inputs(1, 2, L, 64, dtype, seed=int(gain * 100) + L, qk_gain=gain)
+    check_forward(inp, label=f"dense support gain{gain} L{L}")
+
+
 @pytest.mark.parametrize("causal,window", [(True, 0), (True, 1), (True, 5), (True, 32), (True, 100)])
 @pytest.mark.parametrize("L", [50, 300, 1100])
 def test_causal_and_window(causal, window, L):
