@@ -7,19 +7,24 @@
 //   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
 //   dV_j = sum_i p_ij dO_i.
 // Everything off the support is exactly zero, so only the scores need a
-// dense pass: one workgroup = 4 independent waves of 16 query rows; each
-// wave recomputes S tile by tile on MFMA (same tile code as the forward),
-// and handles every support entry as it appears:
-//   dp_ij by a gather of V_j and a 16-lane dot product with dO_i,
-//   sum w, sum w dp, X_i = sum w dp K_j and Y_i = sum w K_j,
-// so that dQ_i = scale (X_i - c_i Y_i) needs no second pass.  The entries
-// (key, w, dp) are kept in an LDS list; after c_i is known each entry adds
-// scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.  A row
-// whose support outgrows its list redoes the score pass for that step.
+// dense pass.  One workgroup = 4 waves of 16 query rows of one (batch, head);
+// lane (g, c) of a wave holds rows 4g .. 4g + 3 of each 16 x 16 score tile
+// (key c) and the d-slice [c D/16, (c + 1) D/16) of those rows' Q and dO.
+//   1. S is recomputed on MFMA from K chunks staged in LDS (chunk_stream.hpp)
+//      and every support entry (key, w) goes to its row's list in LDS.
+//   2. Per row, the entries are processed in batches whose V and K row
+//      gathers are all issued before any is used: dp by a 16-lane dot
+//      product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
+//      dQ_i = scale (X - c_i Y) without another pass; then every entry adds
+//      scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.
+// A row whose support outgrows its list is finished by two more passes over
+// the keys (all waves take part, only those rows do work): one for dp, the
+// sums, X and Y, one for the atomics once c_i is known.
 #pragma once
 
+#include "chunk_stream.hpp"
 #include "common.hpp"
-#include "fwd_stream.hpp"
+#include "fwd_short.hpp"
 #include "tau_solver.hpp"
 
 namespace ea {
@@ -40,10 +45,14 @@ struct BwdArgs {
     int nqt;
 };
 
-template <int CAP>
-struct BwdCfg {
+template <int DT, int D>
+struct BwdCfg : ChunkCfg<DT, D> {
+    typedef ChunkCfg<DT, D> S;
     static constexpr int BM = 64;
-    static constexpr size_t lds_bytes = static_cast<size_t>(BM) * CAP * (2 * sizeof(float) + sizeof(uint16_t));
+    static constexpr int CAP = 64;   // support entries per row
+    static constexpr int NB = 4;     // entries per gather batch
+    static constexpr size_t list_bytes = static_cast<size_t>(BM) * CAP * (2 * sizeof(float) + sizeof(uint16_t));
+    static constexpr size_t lds_bytes = 2 * S::k_bytes + list_bytes + 64;
 };
 
 template <int DT, int DPL>
@@ -76,15 +85,24 @@ __global__ void zero_fill_kernel(float* p, size_t n) {
     }
 }
 
-template <int DT, int D, int CAP>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
+// Rank of this lane among the set lanes of its 16-lane group in `mask`.
+__device__ __forceinline__ void group_rank16(unsigned long long mask, int g, int c, int* rank, int* total) {
+    const unsigned gm = static_cast<unsigned>((mask >> (16 * g)) & 0xFFFFull);
+    *rank = __popc(gm & ((1u << c) - 1u));
+    *total = __popc(gm);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
     typedef typename InT<DT>::type T;
-    constexpr int DPL = D / 16;
-    constexpr int BM = BwdCfg<CAP>::BM;
+    typedef BwdCfg<DT, D> C;
+    constexpr int DPL = D / 16, BM = C::BM, CAP = C::CAP, NB = C::NB, CK = C::S::CK;
     extern __shared__ float lds[];
-    float* lw = lds;                       // [BM][CAP] w
-    float* ldp = lw + BM * CAP;            // [BM][CAP] dp
-    uint16_t* lk = reinterpret_cast<uint16_t*>(ldp + BM * CAP);   // [BM][CAP] key
+    char* Kb = reinterpret_cast<char*>(lds);
+    float* lw = reinterpret_cast<float*>(Kb + 2 * C::S::k_bytes);    // [BM][CAP] w
+    float* ldp = lw + BM * CAP;                                       // [BM][CAP] dp
+    uint16_t* lk = reinterpret_cast<uint16_t*>(ldp + BM * CAP);       // [BM][CAP] key
+    int* flag = reinterpret_cast<int*>(lk + BM * CAP);                // workgroup vote
 
     const int total = a.B * a.H * a.nqt;
     const int wi = xcd_swizzle(blockIdx.x, total);
@@ -102,187 +120,278 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     float* dkh = a.dk + head_off;
     float* dvh = a.dv + head_off;
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
+    const bool hasm = km != nullptr;
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wv = tid / kWave;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane / 16, c = lane % 16;
     const int r0 = 16 * wv;
 
     int klo, khi;
-    key_range(q0 + r0, 16, L, a.causal, a.window, &klo, &khi);
-    const int kt0 = klo / kBN;
-    const int ntile = khi > klo ? (khi + kBN - 1) / kBN - kt0 : 0;
+    key_range(q0, BM, L, a.causal, a.window, &klo, &khi);
+    const int ch0 = klo / CK, ch1 = (khi + CK - 1) / CK;
+    int wlo, whi;
+    key_range(q0 + r0, 16, L, a.causal, a.window, &wlo, &whi);
+
+    ChunkStream<DT, D> cs;
+    cs.Kb = Kb;
+    cs.Vb = nullptr;
+    cs.kh = kh;
+    cs.vh = vh;
+    cs.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+    cs.hasm = hasm;
+    cs.L = L;
+    cs.tid = tid;
+    cs.lane = lane;
 
     QFrag<DT, D> qf;
     qf.load(qh, q0 + r0 + c, L, g);
 
-    float tau[4], dor[4][DPL], qr[4][DPL], X[4][DPL], Y[4][DPL], sw[4], swdp[4];
+    float tau[4];
     int cnt[4];
     bool ovf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = q0 + r0 + 4 * g + i;
-        const bool in = row < L;
-        tau[i] = in ? a.tau[static_cast<size_t>(bh) * L + row] : kInf;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) { dor[i][j] = 0.f; qr[i][j] = 0.f; X[i][j] = 0.f; Y[i][j] = 0.f; }
-        if (in) {
-            load_row_slice<DT, DPL>(doh + static_cast<size_t>(row) * D + DPL * c, dor[i]);
-            load_row_slice<DT, DPL>(qh + static_cast<size_t>(row) * D + DPL * c, qr[i]);
-        }
-        sw[i] = 0.f;
-        swdp[i] = 0.f;
+        tau[i] = row < L ? a.tau[static_cast<size_t>(bh) * L + clamp_row(row, L)] : kInf;
         cnt[i] = 0;
         ovf[i] = false;
     }
-
-    // key validity without a branch around the mask load (see common.hpp)
-    auto key_ok = [&](int key) {
-        const bool in = key < L;
-        if (km == nullptr) return in;
-        const uint8_t mb = km[clamp_row(key, L)];   // unconditional load
-        return in && mb != 0;
-    };
-    auto score = [&](int key, bool kv, const f32x4& acc, int i) {
-        const int row = q0 + r0 + 4 * g + i;
-        const bool ok = kv && row < L && allowed_ij(row, key, a.causal, a.window);
-        return ok ? acc[i] * a.scale : -kInf;
-    };
-    auto dot_dp = [&](int i, int key) {
-        float vr[DPL];
-        load_row_slice<DT, DPL>(vh + static_cast<size_t>(key) * D + DPL * c, vr);
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) part = fmaf(dor[i][j], vr[j], part);
-        return row_sum<16>(part);
-    };
-    // Insert this tile's support entries of row i at positions [base, ...).
-    auto insert = [&](int i, int base, const float (&s)[4][4], int kbase, bool active) {
-        const int rl = r0 + 4 * g + i;
-        int added = 0;
-#pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16) {
-            const float x = s[c16][i] - tau[i];
-            const bool pred = active && x > 0.f;
-            int rank, tot;
-            group_rank(__ballot(pred), g, c, &rank, &tot);
-            if (pred) {
-                lk[rl * CAP + base + added + rank] = static_cast<uint16_t>(kbase + 16 * c16 + c);
-                lw[rl * CAP + base + added + rank] = 0.5f * x;
-            }
-            added += tot;
-        }
-        return added;
+    // this lane's d-slice of dO and Q for row 4g + i (loaded when the row is processed)
+    float dor[DPL], qr[DPL];
+    auto load_row = [&](int i) {
+        const int row = clamp_row(q0 + r0 + 4 * g + i, L);
+        load_row_slice<DT, DPL>(doh + static_cast<size_t>(row) * D + DPL * c, dor);
+        load_row_slice<DT, DPL>(qh + static_cast<size_t>(row) * D + DPL * c, qr);
     };
 
-    // ---- pass 1: support, dp, row sums, X and Y ------------------------------
-    for (int t = 0; t < ntile; ++t) {
-        const int kbase = (kt0 + t) * kBN;
-        float s[4][4];
+    // Support entries of one chunk for this wave: calls put(i, e, key, w)
+    // for each (row 4g + i, key) with s > tau, e = its rank among this
+    // chunk's entries of that row (uniform count per 16-lane group via tot).
+    auto chunk_entries = [&](int ch, const char* kb, unsigned long long M, auto&& put) {
+        const int cb = ch * CK;
 #pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16) {
-            const int key = kbase + 16 * c16 + c;
-            const bool kv = key_ok(key);
-            const f32x4 acc = qf.tile(kh, key, L, g);
+        for (int t = 0; t < CK / 16; ++t) {
+            const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
+            if (mb == 0u || cb + 16 * t >= whi || cb + 16 * t + 16 <= wlo) continue;   // uniform
+            KFrag<DT, D> kf;
+            kf.load_lds(kb + (16 * t + c) * C::S::KSTR, g);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (DT == DT_BF16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
-        }
-        int from[4];
+                for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(qf.a[ks], kf.a[ks], acc);
+            } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (cnt[i] + kBN > CAP) {   // no room for a full tile: keep only a staging window
-                ovf[i] = true;
-                cnt[i] = 0;
+                for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc = mfma_f32(qf.a[u][s], kf.a[u][s], acc);
             }
-            from[i] = cnt[i];
-            cnt[i] += insert(i, cnt[i], s, kbase, true);
-        }
-        wave_sync();
+            float xs[4];
+            bool anyc = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
+                xs[i] = fmaf(acc[i], a.scale, -tau[i]);
+                anyc |= xs[i] > 0.f;
+            }
+            // most tiles of a long row hold no support entry at all: the
+            // masks and the list appends run only where one may be
+            if (!__any(anyc)) continue;   // uniform
+            const int key = cb + 16 * t + c;
+            const bool kv = ((mb >> c) & 1u) != 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = q0 + r0 + 4 * g + i;
+                const bool ok = kv & (row < L) & allowed_ij(row, key, a.causal, a.window);
+                const float x = xs[i];
+                const bool pred = ok & (x > 0.f);
+                int rank, tot;
+                group_rank16(__ballot(pred), g, c, &rank, &tot);
+                put(i, pred, rank, tot, key, 0.5f * x);
+            }
+        }
+    };
+
+    // ---- 1. lists --------------------------------------------------------------------
+    cs.run(ch0, ch1, false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+        chunk_entries(ch, kb, M, [&](int i, bool pred, int rank, int tot, int key, float w) {
             const int rl = r0 + 4 * g + i;
-            for (int e = from[i]; e < cnt[i]; ++e) {
-                const int key = lk[rl * CAP + e];
-                const float w = lw[rl * CAP + e];
-                const float dp = dot_dp(i, key);
-                if (c == 0) ldp[rl * CAP + e] = dp;
-                sw[i] += w;
-                swdp[i] = fmaf(w, dp, swdp[i]);
-                float kr[DPL];
-                load_row_slice<DT, DPL>(kh + static_cast<size_t>(key) * D + DPL * c, kr);
-                const float wdp = w * dp;
-#pragma unroll
-                for (int j = 0; j < DPL; ++j) {
-                    X[i][j] = fmaf(wdp, kr[j], X[i][j]);
-                    Y[i][j] = fmaf(w, kr[j], Y[i][j]);
-                }
+            const bool fits = !ovf[i] && cnt[i] + tot <= CAP;
+            if (pred && fits) {
+                lk[rl * CAP + cnt[i] + rank] = static_cast<uint16_t>(key);
+                lw[rl * CAP + cnt[i] + rank] = w;
             }
-        }
-        wave_sync();
-    }
+            ovf[i] = ovf[i] || !fits;
+            cnt[i] += fits ? tot : 0;
+        });
+    });
+    wave_sync();
 
-    // ---- dQ ------------------------------------------------------------------
-    float cc[4];
+    // dp of a batch of entries of row i: V and K row slices are all gathered first
+    auto batch = [&](int rl, int e0, int n, int (&key)[NB], float (&w)[NB], float (&dp)[NB], float (&kr)[NB][DPL]) {
+        float vr[NB][DPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        cc[i] = sw[i] > 0.f ? swdp[i] / sw[i] : 0.f;
-        const int row = q0 + r0 + 4 * g + i;
-        if (row < L) {
-            float* dst = dqh + static_cast<size_t>(row) * D + DPL * c;
-#pragma unroll
-            for (int j = 0; j < DPL; j += 4)
-                *reinterpret_cast<f32x4*>(dst + j) =
-                    f32x4{a.scale * fmaf(-cc[i], Y[i][j], X[i][j]), a.scale * fmaf(-cc[i], Y[i][j + 1], X[i][j + 1]),
-                          a.scale * fmaf(-cc[i], Y[i][j + 2], X[i][j + 2]), a.scale * fmaf(-cc[i], Y[i][j + 3], X[i][j + 3])};
+        for (int j = 0; j < NB; ++j) {
+            const int e = e0 + j;
+            const bool in = e < n;
+            key[j] = in ? static_cast<int>(lk[rl * CAP + (in ? e : 0)]) : 0;
+            w[j] = in ? lw[rl * CAP + (in ? e : 0)] : 0.f;
         }
-    }
-
-    // ---- pass 2: scatter dK, dV -----------------------------------------------
-    auto scatter = [&](int i, int key, float w, float dp) {
-        const float ds = a.scale * w * (dp - cc[i]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            load_row_slice<DT, DPL>(vh + static_cast<size_t>(key[j]) * D + DPL * c, vr[j]);
+            load_row_slice<DT, DPL>(kh + static_cast<size_t>(key[j]) * D + DPL * c, kr[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            float part = 0.f;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) part = fmaf(dor[d], vr[j][d], part);
+            dp[j] = row_sum<16>(part);
+        }
+    };
+    auto scatter = [&](int key, float w, float dp, float cc) {
+        const float ds = a.scale * w * (dp - cc);
         const float p = w * w;
         float* dkr = dkh + static_cast<size_t>(key) * D + DPL * c;
         float* dvr = dvh + static_cast<size_t>(key) * D + DPL * c;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-            unsafeAtomicAdd(dkr + j, ds * qr[i][j]);
-            unsafeAtomicAdd(dvr + j, p * dor[i][j]);
+        for (int d = 0; d < DPL; ++d) {
+            unsafeAtomicAdd(dkr + d, ds * qr[d]);
+            unsafeAtomicAdd(dvr + d, p * dor[d]);
         }
     };
+    // The same through LDS (the K buffers, idle after the first pass): the
+    // 16 lanes of a group first write their d-slices of one entry's dK and
+    // dV rows, then each atomic instruction covers 16 consecutive floats of
+    // a row (lane c: floats c, c + 16, ...), which the L2 processes far
+    // faster than 16 scattered ones.  Called by the whole wave.
+    float* stg = reinterpret_cast<float*>(Kb) + wv * (8 * D) + g * (2 * D);
+    auto scatter_staged = [&](bool act, int rl, int e, float cc) {
+        const int ee = act ? e : 0;
+        const int key = lk[rl * CAP + ee];
+        const float w = lw[rl * CAP + ee], dp = ldp[rl * CAP + ee];
+        const float ds = act ? a.scale * w * (dp - cc) : 0.f;
+        const float p = act ? w * w : 0.f;
+#pragma unroll
+        for (int d = 0; d < DPL; d += 4) {
+            *reinterpret_cast<f32x4*>(stg + DPL * c + d) = f32x4{ds * qr[d], ds * qr[d + 1], ds * qr[d + 2], ds * qr[d + 3]};
+            *reinterpret_cast<f32x4*>(stg + D + DPL * c + d) = f32x4{p * dor[d], p * dor[d + 1], p * dor[d + 2], p * dor[d + 3]};
+        }
+        wave_sync();
+        if (act) {
+            float* dkr = dkh + static_cast<size_t>(key) * D + c;
+            float* dvr = dvh + static_cast<size_t>(key) * D + c;
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) {
+                unsafeAtomicAdd(dkr + 16 * j, stg[c + 16 * j]);
+                unsafeAtomicAdd(dvr + 16 * j, stg[D + c + 16 * j]);
+            }
+        }
+        wave_sync();
+    };
+    auto store_dq = [&](int i, float cc, const float (&X)[DPL], const float (&Y)[DPL]) {
+        const int row = q0 + r0 + 4 * g + i;
+        if (row < L) {
+            float* dst = dqh + static_cast<size_t>(row) * D + DPL * c;
+#pragma unroll
+            for (int d = 0; d < DPL; d += 4)
+                *reinterpret_cast<f32x4*>(dst + d) =
+                    f32x4{a.scale * fmaf(-cc, Y[d], X[d]), a.scale * fmaf(-cc, Y[d + 1], X[d + 1]),
+                          a.scale * fmaf(-cc, Y[d + 2], X[d + 2]), a.scale * fmaf(-cc, Y[d + 3], X[d + 3])};
+        }
+    };
+
+    // ---- 2. rows whose lists hold the whole support -------------------------------------
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (ovf[i]) continue;
         const int rl = r0 + 4 * g + i;
-        for (int e = 0; e < cnt[i]; ++e) scatter(i, lk[rl * CAP + e], lw[rl * CAP + e], ldp[rl * CAP + e]);
-    }
-    const bool my_ovf = ovf[0] || ovf[1] || ovf[2] || ovf[3];
-    if (__any(my_ovf)) {
-        wave_sync();
-        for (int t = 0; t < ntile; ++t) {
-            const int kbase = (kt0 + t) * kBN;
-            float s[4][4];
+        const int n = ovf[i] ? 0 : cnt[i];   // uniform in the 16-lane group
+        // (rows without entries still store dQ = 0; the gathers are skipped)
+        if (__any(n > 0)) load_row(i);
+        float X[DPL], Y[DPL], sw = 0.f, swdp = 0.f;
 #pragma unroll
-            for (int c16 = 0; c16 < 4; ++c16) {
-                const int key = kbase + 16 * c16 + c;
-                const bool kv = key_ok(key);
-                const f32x4 acc = qf.tile(kh, key, L, g);
+        for (int d = 0; d < DPL; ++d) { X[d] = 0.f; Y[d] = 0.f; }
+        for (int e0 = 0; __any(e0 < n); e0 += NB) {
+            int key[NB];
+            float w[NB], dp[NB], kr[NB][DPL];
+            batch(rl, e0, n, key, w, dp, kr);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
-            }
-            int n_in[4];
+            for (int j = 0; j < NB; ++j) {
+                if (c == 0 && e0 + j < n) ldp[rl * CAP + e0 + j] = dp[j];
+                sw += w[j];
+                swdp = fmaf(w[j], dp[j], swdp);
+                const float wdp = w[j] * dp[j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) n_in[i] = insert(i, 0, s, kbase, ovf[i]);
-            wave_sync();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rl = r0 + 4 * g + i;
-                for (int e = 0; e < n_in[i]; ++e) {
-                    const int key = lk[rl * CAP + e];
-                    const float w = lw[rl * CAP + e];
-                    scatter(i, key, w, dot_dp(i, key));
+                for (int d = 0; d < DPL; ++d) {
+                    X[d] = fmaf(wdp, kr[j][d], X[d]);
+                    Y[d] = fmaf(w[j], kr[j][d], Y[d]);
                 }
             }
-            wave_sync();
+        }
+        const float cc = sw > 0.f ? swdp / sw : 0.f;
+        if (!ovf[i]) store_dq(i, cc, X, Y);
+        wave_sync();   // the dp of this row are in LDS
+        for (int e = 0; __any(e < n); ++e) {
+            scatter_staged(e < n, rl, e, cc);
+        }
+    }
+
+    // ---- 3. rows with more support than their list --------------------------------------
+    // workgroup-wide vote (the passes below stream keys for every wave)
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (__any(ovf[0] || ovf[1] || ovf[2] || ovf[3]) && lane == 0) atomicOr(flag, 1);
+    __syncthreads();
+    if (*flag == 0) return;   // uniform
+
+    // One row index i at a time (two passes each: sums, then atomics); per
+    // chunk, the overflowed rows' entries of that chunk use the list as a
+    // staging window (at most CK per row).
+    for (int i = 0; i < 4; ++i) {
+        load_row(i);
+        const int rl = r0 + 4 * g + i;
+        float X[DPL], Y[DPL], sw = 0.f, swdp = 0.f, cc = 0.f;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) { X[d] = 0.f; Y[d] = 0.f; }
+        for (int pass = 0; pass < 2; ++pass) {
+            cs.run(ch0, ch1, false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+                int n = 0;
+                chunk_entries(ch, kb, M, [&](int ii, bool pred, int rank, int tot, int key, float w) {
+                    if (ii != i) return;
+                    if (pred && ovf[i]) {
+                        lk[rl * CAP + n + rank] = static_cast<uint16_t>(key);
+                        lw[rl * CAP + n + rank] = w;
+                    }
+                    n += ovf[i] ? tot : 0;
+                });
+                wave_sync();
+                for (int e0 = 0; __any(e0 < n); e0 += NB) {
+                    int key[NB];
+                    float w[NB], dp[NB], kr[NB][DPL];
+                    batch(rl, e0, n, key, w, dp, kr);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        if (pass == 0) {
+                            sw += w[j];
+                            swdp = fmaf(w[j], dp[j], swdp);
+                            const float wdp = w[j] * dp[j];
+#pragma unroll
+                            for (int d = 0; d < DPL; ++d) {
+                                X[d] = fmaf(wdp, kr[j][d], X[d]);
+                                Y[d] = fmaf(w[j], kr[j][d], Y[d]);
+                            }
+                        } else if (e0 + j < n) {
+                            scatter(key[j], w[j], dp[j], cc);
+                        }
+                    }
+                }
+                wave_sync();
+            });
+            if (pass == 0) {
+                cc = sw > 0.f ? swdp / sw : 0.f;
+                if (ovf[i]) store_dq(i, cc, X, Y);
+            }
         }
     }
 }

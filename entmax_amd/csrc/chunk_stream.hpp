@@ -1,0 +1,121 @@
+// Streaming a head's keys through LDS in chunks of 64, for kernels whose key
+// span is too long to hold at once.
+//
+// Every chunk of K (and, on request, V) is loaded once per workgroup with
+// 16-byte pieces (consecutive threads on consecutive pieces), staged in one
+// of two LDS buffers and shared by the four waves.  A chunk's loads are
+// issued two chunks ahead (register sets used alternately), so two chunks of
+// work cover their latency; the workgroup advances in step, one barrier per
+// chunk.  Rows past L are clamped to valid ones (their scores are masked by
+// the caller); the valid-key bits of a chunk (key < L and key mask) come
+// with it as a 64-bit ballot, one key per lane.
+#pragma once
+
+#include "common.hpp"
+
+namespace ea {
+
+template <int DT, int D>
+struct ChunkCfg {
+    static constexpr int CK = 64;                     // keys per chunk
+    static constexpr int ESZ = DT == DT_BF16 ? 2 : 4;
+    static constexpr int EPC = 16 / ESZ;              // elements per 16-byte piece
+    static constexpr int CPR = D / EPC;               // pieces per row
+    static constexpr int NPC = CK * CPR / kThreads;   // pieces per thread per chunk
+    static constexpr int KSTR = D * ESZ + 16;         // K row stride in LDS (bytes)
+    static constexpr int k_bytes = CK * KSTR;         // one K buffer
+    static constexpr int VRS = D * 2 + 32;            // bf16: V row stride (bytes), row-major
+    static constexpr int VSTR = CK + EPC;             // fp32: V^T row stride (elements)
+    static constexpr int v_bytes = DT == DT_BF16 ? CK * VRS : D * VSTR * 4;
+    static_assert(NPC >= 1 && CK == kWave, "whole pieces per thread; one key per lane");
+};
+
+template <int DT, int D>
+struct ChunkStream {
+    typedef typename InT<DT>::type T;
+    typedef ChunkCfg<DT, D> C;
+    char* Kb;              // 2 K buffers (row-major, stride KSTR)
+    char* Vb;              // 2 V buffers (bf16 row-major, fp32 transposed)
+    const T* kh;
+    const T* vh;
+    const uint8_t* kmp;    // key mask of the batch (or any readable byte when !hasm)
+    bool hasm;
+    int L, tid, lane;
+
+    struct Pre {
+        u32x4 k[C::NPC];
+        u32x4 v[C::NPC];
+        uint8_t mb;
+    };
+
+    __device__ __forceinline__ void prefetch(int ch, bool withv, Pre& p) const {
+        const int cb = ch * C::CK;
+        p.mb = kmp[hasm ? clamp_row(cb + lane, L) : 0];   // no branch around the load
+#pragma unroll
+        for (int j = 0; j < C::NPC; ++j) {
+            const int pc = tid + kThreads * j;
+            const size_t off = static_cast<size_t>(clamp_row(cb + pc / C::CPR, L)) * D + (pc % C::CPR) * C::EPC;
+            p.k[j] = *reinterpret_cast<const u32x4*>(kh + off);
+            if (withv) p.v[j] = *reinterpret_cast<const u32x4*>(vh + off);
+        }
+    }
+    __device__ __forceinline__ void stage(int buf, bool withv, const Pre& p) const {
+        char* kb = Kb + buf * C::k_bytes;
+#pragma unroll
+        for (int j = 0; j < C::NPC; ++j) {
+            const int pc = tid + kThreads * j;
+            *reinterpret_cast<u32x4*>(kb + (pc / C::CPR) * C::KSTR + (pc % C::CPR) * 16) = p.k[j];
+        }
+        if (withv) {
+            char* vb = Vb + buf * C::v_bytes;
+#pragma unroll
+            for (int j = 0; j < C::NPC; ++j) {
+                const int pc = tid + kThreads * j;
+                const int key = pc / C::CPR, d0 = (pc % C::CPR) * C::EPC;
+                if constexpr (DT == DT_BF16) {
+                    *reinterpret_cast<u32x4*>(vb + key * C::VRS + d0 * 2) = p.v[j];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < C::EPC; ++e)
+                        reinterpret_cast<float*>(vb)[(d0 + e) * C::VSTR + key] = __uint_as_float(p.v[j][e]);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ unsigned long long valid_bits(int ch, const Pre& p) const {
+        return __ballot((ch * C::CK + lane < L) & (!hasm | (p.mb != 0)));
+    }
+    // fn(ch, kbuf, vbuf, M) for every chunk of [ch0, ch1), in order.  Every
+    // thread of the workgroup must call this with the same arguments.
+    template <typename F>
+    __device__ __forceinline__ void run(int ch0, int ch1, bool withv, F&& fn) const {
+        if (ch0 >= ch1) return;
+        Pre pa, pb;
+        prefetch(ch0, withv, pa);
+        if (ch0 + 1 < ch1) prefetch(ch0 + 1, withv, pb);
+        stage(0, withv, pa);
+        unsigned long long Ma = valid_bits(ch0, pa), Mb = 0ull;
+        __syncthreads();
+        for (int ch = ch0; ch < ch1; ch += 2) {
+            // chunk ch sits in buffer 0; chunk ch + 1 is in flight in pb
+            if (ch + 2 < ch1) prefetch(ch + 2, withv, pa);
+            fn(ch, Kb, Vb, Ma);
+            if (ch + 1 < ch1) {
+                stage(1, withv, pb);
+                Mb = valid_bits(ch + 1, pb);
+            }
+            __syncthreads();
+            if (ch + 1 >= ch1) break;
+            // chunk ch + 1 sits in buffer 1; chunk ch + 2 is in flight in pa
+            if (ch + 3 < ch1) prefetch(ch + 3, withv, pb);
+            fn(ch + 1, Kb + C::k_bytes, Vb + C::v_bytes, Mb);
+            if (ch + 2 < ch1) {
+                stage(0, withv, pa);
+                Ma = valid_bits(ch + 2, pa);
+            }
+            __syncthreads();
+        }
+    }
+};
+
+}  // namespace ea

@@ -146,6 +146,12 @@ template <int D> struct QFrag<DT_F32, D> {
     }
 };
 
+// Orders this wave's LDS writes before its later reads by other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Forward launch arguments (device pointers; see the C header for layouts).
 struct FwdArgs {
     const void* q;

@@ -126,9 +126,8 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
 
 template <int DT, int D>
 int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
-    constexpr int CAP = 128;
-    auto kern = ea::bwd_kernel<DT, D, CAP>;
-    const size_t lds = ea::BwdCfg<CAP>::lds_bytes;
+    auto kern = ea::bwd_kernel<DT, D>;
+    const size_t lds = ea::BwdCfg<DT, D>::lds_bytes;
     int rc = set_lds(kern, lds);
     if (rc) return rc;
     const size_t n = static_cast<size_t>(a.B) * a.H * a.L * D;

@@ -29,6 +29,7 @@
 
 #include <type_traits>
 
+#include "chunk_stream.hpp"
 #include "col_solve.hpp"
 #include "common.hpp"
 #include "fwd_short.hpp"
@@ -36,38 +37,28 @@
 namespace ea {
 
 template <int DT, int D>
-struct LongCfg {
+struct LongCfg : ChunkCfg<DT, D> {
+    typedef ChunkCfg<DT, D> S;
     static constexpr int BM = 64;
-    static constexpr int CK = 64;                     // keys per chunk
-    static constexpr int NTC = CK / 16;               // 16-key tiles per chunk
-    static constexpr int ESZ = DT == DT_BF16 ? 2 : 4;
-    static constexpr int EPC = 16 / ESZ;              // elements per 16-byte piece
-    static constexpr int CPR = D / EPC;               // pieces per row
-    static constexpr int NPC = CK * CPR / kThreads;   // pieces per thread per chunk (K or V)
-    static constexpr int KSTR = D * ESZ + 16;         // K row stride in LDS (bytes)
-    static constexpr int k_bytes = CK * KSTR;         // one K buffer
-    static constexpr int VRS = D * 2 + 32;            // bf16: V row stride (bytes)
-    static constexpr int VSTR = CK + EPC;             // fp32: V^T row stride (elements)
-    static constexpr int v_bytes = DT == DT_BF16 ? CK * VRS : D * VSTR * 4;   // one V buffer
+    static constexpr int NTC = S::CK / 16;            // 16-key tiles per chunk
     static constexpr int CAP = 32;                    // band entries per lane
     // one more row: where the branch-free appends land once a list is full
     static constexpr int list_bytes = 4 * (CAP + 1) * kWave * 4;
     // the band lists (passes B, solve) and the V buffers (pass D) share a region
-    static constexpr int vl_bytes = 2 * v_bytes > list_bytes ? 2 * v_bytes : list_bytes;
-    static constexpr size_t lds_bytes = static_cast<size_t>(2 * k_bytes) + vl_bytes + 64;
+    static constexpr int vl_bytes = 2 * S::v_bytes > list_bytes ? 2 * S::v_bytes : list_bytes;
+    static constexpr size_t lds_bytes = static_cast<size_t>(2 * S::k_bytes) + vl_bytes + 64;
     static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? 3 : (DT == DT_F32 && D == 128) ? 1 : 2;
-    static_assert(NPC >= 1 && CK == kWave, "whole pieces per thread; one mask byte per lane and chunk");
 };
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef LongCfg<DT, D> C;
-    constexpr int BM = C::BM, CK = C::CK, NTC = C::NTC, EPC = C::EPC, CPR = C::CPR, NPC = C::NPC;
+    constexpr int BM = C::BM, CK = C::CK, NTC = C::NTC;
     constexpr int CAP = C::CAP;
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);                           // 2 K buffers
-    char* Vb = Kb + 2 * C::k_bytes;                                    // 2 V buffers (pass D)
+    char* Vb = Kb + 2 * C::S::k_bytes;                                    // 2 V buffers (pass D)
     float* lists = reinterpret_cast<float*>(Vb);                       // band lists (B, solve)
     int* flag = reinterpret_cast<int*>(Vb + C::vl_bytes);              // workgroup-wide vote
 
@@ -105,82 +96,18 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     QFrag<DT, D> qf;
     qf.load(qh, qrow, L, g);
 
-    // ---- chunk streaming ----------------------------------------------------------
-    struct Pre {
-        u32x4 k[NPC];
-        u32x4 v[NPC];
-        uint8_t mb;
-    };
-    auto prefetch = [&](int ch, bool withv, Pre& p) {
-        const int cb = ch * CK;
-        p.mb = kmp[hasm ? clamp_row(cb + lane, L) : 0];   // no branch around the load
-#pragma unroll
-        for (int j = 0; j < NPC; ++j) {
-            const int pc = tid + kThreads * j;
-            const size_t off = static_cast<size_t>(clamp_row(cb + pc / CPR, L)) * D + (pc % CPR) * EPC;
-            p.k[j] = *reinterpret_cast<const u32x4*>(kh + off);
-            if (withv) p.v[j] = *reinterpret_cast<const u32x4*>(vh + off);
-        }
-    };
-    auto stage = [&](int buf, bool withv, const Pre& p) {
-        char* kb = Kb + buf * C::k_bytes;
-#pragma unroll
-        for (int j = 0; j < NPC; ++j) {
-            const int pc = tid + kThreads * j;
-            *reinterpret_cast<u32x4*>(kb + (pc / CPR) * C::KSTR + (pc % CPR) * 16) = p.k[j];
-        }
-        if (withv) {
-            char* vb = Vb + buf * C::v_bytes;
-#pragma unroll
-            for (int j = 0; j < NPC; ++j) {
-                const int pc = tid + kThreads * j;
-                const int key = pc / CPR, d0 = (pc % CPR) * EPC;
-                if constexpr (DT == DT_BF16) {
-                    *reinterpret_cast<u32x4*>(vb + key * C::VRS + d0 * 2) = p.v[j];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e)
-                        reinterpret_cast<float*>(vb)[(d0 + e) * C::VSTR + key] = __uint_as_float(p.v[j][e]);
-                }
-            }
-        }
-    };
-    // One pass over the span: fn(ch, kbuf, vbuf, M) for every chunk, M = the
-    // chunk's valid-key bits (uniform).  The loads of a chunk are issued two
-    // chunks ahead (register sets pa / pb, used alternately with the two LDS
-    // buffers), so that two chunks of work cover their latency.  The
-    // workgroup stays in step: one barrier per chunk.
-    auto valid_bits = [&](int ch, const Pre& p) {
-        return __ballot((ch * CK + lane < L) & (!hasm | (p.mb != 0)));
-    };
-    auto stream = [&](bool withv, auto&& fn) {
-        if (ch0 >= ch1) return;
-        Pre pa, pb;
-        prefetch(ch0, withv, pa);
-        if (ch0 + 1 < ch1) prefetch(ch0 + 1, withv, pb);
-        stage(0, withv, pa);
-        unsigned long long Ma = valid_bits(ch0, pa), Mb = 0ull;
-        __syncthreads();
-        for (int ch = ch0; ch < ch1; ch += 2) {
-            // chunk ch sits in buffer 0; chunk ch + 1 is in flight in pb
-            if (ch + 2 < ch1) prefetch(ch + 2, withv, pa);
-            fn(ch, Kb, Vb, Ma);
-            if (ch + 1 < ch1) {
-                stage(1, withv, pb);
-                Mb = valid_bits(ch + 1, pb);
-            }
-            __syncthreads();
-            if (ch + 1 >= ch1) break;
-            // chunk ch + 1 sits in buffer 1; chunk ch + 2 is in flight in pa
-            if (ch + 3 < ch1) prefetch(ch + 3, withv, pb);
-            fn(ch + 1, Kb + C::k_bytes, Vb + C::v_bytes, Mb);
-            if (ch + 2 < ch1) {
-                stage(0, withv, pa);
-                Ma = valid_bits(ch + 2, pa);
-            }
-            __syncthreads();
-        }
-    };
+    // ---- chunk streaming (chunk_stream.hpp) ---------------------------------------
+    ChunkStream<DT, D> cs;
+    cs.Kb = Kb;
+    cs.Vb = Vb;
+    cs.kh = kh;
+    cs.vh = vh;
+    cs.kmp = kmp;
+    cs.hasm = hasm;
+    cs.L = L;
+    cs.tid = tid;
+    cs.lane = lane;
+    auto stream = [&](bool withv, auto&& fn) { cs.run(ch0, ch1, withv, fn); };
     // S^T tiles of one chunk for this wave (raw accumulators, masked keys
     // -1e30 through the bias step, causal / window entries -inf), or -inf
     // for tiles outside the wave's keys.  ok(t): tile computed.

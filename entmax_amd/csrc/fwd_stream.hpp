@@ -33,11 +33,6 @@ struct StreamCfg {
     static_assert(CAP / TPR <= 64, "at most 64 list entries per lane in the solve");
 };
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Rank of this lane among the set lanes of its 16-lane group in `mask`.
 __device__ __forceinline__ void group_rank(unsigned long long mask, int g, int c, int* rank, int* total) {
     const unsigned gm = static_cast<unsigned>((mask >> (16 * g)) & 0xFFFFull);
