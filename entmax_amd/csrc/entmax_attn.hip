@@ -80,13 +80,14 @@ int launch_short(const ea::FwdArgs& a, hipStream_t st) {
 
 template <int DT, int D>
 int launch_stream(const ea::FwdArgs& a, hipStream_t st) {
-    constexpr int CAP = 128;
+    constexpr int CAP = 96;
     typedef ea::StreamCfg<D, CAP> C;
     auto kern = ea::fwd_stream_kernel<DT, D, CAP>;
-    int rc = set_lds(kern, C::lds_bytes);
+    const size_t lds = C::template total_bytes<DT>();
+    int rc = set_lds(kern, lds);
     if (rc) return rc;
     const int grid = a.B * a.H * a.nqt;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), C::lds_bytes, st, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), lds, st, a);
     return check_launch("fwd_stream");
 }
 

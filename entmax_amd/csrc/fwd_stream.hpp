@@ -18,7 +18,11 @@
 // streams its support into the list and flushes it into O when full.
 #pragma once
 
+#include <type_traits>
+
+#include "chunk_stream.hpp"
 #include "common.hpp"
+#include "fwd_short.hpp"
 #include "tau_solver.hpp"
 
 namespace ea {
@@ -30,6 +34,8 @@ struct StreamCfg {
     static constexpr size_t lds_bytes =
         static_cast<size_t>(BM) * CAP * (sizeof(float) + sizeof(uint16_t)) +
         sizeof(float) * 3 * BM + sizeof(int) * 2 * BM;
+    template <int DT>
+    static constexpr size_t total_bytes() { return lds_bytes + 2 * ChunkCfg<DT, D>::k_bytes; }
     static_assert(CAP / TPR <= 64, "at most 64 list entries per lane in the solve");
 };
 
@@ -52,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
     int* rown = reinterpret_cast<int*>(rowts + BM + BM);            // [BM] allowed count
     int* rowc = rown + BM;                             // [BM] list length, -1 = overflow
     uint16_t* lk = reinterpret_cast<uint16_t*>(rowc + BM);         // [BM][CAP] keys
+    float* kbufs = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + C::lds_bytes);   // K chunk buffers
 
     const int total = a.B * a.H * a.nqt;
     const int w = xcd_swizzle(blockIdx.x, total);
@@ -67,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wv = tid / kWave;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane / 16, c = lane % 16;
     const int r0 = 16 * wv;            // this wave's first row (tile-local)
 
@@ -94,83 +102,145 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
     };
 
     // ---- 1. scores, row max, candidate lists --------------------------------
+    // K streams through LDS in 64-key chunks shared by the four waves
+    // (chunk_stream.hpp); the row max is reduced once per chunk, the allowed
+    // count once at the end, and chunks without a candidate for the wave
+    // cost only the products and a comparison.
     float m[4];
     int n[4], cnt[4];
     bool ovf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -kInf; n[i] = 0; cnt[i] = 0; ovf[i] = false; }
-
-    for (int t = 0; t < ntile; ++t) {
-        const int kbase = (kt0 + t) * kBN;
-        float s[4][4];
+    float nl[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+        int wlo_k, whi_k;
+        key_range(q0, BM, L, a.causal, a.window, &wlo_k, &whi_k);
+        const int ch0 = wlo_k / kBN, ch1 = (whi_k + kBN - 1) / kBN;
+        ChunkStream<DT, D> cs;
+        cs.Kb = reinterpret_cast<char*>(kbufs);
+        cs.Vb = nullptr;
+        cs.kh = kh;
+        cs.vh = vh;
+        cs.kmp = km != nullptr ? km : reinterpret_cast<const uint8_t*>(qh);
+        cs.hasm = km != nullptr;
+        cs.L = L;
+        cs.tid = tid;
+        cs.lane = lane;
+        const float inv_scale = 1.f / a.scale;
+        cs.run(ch0, ch1, false, [&](int ch, const char* kb, const char*, unsigned long long M) {
+            const int kbase = ch * kBN;
+            if (kbase >= khi || kbase + kBN <= klo) return;   // uniform: none of this wave's keys
+            float s[4][4];
+            bool any = false;
+            auto products = [&](auto causal_tag) {
+                constexpr bool CAUSAL = decltype(causal_tag)::value;
+                float tm[4] = {-kInf, -kInf, -kInf, -kInf};
 #pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16) {
-            const int key = kbase + 16 * c16 + c;
-            const bool kv = key_ok(key);
-            const f32x4 acc = qf.tile(kh, key, L, g);
+                for (int c16 = 0; c16 < 4; ++c16) {
+                    KFrag<DT, D> kf;
+                    kf.load_lds(kb + (16 * c16 + c) * ChunkCfg<DT, D>::KSTR, g);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (DT == DT_BF16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c16][i] = score(key, kv, acc, i);
-        }
-        bool any = false;
+                        for (int ks = 0; ks < D / 32; ++ks) acc = mfma_bf16(qf.a[ks], kf.a[ks], acc);
+                    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float tm = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
-            int tn = (s[0][i] > -kInf) + (s[1][i] > -kInf) + (s[2][i] > -kInf) + (s[3][i] > -kInf);
-            tm = row_max<16>(tm);
-            tn = static_cast<int>(row_sum<16>(static_cast<float>(tn)));
-            m[i] = fmaxf(m[i], tm);
-            n[i] += tn;
-            const float thr = m[i] - 2.f;
+                        for (int u = 0; u < D / 16; ++u)
 #pragma unroll
-            for (int c16 = 0; c16 < 4; ++c16) any |= s[c16][i] > thr;
-        }
-        if (!__any(any)) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rl = r0 + 4 * g + i;
-            const float thr = m[i] - 2.f;
-            // make room: drop entries that fell below the current threshold
-            const bool need = !ovf[i] && cnt[i] + kBN > CAP;
-            if (__any(need)) {
-                int wr = 0;
-                const int tot = need ? cnt[i] : 0;
-                int nch = (tot + 15) / 16;
-                int maxch = nch;
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) maxch = max(maxch, __shfl_xor(maxch, o, kWave));
-                for (int ch = 0; ch < maxch; ++ch) {
-                    const int idx = 16 * ch + c;
-                    const bool in = idx < tot;
-                    const float v = in ? lv[rl * CAP + idx] : -kInf;
-                    const uint16_t kk = in ? lk[rl * CAP + idx] : static_cast<uint16_t>(0);
-                    const bool keep = in && v > thr;
-                    int rank, tot2;
-                    group_rank(__ballot(keep), g, c, &rank, &tot2);
-                    wave_sync();
-                    if (keep) {
-                        lv[rl * CAP + wr + rank] = v;
-                        lk[rl * CAP + wr + rank] = kk;
+                            for (int q = 0; q < 4; ++q) acc = mfma_f32(qf.a[u][q], kf.a[u][q], acc);
                     }
-                    wave_sync();
-                    wr += tot2;
-                }
-                if (need) cnt[i] = wr;
-            }
+                    const int key = kbase + 16 * c16 + c;
+                    const bool kv = ((M >> (16 * c16 + c)) & 1ull) != 0ull;
 #pragma unroll
-            for (int c16 = 0; c16 < 4; ++c16) {
-                const bool pred = !ovf[i] && s[c16][i] > thr;
-                int rank, tot2;
-                group_rank(__ballot(pred), g, c, &rank, &tot2);
-                const int slot = cnt[i] + rank;
-                if (pred && slot < CAP) {
-                    lv[rl * CAP + slot] = s[c16][i];
-                    lk[rl * CAP + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (CAUSAL) {
+                            // scaled scores, masks per element, count per element
+                            s[c16][i] = score(key, kv, acc, i);
+                            nl[i] += s[c16][i] > -kInf ? 1.f : 0.f;
+                        } else {
+                            // raw accumulators (scaled only where they are kept);
+                            // rows past L are never written out
+                            s[c16][i] = kv ? acc[i] : -kInf;
+                        }
+                        tm[i] = fmaxf(tm[i], s[c16][i]);
+                    }
                 }
-                cnt[i] += tot2;
+                if constexpr (!CAUSAL) {
+                    const float nv = static_cast<float>(__popcll(M));   // uniform
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nl[i] += c == 0 ? nv : 0.f;   // summed over the 16 lanes below
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float rm = row_max<16>(tm[i]);
+                    m[i] = fmaxf(m[i], CAUSAL ? rm : rm * a.scale);
+                    // threshold m - 2, in the units of s (a slightly lower raw
+                    // threshold only keeps more candidates)
+                    const float thr = CAUSAL ? m[i] - 2.f : (m[i] - 2.f) * inv_scale - 1e-6f * fabsf(m[i] * inv_scale);
+#pragma unroll
+                    for (int c16 = 0; c16 < 4; ++c16) any |= s[c16][i] > thr;
+                }
+                if constexpr (!CAUSAL) {
+                    if (__any(any)) {
+#pragma unroll
+                        for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[c16][i] = s[c16][i] * a.scale;   // -inf stays -inf
+                    }
+                }
+            };
+            if (a.causal || a.window > 0) products(std::true_type{});
+            else products(std::false_type{});
+            if (!__any(any)) return;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = r0 + 4 * g + i;
+                const float thr = m[i] - 2.f;
+                // make room: drop entries that fell below the current threshold
+                const bool need = !ovf[i] && cnt[i] + kBN > CAP;
+                if (__any(need)) {
+                    int wr = 0;
+                    const int tot = need ? cnt[i] : 0;
+                    int nch = (tot + 15) / 16;
+                    int maxch = nch;
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) maxch = max(maxch, __shfl_xor(maxch, o, kWave));
+                    for (int chh = 0; chh < maxch; ++chh) {
+                        const int idx = 16 * chh + c;
+                        const bool in = idx < tot;
+                        const float v = in ? lv[rl * CAP + idx] : -kInf;
+                        const uint16_t kk = in ? lk[rl * CAP + idx] : static_cast<uint16_t>(0);
+                        const bool keep = in && v > thr;
+                        int rank, tot2;
+                        group_rank(__ballot(keep), g, c, &rank, &tot2);
+                        wave_sync();
+                        if (keep) {
+                            lv[rl * CAP + wr + rank] = v;
+                            lk[rl * CAP + wr + rank] = kk;
+                        }
+                        wave_sync();
+                        wr += tot2;
+                    }
+                    if (need) cnt[i] = wr;
+                }
+#pragma unroll
+                for (int c16 = 0; c16 < 4; ++c16) {
+                    const bool pred = !ovf[i] && s[c16][i] > thr;
+                    int rank, tot2;
+                    group_rank(__ballot(pred), g, c, &rank, &tot2);
+                    const int slot = cnt[i] + rank;
+                    if (pred && slot < CAP) {
+                        lv[rl * CAP + slot] = s[c16][i];
+                        lk[rl * CAP + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
+                    }
+                    cnt[i] += tot2;
+                }
+                if (cnt[i] > CAP) ovf[i] = true;
             }
-            if (cnt[i] > CAP) ovf[i] = true;
-        }
+        });
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n[i] = static_cast<int>(row_sum<16>(nl[i]));
     if (c == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
