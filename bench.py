@@ -72,6 +72,43 @@ def algorithmic_bytes(w, key_mask):
     return q + 2 * kv_rows * row + o + tau + mask
 
 
+def kernel_source_sha():
+    """SHA-256 over the HIP sources; measured counters are tied to it."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "entmax_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's forward kernel, from the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/traffic.json,
+    or None when none were taken for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(workload)
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec["traffic_bytes"]
+
+
+def copy_probe(mib=256, reps=10):
+    """A plain device copy of known size, for calibrating the byte counters."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "reps": reps}))
+
+
 def cpu_baseline(name, budget_s=12.0):
     """Time the oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
@@ -119,7 +156,13 @@ def main():
                     choices=["tiny", "encoder", "long", "decoder", "longctx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device copy (byte-counter calibration) and exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): every (batch, head) is independent, "
@@ -217,8 +260,8 @@ def main():
         bytes_per_launch = algorithmic_bytes(w, km_cpu)
         achieved = bytes_per_launch / (fwd_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "fwd", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_per_launch,
-                "launch_ms": fwd_ms}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
+                "bytes_per_launch": bytes_per_launch, "launch_ms": fwd_ms}
     else:
         peak = MFMA_F32_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
         if w.backward and bwd_ms > fwd_ms:
@@ -231,7 +274,8 @@ def main():
             flop = 2.0 * w.d * pairs + 2.0 * w.d * nnz
         achieved = flop / (kms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None, "flop_per_launch": flop, "launch_ms": kms}
+                "frac": achieved / peak, "traffic": measured_traffic(w.name) if kname == "fwd" else None,
+                "flop_per_launch": flop, "launch_ms": kms}
 
     res = {
         "metric": METRIC,

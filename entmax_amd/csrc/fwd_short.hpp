@@ -150,9 +150,9 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     // ---- 0. loads ----------------------------------------------------------------
     // Issue order matters: a wait on a load also waits for every load issued
     // before it.  The key-mask bytes go first (two per lane: keys kbase + lane
-    // and kbase + 64 + lane); Q, K and V do not depend on the mask (rows past
-    // L are clamped to valid ones; masked keys are dropped through their
-    // scores, and their V rows meet p = 0), so they are in flight together.
+    // and kbase + 64 + lane); Q and K do not depend on the mask (rows past L
+    // are clamped to valid ones; masked keys are dropped through their
+    // scores), so they are in flight together with it.  V follows the mask.
     // No branch around any load: without a mask the byte loads read a byte
     // of Q and ignore it.
     const bool hasm = km != nullptr;
@@ -174,11 +174,6 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
         kreg[j] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(clamp_row(kbase + ch / CPR, L)) * D + (ch % CPR) * EPC);
     }
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        const int ch = tid + kThreads * j;
-        vreg[j] = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(clamp_row(kbase + ch / CPR, L)) * D + (ch % CPR) * EPC);
-    }
-#pragma unroll
     for (int j = 0; j < C::NKC; ++j) {
         const int ch = tid + kThreads * j;
         *reinterpret_cast<u32x4*>(Ks + (ch / CPR) * C::KSTR + (ch % CPR) * 16) = kreg[j];
@@ -192,6 +187,16 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     auto mbits16 = [&](int t) -> unsigned {   // the 16 key bits of tile t
         return static_cast<unsigned>(((t < 4 ? M0 : M1) >> (16 * (t & 3))) & 0xFFFFull);
     };
+    // V rows only now that the mask is known: a row that may not be attended
+    // reads the span's first row instead (fetched anyway; its p is 0), so
+    // padded keys cost no HBM traffic.  V is needed in step 3 only.
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int ch = tid + kThreads * j;
+        const int kl = ch / CPR;   // key within the span
+        const bool vok = (((kl < kWave ? M0 : M1) >> (kl & (kWave - 1))) & 1ull) != 0ull;
+        vreg[j] = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(vok ? kbase + kl : kbase) * D + (ch % CPR) * EPC);
+    }
 
     // tiles this wave's 16 rows may attend (causal / window; the mask is
     // applied below): [t0, tc1), uniform over the wave
