@@ -14,7 +14,9 @@ Prints ONE JSON line.  ``value`` is effective TFLOP/s: 4 d FLOPs per allowed
 A count as done), plus 6 d per pair for the backward.  ``roofline`` reports
 the dominant kernel: its algorithmic bytes (HBM-bound workloads) or
 algorithmic MFMA FLOPs (MFMA-bound ones) per launch over its average launch
-time, measured with HIP events on the launch stream inside the timed region.
+time, measured with HIP events on the launch stream over the timed region
+(forward-only steps: the region over the step count; forward + backward:
+events at the step boundaries and between the two launches).
 ``cpu_baseline`` times the float64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -203,19 +205,13 @@ def main():
         sets.append(s)
     torch.cuda.synchronize()
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(s, mid=None):
         entmax_attn_fwd(s["q"], s["k"], s["v"], s["key_mask"], w.causal, w.window, out=s["out"], tau_out=s["tau"])
-        if ev is not None:
-            ev[1].record()
         if w.backward:
-            if ev is not None:
-                ev[2].record()
+            if mid is not None:
+                mid.record()   # between the forward and the backward launch, same stream
             entmax_attn_bwd(s["q"], s["k"], s["v"], s["tau"], s["dout"], s["key_mask"], w.causal, w.window,
                             dq=s["grads"][0], dk=s["grads"][1], dv=s["grads"][2])
-            if ev is not None:
-                ev[3].record()
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -237,20 +233,34 @@ def main():
             del pr
         torch.cuda.synchronize()
 
-    nev = 4 if w.backward else 2
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Timed region: the steps back to back on the launch stream, HIP events
+    # only at its ends (and, with a backward, one per step boundary plus one
+    # between the two launches: those kernels run for milliseconds).  Per-launch
+    # events around microsecond kernels would add gaps to the steps.
+    ev = lambda: torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(sets[i % nsets], evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    if w.backward:
+        bounds = [ev() for _ in range(args.steps + 1)]
+        mids = [ev() for _ in range(args.steps)]
+        bounds[0].record()
+        for i in range(args.steps):
+            step(sets[i % nsets], mids[i])
+            bounds[i + 1].record()
+        torch.cuda.synchronize()
+        total_ms = bounds[0].elapsed_time(bounds[-1])
+        fwd_ms = sum(bounds[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
+        bwd_ms = sum(mids[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)) / args.steps
+    else:
+        t_start, t_end = ev(), ev()
+        t_start.record()
+        for i in range(args.steps):
+            step(sets[i % nsets])
+        t_end.record()
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        fwd_ms = total_ms / args.steps   # the forward launch is the whole step
+        bwd_ms = 0.0
     ms_per_step = total_ms / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps if w.backward else 0.0
 
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
 
