@@ -5,13 +5,12 @@
 // 16w .. 16w+15 and lane (g, c) = (lane / 16, lane % 16) serves query row c.
 // Apart from the V^T staging area every step is private to a wave: one
 // barrier in total.
-//   0. All global loads are issued at once, none behind a branch: the Q
-//      fragments and the K fragments of every 16-key tile of the span (rows
-//      clamped to L; masked keys are dropped after the product), the
-//      key-mask bytes, then the V rows (masked rows are redirected to an
-//      already-fetched row and zeroed).  V waits in registers and is stored
-//      transposed into LDS only after step 2, so that steps 1 and 2 run
-//      while it arrives.
+//   0. Global loads, none behind a branch: the key-mask bytes and the Q
+//      fragments, then the K and V rows of the span (rows of keys that may
+//      not be attended are redirected to an already-fetched row; their
+//      scores are masked).  K is staged in LDS; V waits in registers and is
+//      stored into LDS only after step 2, so that steps 1 and 2 run while it
+//      arrives.
 //   1. S^T = K Q^T on MFMA (operands swapped, so each lane holds 4
 //      consecutive keys of one query in each 16-key tile), masked (padding /
 //      causal / window as -inf) and kept in registers: the four lanes
@@ -150,11 +149,9 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     // ---- 0. loads ----------------------------------------------------------------
     // Issue order matters: a wait on a load also waits for every load issued
     // before it.  The key-mask bytes go first (two per lane: keys kbase + lane
-    // and kbase + 64 + lane); Q and K do not depend on the mask (rows past L
-    // are clamped to valid ones; masked keys are dropped through their
-    // scores), so they are in flight together with it.  V follows the mask.
-    // No branch around any load: without a mask the byte loads read a byte
-    // of Q and ignore it.
+    // and kbase + 64 + lane), then Q, which does not depend on the mask; K
+    // and V rows follow the mask.  No branch around any load: without a mask
+    // the byte loads read a byte of Q and ignore it.
     const bool hasm = km != nullptr;
     const uint8_t* kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
     const int mkey0 = kbase + lane, mkey1 = kbase + kWave + lane;
@@ -167,11 +164,19 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     qf.load(qh, qrow, L, g);
     // K and V rows of the span, once per workgroup: 16-byte chunks,
     // consecutive threads on consecutive chunks
+    // valid keys of the span as two 64-bit masks (bit k <-> key kbase + k,
+    // resp. kbase + 64 + k), uniform over the wave.  K rows of keys that may
+    // not be attended read the span's first row instead (fetched anyway), so
+    // padded keys cost no HBM traffic; their scores are masked below.
+    const unsigned long long M0 = __ballot((mkey0 < L) & (!hasm | (mb0 != 0)));
+    const unsigned long long M1 = C::SPAN > kWave ? __ballot((mkey1 < L) & (!hasm | (mb1 != 0))) : 0ull;
+    auto key_ok = [&](int kl) { return (((kl < kWave ? M0 : M1) >> (kl & (kWave - 1))) & 1ull) != 0ull; };
     u32x4 kreg[C::NKC], vreg[NCH];
 #pragma unroll
     for (int j = 0; j < C::NKC; ++j) {
         const int ch = tid + kThreads * j;
-        kreg[j] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(clamp_row(kbase + ch / CPR, L)) * D + (ch % CPR) * EPC);
+        const int kl = ch / CPR;   // key within the span
+        kreg[j] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(key_ok(kl) ? kbase + kl : kbase) * D + (ch % CPR) * EPC);
     }
 #pragma unroll
     for (int j = 0; j < C::NKC; ++j) {
@@ -180,10 +185,6 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     }
     __syncthreads();   // K staged
 
-    // valid keys of the span as two 64-bit masks (bit k <-> key kbase + k,
-    // resp. kbase + 64 + k), uniform over the wave
-    const unsigned long long M0 = __ballot((mkey0 < L) & (!hasm | (mb0 != 0)));
-    const unsigned long long M1 = C::SPAN > kWave ? __ballot((mkey1 < L) & (!hasm | (mb1 != 0))) : 0ull;
     auto mbits16 = [&](int t) -> unsigned {   // the 16 key bits of tile t
         return static_cast<unsigned>(((t < 4 ? M0 : M1) >> (16 * (t & 3))) & 0xFFFFull);
     };
@@ -194,8 +195,7 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     for (int j = 0; j < NCH; ++j) {
         const int ch = tid + kThreads * j;
         const int kl = ch / CPR;   // key within the span
-        const bool vok = (((kl < kWave ? M0 : M1) >> (kl & (kWave - 1))) & 1ull) != 0ull;
-        vreg[j] = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(vok ? kbase + kl : kbase) * D + (ch % CPR) * EPC);
+        vreg[j] = *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(key_ok(kl) ? kbase + kl : kbase) * D + (ch % CPR) * EPC);
     }
 
     // tiles this wave's 16 rows may attend (causal / window; the mask is
