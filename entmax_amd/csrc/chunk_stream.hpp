@@ -27,7 +27,10 @@ struct ChunkCfg {
     static constexpr int VRS = D * 2 + 32;            // bf16: V row stride (bytes), row-major
     static constexpr int VSTR = CK + EPC;             // fp32: V^T row stride (elements)
     static constexpr int v_bytes = DT == DT_BF16 ? CK * VRS : D * VSTR * 4;
+    static constexpr int RB = D * ESZ;                // bytes per K / V row in HBM
+    static constexpr int RS = RB == 128 ? 7 : RB == 256 ? 8 : 9;
     static_assert(NPC >= 1 && CK == kWave, "whole pieces per thread; one key per lane");
+    static_assert((1 << RS) == RB, "row bytes a power of two");
 };
 
 template <int DT, int D>
@@ -48,15 +51,20 @@ struct ChunkStream {
         uint8_t mb;
     };
 
+    // 32-bit byte offsets from the head's base (a head holds at most
+    // 65536 rows of at most 512 bytes), so that the address is one scalar
+    // base plus one vector offset
     __device__ __forceinline__ void prefetch(int ch, bool withv, Pre& p) const {
         const int cb = ch * C::CK;
         p.mb = kmp[hasm ? clamp_row(cb + lane, L) : 0];   // no branch around the load
+        const char* kc = reinterpret_cast<const char*>(kh);
+        const char* vc = reinterpret_cast<const char*>(vh);
 #pragma unroll
         for (int j = 0; j < C::NPC; ++j) {
             const int pc = tid + kThreads * j;
-            const size_t off = static_cast<size_t>(clamp_row(cb + pc / C::CPR, L)) * D + (pc % C::CPR) * C::EPC;
-            p.k[j] = *reinterpret_cast<const u32x4*>(kh + off);
-            if (withv) p.v[j] = *reinterpret_cast<const u32x4*>(vh + off);
+            const unsigned off = (static_cast<unsigned>(clamp_row(cb + pc / C::CPR, L)) << C::RS) + (pc % C::CPR) * 16u;
+            p.k[j] = *reinterpret_cast<const u32x4*>(kc + off);
+            if (withv) p.v[j] = *reinterpret_cast<const u32x4*>(vc + off);
         }
     }
     __device__ __forceinline__ void stage(int buf, bool withv, const Pre& p) const {

@@ -188,6 +188,12 @@ __host__ __device__ __forceinline__ void key_range(int q0, int bm, int L, int ca
     *hi = h;
 }
 
+// *p += v on an LDS address, as one LDS read-modify-write without return
+// (ds_add_u32); relaxed, for slots that only the calling lane updates
+__device__ __forceinline__ void lds_add(unsigned* p, unsigned v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Workgroup -> work item: consecutive work items (the Q tiles of one head)
 // land on the same XCD, whose L2 then serves the head's K and V.
 // Workgroups are dealt round-robin to the 8 XCDs.

@@ -9,12 +9,14 @@
 // workgroup in LDS (two buffers; a chunk's loads are issued two chunks ahead)
 // and shared by the four waves; S is recomputed on MFMA in every pass
 // instead of being stored.
-//   A. row max and allowed count, and a rough count of candidates;
-//   C. (only when some lane has too many candidates for its list) three
-//      bisection levels at once: g at the seven midpoints of the next three
-//      levels of the bisection tree ("ADASPLASH -- ROBERTA Benchmark
-//      Result", section 2.3 Theorem 2; bracket of the "DistilBERT SST-2
-//      with AdaSplash Attention" model card, Mathematical Formulation 2);
+//   A. row max and allowed count;
+//   C. (when a row allows more keys than its lists hold, until every lane's
+//      band fits) three bisection levels at once ("ADASPLASH -- ROBERTA
+//      Benchmark Result", section 2.3 Theorem 2; bracket of the "DistilBERT
+//      SST-2 with AdaSplash Attention" model card, Mathematical Formulation
+//      2): a per-lane histogram of the bracket's eight cells three steps
+//      down, with the count and the first two moments per cell, gives g at
+//      all seven midpoints and the exact band size of every cell;
 //   B. the band: scores in the current bracket (lo, hi] go to a per-lane
 //      list in LDS, those above hi are folded into exact sums (U); if a
 //      list overflows, C runs again and B is repeated;
@@ -112,36 +114,42 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     // -1e30 through the bias step, causal / window entries -inf), or -inf
     // for tiles outside the wave's keys.  ok(t): tile computed.
     constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
+    const int klane = c * C::KSTR + 16 * g;   // this lane's K piece within a staged chunk
+    // every row of the wave is a query row (uniform)
+    const bool allrows = q0 + 16 * wv + 15 < L;
     auto tiles = [&](int ch, const char* kb, unsigned long long M, f32x4 (&sv)[NTC], bool (&ok)[NTC]) {
         const int cb = ch * CK;
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
-            sv[t] = f32x4{-kInf, -kInf, -kInf, -kInf};
             const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
             ok[t] = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
-            if (!ok[t]) continue;
+            if (!ok[t]) {
+                sv[t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+                continue;
+            }
             KFrag<DT, D> kf;
-            kf.load_lds(kb + (16 * t + c) * C::KSTR, g);
+            kf.load_lds_at(kb + klane + 16 * t * C::KSTR);
             sv[t] = mb == 0xFFFFu ? kf.st(qf) : kf.st_bias(qf, ((mb >> c) & 1u) ? 0u : kMaskedBits, g);
             if (a.causal) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = cb + 16 * t + 4 * g + i;
-                    sv[t][i] = (key <= khi_i) & (key > klo_i) ? sv[t][i] : -kInf;
+                    sv[t][i] = ((key <= khi_i) & (key > klo_i)) ? sv[t][i] : -kInf;
                 }
             }
+            if (!allrows) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[t][i] = rowok ? sv[t][i] : -kInf;
+                for (int i = 0; i < 4; ++i) sv[t][i] = rowok ? sv[t][i] : -kInf;
+            }
         }
     };
 
     const float c2 = 0.5f * a.scale;
 
-    // ---- A. row max, allowed count, candidate estimate ---------------------------
-    // cand: entries above (running row max - 2) in score units, i.e. x > -1
-    // against the row max seen so far -- an over-count of the final one
-    float mlane = -kInf, nl = 0.f, cand = 0.f, mrun = -kInf;
-    const float thr_raw = 2.f / a.scale;
+    // ---- A. row max and allowed count -----------------------------------------------
+    // Without a causal mask every row of the tile allows the same keys: the
+    // count comes from the chunks' key bits.
+    float mlane = -kInf, nl = 0.f, npop = 0.f;
     stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
         f32x4 sv[NTC];
         bool ok[NTC];
@@ -149,21 +157,15 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
             if (!ok[t]) continue;
+            mlane = fmaxf(mlane, fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
+            if (a.causal) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mlane = fmaxf(mlane, sv[t][i]);
-        }
-        mrun = col4_max(mlane);
-#pragma unroll
-        for (int t = 0; t < NTC; ++t) {
-            if (!ok[t]) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float s = sv[t][i];
-                nl += s > -1e29f ? 1.f : 0.f;
-                cand += s > mrun - thr_raw ? 1.f : 0.f;
+                for (int i = 0; i < 4; ++i) nl += sv[t][i] > -1e29f ? 1.f : 0.f;
             }
         }
+        if (!a.causal) npop += static_cast<float>(__popcll(M));
     });
+    if (!a.causal) nl = (g == 0 && rowok) ? npop : 0.f;
     const float mrow = col4_max(mlane);
     const float n = col4_sum(nl);
     const bool empty = n == 0.f;
@@ -186,19 +188,46 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
         return r != 0;
     };
 
-    // ---- C. three bisection levels per pass -------------------------------------
+    // ---- C. three bisection levels per pass, from a histogram -------------------
+    // The bracket [lo, hi] is cut into the 8 cells three steps down; every
+    // entry above max(lo, lb) goes to its cell (cell 8: above hi), where this
+    // lane accumulates the count and the first two moments of its offset r
+    // from the cell's lower edge e (cells 0-7: r in cell widths, cell 8:
+    // r = x - hi), in 22-bit fixed point through integer LDS adds (one
+    // private slot per lane: no two lanes touch one address; integer adds are
+    // full rate, float adds are not).  After the pass, g at each of the seven
+    // inner edges follows from the cell sums above it
+    //   sum_{x > e_k} (x - e_k)^2 = sum over cells j >= k of
+    //     S2_j + 2 (e_j - e_k) S1_j + (e_j - e_k)^2 N_j,
+    // and the three steps walk the tree of these midpoints.  Entries at or
+    // below max(lo, lb) go to a dump cell (9).  The fixed-point rounding
+    // (2^-23 of a cell width, or absolute for cell 8) is of the order of the
+    // float rounding of the sums themselves.
+    constexpr int kCells = 10;
+    unsigned* hist = reinterpret_cast<unsigned*>(lists) + wv * (kCells * 3 * kWave) + lane;   // [cell][N, S1, S2] at stride kWave
+    static_assert(4 * kCells * 3 * kWave * 4 <= C::vl_bytes, "histograms fit the list region");
+    // steps whose midpoint lies below lb move the lower end without an
+    // evaluation: take them before a pass, so that its levels all count
+    auto forced = [&]() {
+        for (;;) {
+            const float mid = 0.5f * (s.lo + s.hi);
+            const bool f = s.it < kIters && mid < s.lb;
+            if (!__any(f)) break;
+            if (f) {
+                s.lo = mid;
+                ++s.it;
+            }
+        }
+    };
     auto pass_c = [&]() -> int {
-        // the seven midpoints of the next three levels, as the steps would form them
+        forced();
         const float lo = s.lo, hi = s.hi;
-        const float p4 = 0.5f * (lo + hi);
-        const float p2 = 0.5f * (lo + p4), p6 = 0.5f * (p4 + hi);
-        const float p1 = 0.5f * (lo + p2), p3 = 0.5f * (p2 + p4), p5 = 0.5f * (p4 + p6), p7 = 0.5f * (p6 + hi);
-        const float pts[7] = {p1, p2, p3, p4, p5, p6, p7};
-        // per lane: g parts and the number of entries above each point
-        float acc[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int cnt[7] = {0, 0, 0, 0, 0, 0, 0};
-        const float lo_eff = fmaxf(lo, s.lb);   // entries at or below it are never listed
-        int cnt_lo = 0, cnt_hi = 0;
+        const float w = (hi - lo) * 0.125f;          // cell width (power-of-two scaling)
+        const float iw = 8.f / (hi - lo);
+        const float lo_eff = fmaxf(lo, s.lb);
+        constexpr float kFix = 4194304.f;            // 2^22
+#pragma unroll
+        for (int k = 0; k < kCells * 3; ++k) hist[k * kWave] = 0u;
         stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
             f32x4 sv[NTC];
             bool ok[NTC];
@@ -209,41 +238,65 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float x = fmaf(sv[t][i], c2, -mc2);
-#pragma unroll
-                    for (int k = 0; k < 7; ++k) {
-                        const float y = relu1(x - pts[k]);
-                        acc[k] = fmaf(y, y, acc[k]);
-                        cnt[k] += x > pts[k] ? 1 : 0;
-                    }
-                    cnt_lo += x > lo_eff ? 1 : 0;
-                    cnt_hi += x > hi ? 1 : 0;
+                    const float u = (x - lo) * iw;
+                    const float cf = x > lo_eff ? floorf(fminf(u, 8.f)) : 9.f;
+                    // offset in [0, 1] (clamped: the dump cell's is meaningless)
+                    const float r = __builtin_amdgcn_fmed3f(cf == 8.f ? x - hi : u - cf, 0.f, 1.f);
+                    unsigned* h = hist + static_cast<int>(cf) * (3 * kWave);
+                    lds_add(h, 1u);
+                    lds_add(h + kWave, static_cast<unsigned>(r * kFix));
+                    lds_add(h + 2 * kWave, static_cast<unsigned>(r * r * kFix));
                 }
             }
         });
-        float gk[7];
+        // row sums per cell; this lane's counts are kept for the band size
+        constexpr float kUnfix = 1.f / kFix;
+        float nl_cell[8];
+        float N = 0.f, A1 = 0.f, A2 = 0.f;   // cells above the current edge, relative to it
+        float gk[8];                          // g at the edges e_0 .. e_7
+        N = col4_sum(static_cast<float>(hist[(8 * 3) * kWave]));
+        A1 = col4_sum(static_cast<float>(hist[(8 * 3 + 1) * kWave])) * kUnfix;
+        A2 = col4_sum(static_cast<float>(hist[(8 * 3 + 2) * kWave])) * kUnfix;
 #pragma unroll
-        for (int k = 0; k < 7; ++k) gk[k] = col4_sum(acc[k]);
-        // walk the tree: g > 1 (or a midpoint below lb) moves the lower end;
-        // track this lane's entries in the final cell (lo, hi]
-        int node = 3;   // p4
-        int above_lo = cnt_lo, above_hi = cnt_hi;   // entries above lo / above hi (this lane)
+        for (int k = 7; k >= 0; --k) {
+            // reference from e_(k+1) down to e_k
+            A2 = fmaf(w * N, w, fmaf(2.f * w, A1, A2));
+            A1 = fmaf(w, N, A1);
+            const float nk = static_cast<float>(hist[(k * 3) * kWave]);
+            nl_cell[k] = nk;
+            N += col4_sum(nk);
+            A1 = fmaf(col4_sum(static_cast<float>(hist[(k * 3 + 1) * kWave])), w * kUnfix, A1);
+            A2 = fmaf(col4_sum(static_cast<float>(hist[(k * 3 + 2) * kWave])), w * w * kUnfix, A2);
+            gk[k] = A2;
+        }
+        // the seven midpoints of the next three levels, as the steps would form them
+        const float p4 = 0.5f * (lo + hi);
+        const float p2 = 0.5f * (lo + p4), p6 = 0.5f * (p4 + hi);
+        const float p1 = 0.5f * (lo + p2), p3 = 0.5f * (p2 + p4), p5 = 0.5f * (p4 + p6), p7 = 0.5f * (p6 + hi);
+        const float pts[8] = {lo, p1, p2, p3, p4, p5, p6, p7};
+        // walk the tree: g > 1 (or a midpoint below lb) moves the lower end
+        int node = 4, cell = 0;
 #pragma unroll
         for (int lev = 0; lev < 3; ++lev) {
             if (s.it >= kIters) break;
+            const int step = 4 >> (lev + 1);
             const float mid = pts[node];
             const bool up = gk[node] > 1.f || mid < s.lb;
             if (up) {
                 s.lo = mid;
-                above_lo = cnt[node];
+                cell = node;
             } else {
                 s.hi = mid;
-                above_hi = cnt[node];
             }
             ++s.it;
-            const int step = lev == 0 ? 2 : 1;
             node = up ? node + step : node - step;
         }
-        return above_lo - above_hi;   // band entries of this lane (an over-count while lo < lb)
+        // this lane's entries in the final cell (lo, hi]; none for rows
+        // that have taken all their steps
+        float band = nl_cell[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) band = cell == k ? nl_cell[k] : band;
+        return s.it >= kIters ? 0 : static_cast<int>(band);
     };
 
     // ---- B. band lists and U ---------------------------------------------------------
@@ -279,21 +332,21 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     // ---- tau -----------------------------------------------------------------------------
     // lists alias the V buffers, which pass D rewrites only after this
     {
-        // pass C until the band of every lane fits its list (known from the
-        // counts), then pass B; a list that still overflows (the candidate
-        // estimate was used) sends the workgroup back to pass C
-        bool need_c = vote_any(cand > static_cast<float>(CAP));
+        // pass C until the band of every lane fits its list (known exactly
+        // from the cell counts), then pass B.  Rows allowing more keys than
+        // four full lists start with pass C; a list that overflows anyway
+        // sends the workgroup back to pass C.  Rows take different numbers
+        // of steps (forced ones), so every loop decision is a vote.
+        bool need_c = vote_any(n > static_cast<float>(4 * CAP));
         for (;;) {
-            while (need_c && s.it < kIters) need_c = vote_any(pass_c() > CAP);
-            if (s.it >= kIters) break;   // uniform: every row has taken all steps
+            while (need_c) need_c = vote_any(pass_c() > CAP);
             pass_b();
-            if (!vote_any(len > CAP)) break;
+            if (!vote_any(len > CAP && s.it < kIters)) break;
             need_c = true;
         }
     }
-    float tr;
-    if (s.it >= kIters) tr = 0.5f * (s.lo + s.hi);
-    else tr = col_finish<CAP>(col, len, s);
+    // rows that have taken all 25 steps return the midpoint
+    const float tr = col_finish<CAP>(col, len, s);
     if (a.tau != nullptr && g == 0 && rowok) a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tr);
     const float sh = empty ? 0.f : mc2 + tr;
     __syncthreads();   // lists done: the region holds V from now on

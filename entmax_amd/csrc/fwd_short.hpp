@@ -63,10 +63,11 @@ template <int DT, int D> struct KFrag;
 template <int D> struct KFrag<DT_BF16, D> {
     bf16x8 a[D / 32];
     // from a row-major LDS copy (row = this lane's key)
-    __device__ __forceinline__ void load_lds(const char* row, int g) {
+    __device__ __forceinline__ void load_lds(const char* row, int g) { load_lds_at(row + 16 * g); }
+    // p: this lane's first piece (row + 16 g)
+    __device__ __forceinline__ void load_lds_at(const char* p) {
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 2 * (32 * ks + 8 * g)));
+        for (int ks = 0; ks < D / 32; ++ks) a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 64 * ks));
     }
     // key must be a valid row index; ok = false loads it but yields zeros
     __device__ __forceinline__ void load(const uint16_t* kh, int key, bool ok, int g) {
@@ -91,9 +92,10 @@ template <int D> struct KFrag<DT_BF16, D> {
 };
 template <int D> struct KFrag<DT_F32, D> {
     f32x4 a[D / 16];
-    __device__ __forceinline__ void load_lds(const char* row, int g) {
+    __device__ __forceinline__ void load_lds(const char* row, int g) { load_lds_at(row + 16 * g); }
+    __device__ __forceinline__ void load_lds_at(const char* p) {
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u) a[u] = *reinterpret_cast<const f32x4*>(row + 4 * (16 * u + 4 * g));
+        for (int u = 0; u < D / 16; ++u) a[u] = *reinterpret_cast<const f32x4*>(p + 64 * u);
     }
     __device__ __forceinline__ void load(const float* kh, int key, bool ok, int g) {
 #pragma unroll
