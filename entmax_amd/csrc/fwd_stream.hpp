@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
             const int kbase = ch * kBN;
             if (kbase >= khi || kbase + kBN <= klo) return;   // uniform: none of this wave's keys
             float s[4][4];
+            float thr_s[4];   // each row's current threshold m - 2, in the units of s
             bool any = false;
             auto products = [&](auto causal_tag) {
                 constexpr bool CAUSAL = decltype(causal_tag)::value;
@@ -177,18 +178,12 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
                     // threshold m - 2, in the units of s (a slightly lower raw
                     // threshold only keeps more candidates)
                     const float thr = CAUSAL ? m[i] - 2.f : (m[i] - 2.f) * inv_scale - 1e-6f * fabsf(m[i] * inv_scale);
+                    thr_s[i] = thr;
 #pragma unroll
                     for (int c16 = 0; c16 < 4; ++c16) any |= s[c16][i] > thr;
                 }
-                if constexpr (!CAUSAL) {
-                    if (__any(any)) {
-#pragma unroll
-                        for (int c16 = 0; c16 < 4; ++c16)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s[c16][i] = s[c16][i] * a.scale;   // -inf stays -inf
-                    }
-                }
             };
+            const bool raw = !(a.causal || a.window > 0);   // s holds unscaled accumulators
             if (a.causal || a.window > 0) products(std::true_type{});
             else products(std::false_type{});
             if (!__any(any)) return;
@@ -223,14 +218,18 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
                     }
                     if (need) cnt[i] = wr;
                 }
+                // appends: most (row, tile) pairs of a chunk have none, and
+                // skip the ranking (uniform test)
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
-                    const bool pred = !ovf[i] && s[c16][i] > thr;
+                    const bool pred = !ovf[i] && s[c16][i] > thr_s[i];
+                    const unsigned long long bal = __ballot(pred);
+                    if (bal == 0ull) continue;
                     int rank, tot2;
-                    group_rank(__ballot(pred), g, c, &rank, &tot2);
+                    group_rank(bal, g, c, &rank, &tot2);
                     const int slot = cnt[i] + rank;
                     if (pred && slot < CAP) {
-                        lv[rl * CAP + slot] = s[c16][i];
+                        lv[rl * CAP + slot] = raw ? s[c16][i] * a.scale : s[c16][i];
                         lk[rl * CAP + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
                     }
                     cnt[i] += tot2;
