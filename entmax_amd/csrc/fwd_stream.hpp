@@ -191,8 +191,16 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int rl = r0 + 4 * g + i;
                 const float thr = m[i] - 2.f;
+                // this chunk's candidates of the row (a ballot per 16-key tile)
+                unsigned long long bal[4];
+                int add = 0;
+#pragma unroll
+                for (int c16 = 0; c16 < 4; ++c16) {
+                    bal[c16] = __ballot(!ovf[i] && s[c16][i] > thr_s[i]);
+                    add += __popc(static_cast<unsigned>((bal[c16] >> (16 * g)) & 0xFFFFull));
+                }
                 // make room: drop entries that fell below the current threshold
-                const bool need = !ovf[i] && cnt[i] + kBN > CAP;
+                const bool need = !ovf[i] && cnt[i] + add > CAP;
                 if (__any(need)) {
                     int wr = 0;
                     const int tot = need ? cnt[i] : 0;
@@ -222,11 +230,10 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
                 // skip the ranking (uniform test)
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
-                    const bool pred = !ovf[i] && s[c16][i] > thr_s[i];
-                    const unsigned long long bal = __ballot(pred);
-                    if (bal == 0ull) continue;
+                    if (bal[c16] == 0ull) continue;
+                    const bool pred = ((bal[c16] >> lane) & 1ull) != 0ull;
                     int rank, tot2;
-                    group_rank(bal, g, c, &rank, &tot2);
+                    group_rank(bal[c16], g, c, &rank, &tot2);
                     const int slot = cnt[i] + rank;
                     if (pred && slot < CAP) {
                         lv[rl * CAP + slot] = raw ? s[c16][i] * a.scale : s[c16][i];
