@@ -245,11 +245,13 @@ __device__ __forceinline__ float col_lower_bound(float xl) {
 // sv: this lane's raw scores (unscaled accumulators, -inf where excluded)
 // of tiles [t0, t1); x = fma(acc, c2, -mc2) is the half-scaled shifted
 // score (c2 = scale / 2, mc2 = row max of acc times c2).  n >= 1: allowed
-// keys of the row.  xlmax: this lane's largest x (-inf if none).  col: this lane's scratch column (NT * 4 floats at
-// stride kWave).  Must be called by every lane of the wave.  Returns t in
+// keys of the row.  xlmax: this lane's largest x (-inf if none).  col: this
+// lane's scratch column (KMAX floats at stride kWave; KMAX exceeds the
+// number of this lane's allowed keys).  Must be called by every lane of the
+// wave.  Returns t in
 // the half-scaled shifted domain (tau = 2 (mc2 + t)), equal in the four
 // lanes of the row.
-template <int NT>
+template <int NT, int KMAX>
 __device__ __forceinline__ float col_solve(const f32x4 (&sv)[NT], int t0, int t1, float c2, float mc2, float n,
                                            float xlmax, float* col) {
     ColState s;
@@ -273,7 +275,7 @@ __device__ __forceinline__ float col_solve(const f32x4 (&sv)[NT], int t0, int t1
             len += x > s.lb ? 1 : 0;
         }
     }
-    return col_finish<NT * 4>(col, len, s);
+    return col_finish<KMAX>(col, len, s);
 }
 
 // From a state whose band (entries in (lo, hi] above lb, at most KMAX per

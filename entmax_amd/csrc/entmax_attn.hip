@@ -67,10 +67,10 @@ int set_lds(K kernel, size_t bytes) {
     return ENTMAX_OK;
 }
 
-template <int DT, int D, int NKT>
+template <int DT, int D, int NKT, int KC = NKT * ea::kBN / 4>
 int launch_short(const ea::FwdArgs& a, hipStream_t st) {
-    typedef ea::ShortCfg<DT, D, NKT> C;
-    auto kern = ea::fwd_short_kernel<DT, D, NKT>;
+    typedef ea::ShortCfg<DT, D, NKT, KC> C;
+    auto kern = ea::fwd_short_kernel<DT, D, NKT, KC>;
     int rc = set_lds(kern, C::lds_bytes);
     if (rc) return rc;
     const int grid = a.B * a.H * a.nqt;
@@ -115,6 +115,9 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
     }
     if (s64 <= 128) {
         a.nqt = (L + 63) / 64;
+        // a causal window of at most 32 keys leaves a lane at most 12 allowed
+        // keys (three 16-key tiles): a smaller scratch, more workgroups per CU
+        if (a.causal && a.window > 0 && a.window <= 32) return launch_short<DT, D, 2, 16>(a, st);
         return launch_short<DT, D, 2>(a, st);
     }
     // spans beyond 2048 keys: one pass over K with candidate lists and a

@@ -31,7 +31,9 @@
 
 namespace ea {
 
-template <int DT, int D, int NKT>
+// KC: scratch slots per lane for the solve's candidates, at least the
+// largest number of allowed keys one lane can hold (4 per 16-key tile)
+template <int DT, int D, int NKT, int KC = NKT * kBN / 4>
 struct ShortCfg {
     static constexpr int BM = 64;
     static constexpr int SPAN = NKT * kBN;
@@ -45,7 +47,7 @@ struct ShortCfg {
     // reads); fp32: V^T
     static constexpr int VRS = D * 2 + 32;
     static constexpr int v_bytes = DT == DT_BF16 ? SPAN * VRS : D * VSTR * ESZ;
-    static constexpr int scr_bytes = 4 * NT * 4 * kWave * 4;   // per wave: NT*4 rows x 64 lanes
+    static constexpr int scr_bytes = 4 * KC * kWave * 4;       // per wave: KC rows x 64 lanes
     static constexpr int KSTR = D * ESZ + 16;                   // K row stride in LDS (bytes)
     static constexpr int k_bytes = SPAN * KSTR;
     static constexpr int NKC = SPAN * CPR / kThreads;           // K chunks per thread
@@ -55,7 +57,8 @@ struct ShortCfg {
     static_assert(NCH >= 1 && SPAN <= 2 * kWave, "whole chunks per thread; mask bits in two ballots");
     // waves per SIMD to aim for: 3 workgroups per CU where the register
     // budget allows it (168 registers), else whatever fits
-    static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? 3 : 1;
+    static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? (lds_bytes * 4 <= 160 * 1024 ? 4 : 3) : 1;
+    static_assert(KC <= NT * 4 && KC >= 16, "scratch slots");
 };
 
 // K fragments of one 16-key tile, in the same lane layout as QFrag::a.
@@ -115,10 +118,10 @@ template <int D> struct KFrag<DT_F32, D> {
     }
 };
 
-template <int DT, int D, int NKT>
-__global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_short_kernel(FwdArgs a) {
+template <int DT, int D, int NKT, int KC>
+__global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fwd_short_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
-    typedef ShortCfg<DT, D, NKT> C;
+    typedef ShortCfg<DT, D, NKT, KC> C;
     constexpr int BM = C::BM, NT = C::NT, EPC = C::EPC, CPR = C::CPR, NCH = C::NCH, VSTR = C::VSTR;
     extern __shared__ float lds[];
     char* Ks = reinterpret_cast<char*>(lds);              // K rows (steps 0-1)
@@ -288,8 +291,8 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT>::kOcc)) void fwd_sh
     // ---- 2. tau ----------------------------------------------------------------------------
     const float c2 = 0.5f * a.scale;
     const float mc2 = empty ? 0.f : mraw * c2;
-    float* col = scratch + wv * (NT * 4 * kWave) + lane;
-    float tr = col_solve<NT>(sv, t0, t1, c2, mc2, empty ? 1.f : n, fmaf(mlane, c2, -mc2), col);
+    float* col = scratch + wv * (KC * kWave) + lane;
+    float tr = col_solve<NT, KC>(sv, t0, t1, c2, mc2, empty ? 1.f : n, fmaf(mlane, c2, -mc2), col);
     if (a.tau != nullptr && g == 0 && rowok) a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tr);
     const float sh = empty ? 0.f : mc2 + tr;   // p = clamp(acc c2 - sh)^2; empty rows have acc = -inf
 
