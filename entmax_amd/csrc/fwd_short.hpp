@@ -51,12 +51,17 @@ struct ShortCfg {
     static constexpr int KSTR = D * ESZ + 16;                   // K row stride in LDS (bytes)
     static constexpr int k_bytes = SPAN * KSTR;
     static constexpr int NKC = SPAN * CPR / kThreads;           // K chunks per thread
-    // K staging (step 0-1) and the solve's scratch (step 2) share one region
+    // K staging (step 0-1) and the solve's scratch (step 2) share one region;
+    // with a reduced scratch (KC below the span's 4 keys per tile and lane)
+    // V takes the same region after the solve as well, at the cost of one
+    // more barrier, so that more workgroups fit a CU
+    static constexpr bool kAlias = KC < NT * 4;
     static constexpr int ks_bytes = k_bytes > scr_bytes ? k_bytes : scr_bytes;
-    static constexpr size_t lds_bytes = static_cast<size_t>(ks_bytes) + v_bytes;
+    static constexpr int ksv_bytes = ks_bytes > v_bytes ? ks_bytes : v_bytes;
+    static constexpr size_t lds_bytes = kAlias ? static_cast<size_t>(ksv_bytes) : static_cast<size_t>(ks_bytes) + v_bytes;
     static_assert(NCH >= 1 && SPAN <= 2 * kWave, "whole chunks per thread; mask bits in two ballots");
-    // waves per SIMD to aim for: 3 workgroups per CU where the register
-    // budget allows it (168 registers), else whatever fits
+    // waves per SIMD to aim for (bf16, d = 64): four workgroups per CU when
+    // their LDS fits (128 registers), else three (168 registers)
     static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? (lds_bytes * 4 <= 160 * 1024 ? 4 : 3) : 1;
     static_assert(KC <= NT * 4 && KC >= 16, "scratch slots");
 };
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
     extern __shared__ float lds[];
     char* Ks = reinterpret_cast<char*>(lds);              // K rows (steps 0-1)
     float* scratch = lds;                                  // the solve's scratch (step 2), same region
-    char* Vs = reinterpret_cast<char*>(lds) + C::ks_bytes;   // V (bf16: row-major; fp32: V^T)
+    char* Vs = reinterpret_cast<char*>(lds) + (C::kAlias ? 0 : C::ks_bytes);   // V (bf16: row-major; fp32: V^T)
 
     const int total = a.B * a.H * a.nqt;
     const int w = xcd_swizzle(blockIdx.x, total);
@@ -299,6 +304,7 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
     // V into LDS, only now, so that steps 1 and 2 ran while it arrived.
     // bf16: row-major (the P V operand is read back with transpose loads);
     // fp32: transposed, one element at a time.
+    if constexpr (C::kAlias) __syncthreads();   // every wave is done with its scratch: the region takes V
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int ch = tid + kThreads * j;
