@@ -33,7 +33,10 @@ struct ChunkCfg {
     static_assert((1 << RS) == RB, "row bytes a power of two");
 };
 
-template <int DT, int D>
+// NBUF: LDS buffers per stream.  Two let a chunk be staged while the
+// previous one is in use (one barrier per chunk); one halves the LDS at the
+// cost of a second barrier per chunk.
+template <int DT, int D, int NBUF = 2>
 struct ChunkStream {
     typedef typename InT<DT>::type T;
     typedef ChunkCfg<DT, D> C;
@@ -98,6 +101,28 @@ struct ChunkStream {
     template <typename F>
     __device__ __forceinline__ void run(int ch0, int ch1, bool withv, F&& fn) const {
         if (ch0 >= ch1) return;
+        if constexpr (NBUF == 1) {
+            Pre pa, pb;
+            prefetch(ch0, withv, pa);
+            if (ch0 + 1 < ch1) prefetch(ch0 + 1, withv, pb);
+            for (int ch = ch0; ch < ch1; ch += 2) {
+                // chunk ch is in flight in pa, chunk ch + 1 in pb
+                stage(0, withv, pa);
+                const unsigned long long Ma = valid_bits(ch, pa);
+                __syncthreads();
+                if (ch + 2 < ch1) prefetch(ch + 2, withv, pa);
+                fn(ch, Kb, Vb, Ma);
+                __syncthreads();
+                if (ch + 1 >= ch1) break;
+                stage(0, withv, pb);
+                const unsigned long long Mb = valid_bits(ch + 1, pb);
+                __syncthreads();
+                if (ch + 3 < ch1) prefetch(ch + 3, withv, pb);
+                fn(ch + 1, Kb, Vb, Mb);
+                __syncthreads();
+            }
+            return;
+        }
         Pre pa, pb;
         prefetch(ch0, withv, pa);
         if (ch0 + 1 < ch1) prefetch(ch0 + 1, withv, pb);

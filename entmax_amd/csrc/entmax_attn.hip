@@ -81,8 +81,8 @@ int launch_short(const ea::FwdArgs& a, hipStream_t st) {
 template <int DT, int D>
 int launch_stream(const ea::FwdArgs& a, hipStream_t st) {
     // rows whose running max lags hold up to ~50 scores within 2 of it at
-    // once: 96 keep list overflows (and their recompute fallback) rare
-    constexpr int CAP = 96;
+    // once: 80 keep list overflows (and their recompute fallback) rare
+    constexpr int CAP = 80;
     typedef ea::StreamCfg<D, CAP> C;
     auto kern = ea::fwd_stream_kernel<DT, D, CAP>;
     const size_t lds = C::template total_bytes<DT>();

@@ -34,8 +34,10 @@ struct StreamCfg {
     static constexpr size_t lds_bytes =
         static_cast<size_t>(BM) * CAP * (sizeof(float) + sizeof(uint16_t)) +
         sizeof(float) * 3 * BM + sizeof(int) * 2 * BM;
+    // one K chunk buffer (ChunkStream<.., 1>): with CAP = 80 a bf16 workgroup
+    // takes under a third of the LDS
     template <int DT>
-    static constexpr size_t total_bytes() { return lds_bytes + 2 * ChunkCfg<DT, D>::k_bytes; }
+    static constexpr size_t total_bytes() { return lds_bytes + ChunkCfg<DT, D>::k_bytes; }
     static_assert(CAP / TPR <= 64, "at most 64 list entries per lane in the solve");
 };
 
@@ -47,7 +49,7 @@ __device__ __forceinline__ void group_rank(unsigned long long mask, int g, int c
 }
 
 template <int DT, int D, int CAP>
-__global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef StreamCfg<D, CAP> C;
     constexpr int BM = C::BM, TPR = C::TPR;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void fwd_stream_kernel(FwdArgs a) {
         int wlo_k, whi_k;
         key_range(q0, BM, L, a.causal, a.window, &wlo_k, &whi_k);
         const int ch0 = wlo_k / kBN, ch1 = (whi_k + kBN - 1) / kBN;
-        ChunkStream<DT, D> cs;
+        ChunkStream<DT, D, 1> cs;
         cs.Kb = reinterpret_cast<char*>(kbufs);
         cs.Vb = nullptr;
         cs.kh = kh;
