@@ -12,9 +12,10 @@
 // (key c) and the d-slice [c D/16, (c + 1) D/16) of those rows' Q and dO.
 //   1. S is recomputed on MFMA from K chunks staged in LDS (chunk_stream.hpp)
 //      and every support entry (key, w) goes to its row's list in LDS.
-//   2. Per row, the entries are processed in batches whose V and K row
-//      gathers are all issued before any is used: dp by a 16-lane dot
-//      product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
+//   2. Per row, the entries are processed in batches of NB (V and K row
+//      gathers of a batch are issued before any is used; one entry per batch
+//      keeps the registers within three workgroups per CU): dp by a 16-lane
+//      dot product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
 //      dQ_i = scale (X - c_i Y) without another pass; then every entry adds
 //      scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.
 // A row whose support outgrows its list is finished by two more passes over
@@ -49,10 +50,12 @@ template <int DT, int D>
 struct BwdCfg : ChunkCfg<DT, D> {
     typedef ChunkCfg<DT, D> S;
     static constexpr int BM = 64;
-    static constexpr int CAP = 64;   // support entries per row
-    static constexpr int NB = 4;     // entries per gather batch
+    // support entries per row; with one K chunk buffer (ChunkStream<.., 1>)
+    // a bf16 d = 128 workgroup takes under a third of the LDS
+    static constexpr int CAP = 48;
+    static constexpr int NB = 1;     // entries per gather batch
     static constexpr size_t list_bytes = static_cast<size_t>(BM) * CAP * (2 * sizeof(float) + sizeof(uint16_t));
-    static constexpr size_t lds_bytes = 2 * S::k_bytes + list_bytes + 64;
+    static constexpr size_t lds_bytes = S::k_bytes + list_bytes + 64;
 };
 
 template <int DT, int DPL>
@@ -93,13 +96,13 @@ __device__ __forceinline__ void group_rank16(unsigned long long mask, int g, int
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(BwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef BwdCfg<DT, D> C;
     constexpr int DPL = D / 16, BM = C::BM, CAP = C::CAP, NB = C::NB, CK = C::S::CK;
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
-    float* lw = reinterpret_cast<float*>(Kb + 2 * C::S::k_bytes);    // [BM][CAP] w
+    float* lw = reinterpret_cast<float*>(Kb + C::S::k_bytes);        // [BM][CAP] w
     float* ldp = lw + BM * CAP;                                       // [BM][CAP] dp
     uint16_t* lk = reinterpret_cast<uint16_t*>(ldp + BM * CAP);       // [BM][CAP] key
     int* flag = reinterpret_cast<int*>(lk + BM * CAP);                // workgroup vote
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(BwdArgs a) {
     int wlo, whi;
     key_range(q0 + r0, 16, L, a.causal, a.window, &wlo, &whi);
 
-    ChunkStream<DT, D> cs;
+    ChunkStream<DT, D, 1> cs;
     cs.Kb = Kb;
     cs.Vb = nullptr;
     cs.kh = kh;
