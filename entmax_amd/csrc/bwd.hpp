@@ -10,12 +10,13 @@
 // dense pass.  One workgroup = 4 waves of 16 query rows of one (batch, head);
 // lane (g, c) of a wave holds rows 4g .. 4g + 3 of each 16 x 16 score tile
 // (key c) and the d-slice [c D/16, (c + 1) D/16) of those rows' Q and dO.
-//   1. S is recomputed on MFMA from K chunks staged in LDS (chunk_stream.hpp)
-//      and every support entry (key, w) goes to its row's list in LDS.
-//   2. Per row, the entries are processed in batches of NB (V and K row
-//      gathers of a batch are issued before any is used; one entry per batch
-//      keeps the registers within three workgroups per CU): dp by a 16-lane
-//      dot product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
+//   1. S is recomputed on MFMA from K chunks staged in LDS (chunk_stream.hpp,
+//      one buffer, loads one chunk ahead) and every support entry (key, w)
+//      goes to its row's list in LDS.
+//   2. Per row, the entries are processed in batches of NB = 2 (V and K row
+//      gathers of a batch are issued before any is used; small batches keep
+//      the registers within three workgroups per CU): dp by a 16-lane dot
+//      product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
 //      dQ_i = scale (X - c_i Y) without another pass; then every entry adds
 //      scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.
 // A row whose support outgrows its list is finished by two more passes over
@@ -53,7 +54,7 @@ struct BwdCfg : ChunkCfg<DT, D> {
     // support entries per row; with one K chunk buffer (ChunkStream<.., 1>)
     // a bf16 d = 128 workgroup takes under a third of the LDS
     static constexpr int CAP = 48;
-    static constexpr int NB = 1;     // entries per gather batch
+    static constexpr int NB = 2;     // entries per gather batch
     static constexpr size_t list_bytes = static_cast<size_t>(BM) * CAP * (2 * sizeof(float) + sizeof(uint16_t));
     static constexpr size_t lds_bytes = S::k_bytes + list_bytes + 64;
 };
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
     int wlo, whi;
     key_range(q0 + r0, 16, L, a.causal, a.window, &wlo, &whi);
 
-    ChunkStream<DT, D, 1> cs;
+    ChunkStream<DT, D, 1, 1> cs;
     cs.Kb = Kb;
     cs.Vb = nullptr;
     cs.kh = kh;

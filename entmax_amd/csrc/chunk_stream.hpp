@@ -35,8 +35,10 @@ struct ChunkCfg {
 
 // NBUF: LDS buffers per stream.  Two let a chunk be staged while the
 // previous one is in use (one barrier per chunk); one halves the LDS at the
-// cost of a second barrier per chunk.
-template <int DT, int D, int NBUF = 2>
+// cost of a second barrier per chunk.  NPRE (with one buffer): chunks in
+// flight in registers, 2 (loads issued two chunks ahead) or 1 (one chunk
+// ahead, half the registers).
+template <int DT, int D, int NBUF = 2, int NPRE = 2>
 struct ChunkStream {
     typedef typename InT<DT>::type T;
     typedef ChunkCfg<DT, D> C;
@@ -101,6 +103,19 @@ struct ChunkStream {
     template <typename F>
     __device__ __forceinline__ void run(int ch0, int ch1, bool withv, F&& fn) const {
         if (ch0 >= ch1) return;
+        if constexpr (NBUF == 1 && NPRE == 1) {
+            Pre pa;
+            prefetch(ch0, withv, pa);
+            for (int ch = ch0; ch < ch1; ++ch) {
+                stage(0, withv, pa);
+                const unsigned long long Ma = valid_bits(ch, pa);
+                __syncthreads();
+                if (ch + 1 < ch1) prefetch(ch + 1, withv, pa);
+                fn(ch, Kb, Vb, Ma);
+                __syncthreads();
+            }
+            return;
+        }
         if constexpr (NBUF == 1) {
             Pre pa, pb;
             prefetch(ch0, withv, pa);
