@@ -58,6 +58,12 @@ __device__ __forceinline__ float col4_sum(float v) {
     const u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+__device__ __forceinline__ int col4_sum_int(int v) {
+    const u32x2 a = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+    const unsigned t = a[0] + a[1];
+    const u32x2 b = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+    return static_cast<int>(b[0] + b[1]);
+}
 __device__ __forceinline__ float col4_max(float v) {
     const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     const float t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -138,7 +144,7 @@ __device__ __forceinline__ float col_exact(const float (&sl)[K], const ColState&
         const float d = s.hc - tt;            // >= 0
         float s1 = fmaf(s.cnt, d, s.a1);
         float s2 = fmaf(s.cnt * d, d, fmaf(2.f * d, s.a1, s.a2));
-        float cn = s.cnt;
+        int ci = static_cast<int>(s.cnt);   // an integer count: one add-with-carry per slot
         float mn = kInf;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -147,12 +153,12 @@ __device__ __forceinline__ float col_exact(const float (&sl)[K], const ColState&
             const bool in = x > tt;
             s1 += y;
             s2 = fmaf(y, y, s2);
-            cn += in ? 1.f : 0.f;
+            ci += in ? 1 : 0;
             mn = fminf(mn, in ? x : kInf);
         }
         s1 = col4_sum(s1);
         s2 = col4_sum(s2);
-        cn = col4_sum(cn);
+        const float cn = static_cast<float>(col4_sum_int(ci));
         mn = col4_min(mn);
         // closed form on the support {x > tt}: sum (x - tt - e)^2 = 1, the
         // smaller root e = (s1 - sqrt(D)) / cn = (s2 - 1) / (s1 + sqrt(D)),
