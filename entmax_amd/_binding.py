@@ -19,11 +19,14 @@ ENTMAX_F32 = 0
 ENTMAX_BF16 = 1
 
 EXPORTS = (
-    "entmax_attn_fwd",
     "entmax_attn_bwd",
-    "entmax_attn_probs",
-    "entmax_attn_status_string",
+    "entmax_attn_bwd_gqa",
+    "entmax_attn_fwd",
+    "entmax_attn_fwd_gqa",
     "entmax_attn_last_error",
+    "entmax_attn_probs",
+    "entmax_attn_probs_gqa",
+    "entmax_attn_status_string",
     "entmax_attn_version",
 )
 
@@ -53,6 +56,13 @@ def load_library(path=LIB_PATH):
     lib.entmax_attn_bwd.restype = i32
     lib.entmax_attn_probs.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_probs.restype = i32
+    # grouped-query variants: H_kv after H
+    lib.entmax_attn_fwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_fwd_gqa.restype = i32
+    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_bwd_gqa.restype = i32
+    lib.entmax_attn_probs_gqa.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_probs_gqa.restype = i32
     lib.entmax_attn_status_string.argtypes = [i32]
     lib.entmax_attn_status_string.restype = ctypes.c_char_p
     lib.entmax_attn_last_error.argtypes = []
@@ -83,16 +93,22 @@ def _dtype_code(t):
 
 
 def _check_qkv(q, k, v=None):
+    """q [B, H, L, d]; k, v [B, H_kv, L, d] with H_kv dividing H. Returns H_kv."""
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    hkv = k.shape[1] if k.dim() == 4 else -1
+    if hkv <= 0 or H % hkv != 0:
+        raise ValueError("k must be [B, H_kv, L, d] with H_kv dividing H")
     for name, t in (("k", k), ("v", v)):
         if t is None:
             continue
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError(f"{name} must match q in shape, dtype and device")
+        if t.shape != (B, hkv, L, d) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be [B, H_kv, L, d] with q's dtype and device")
     for t in (q, k, v):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("q, k, v must be contiguous GPU tensors")
+    return hkv
 
 
 def _check_mask(key_mask, q):
@@ -114,34 +130,36 @@ def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, ta
     Returns (out [B, H, L, d] float32, tau [B, H, L] float32 or None).
     """
     lib = load_library()
-    _check_qkv(q, k, v)
+    hkv = _check_qkv(q, k, v)
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
     if tau_out is None and want_tau:
         tau_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    rc = lib.entmax_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window),
-                             _ptr(out), _ptr(tau_out), B, H, L, d, _dtype_code(q), _stream(q))
+    rc = lib.entmax_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window),
+                                 _ptr(out), _ptr(tau_out), B, H, hkv, L, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return out, tau_out
 
 
 def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, dq=None, dk=None, dv=None):
-    """Gradients (dq, dk, dv) float32 [B, H, L, d] from the forward's tau."""
+    """Gradients float32: dq [B, H, L, d], dk and dv [B, H_kv, L, d], from the forward's tau."""
     lib = load_library()
-    _check_qkv(q, k, v)
+    hkv = _check_qkv(q, k, v)
     _check_qkv(q, dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
     if tau.shape != (B, H, L) or tau.dtype != torch.float32 or not tau.is_contiguous():
         raise ValueError("tau must be a contiguous [B, H, L] float32 tensor")
-    mk = lambda: torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)  # noqa: E731
-    dq = mk() if dq is None else dq
-    dk = mk() if dk is None else dk
-    dv = mk() if dv is None else dv
-    rc = lib.entmax_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
-                             _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, L, d, _dtype_code(q), _stream(q))
+    mk = lambda h: torch.empty((B, h, L, d), dtype=torch.float32, device=q.device)  # noqa: E731
+    dq = mk(H) if dq is None else dq
+    dk = mk(hkv) if dk is None else dk
+    dv = mk(hkv) if dv is None else dv
+    rc = lib.entmax_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, L, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return dq, dk, dv
 
@@ -149,13 +167,13 @@ def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, d
 def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=None):
     """Dense attention weights [B, H, L, L] float32 recomputed from tau."""
     lib = load_library()
-    _check_qkv(q, k)
+    hkv = _check_qkv(q, k)
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
     if probs is None:
         probs = torch.empty((B, H, L, L), dtype=torch.float32, device=q.device)
-    rc = lib.entmax_attn_probs(_ptr(q), _ptr(k), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
-                               _ptr(probs), B, H, L, d, _dtype_code(q), _stream(q))
+    rc = lib.entmax_attn_probs_gqa(_ptr(q), _ptr(k), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                                   _ptr(probs), B, H, hkv, L, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return probs
 

@@ -42,6 +42,7 @@ struct BwdArgs {
     float* dk;
     float* dv;
     int B, H, L;
+    int Hkv;   // key/value heads (H % Hkv == 0)
     int causal, window;
     float scale;
     int nqt;
@@ -117,12 +118,15 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
     const int L = a.L;
     const size_t head_off = static_cast<size_t>(bh) * L * D;
     const T* qh = static_cast<const T*>(a.q) + head_off;
-    const T* kh = static_cast<const T*>(a.k) + head_off;
-    const T* vh = static_cast<const T*>(a.v) + head_off;
+    // the key/value head; its dK and dV collect the atomics of every query
+    // head of its group
+    const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
+    const T* kh = static_cast<const T*>(a.k) + kv_off;
+    const T* vh = static_cast<const T*>(a.v) + kv_off;
     const T* doh = static_cast<const T*>(a.dout) + head_off;
     float* dqh = a.dq + head_off;
-    float* dkh = a.dk + head_off;
-    float* dvh = a.dv + head_off;
+    float* dkh = a.dk + kv_off;
+    float* dvh = a.dv + kv_off;
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
     const bool hasm = km != nullptr;
 

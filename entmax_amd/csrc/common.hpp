@@ -161,10 +161,20 @@ struct FwdArgs {
     float* out;
     float* tau;
     int B, H, L;
+    int Hkv;   // key/value heads (H % Hkv == 0)
     int causal, window;
     float scale;
     int nqt;   // query tiles per head
 };
+
+// Key/value head serving query head bh = b H + h when Hkv heads serve the H
+// query heads in consecutive groups of H / Hkv (the grouped-query repeat of
+// K and V in "ADASPLASH -- ROBERTA Benchmark Result", section 3, Step-by-Step
+// Tensor Execution Trace): b Hkv + h / (H / Hkv).  Uniform.
+__device__ __forceinline__ int kv_head(int bh, int H, int Hkv) {
+    const int b = bh / H;
+    return b * Hkv + (bh - b * H) / (H / Hkv);
+}
 
 template <int DT> struct InT;
 template <> struct InT<DT_F32> { typedef float type; };

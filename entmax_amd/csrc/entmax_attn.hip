@@ -34,8 +34,9 @@ int check_launch(const char* what) {
 }
 
 // Common argument checks; returns ENTMAX_OK or an error code.
-int check_common(int B, int H, int L, int d, int dtype, int causal, int window) {
+int check_common(int B, int H, int Hkv, int L, int d, int dtype, int causal, int window) {
     if (B <= 0 || H <= 0 || L <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, L must be positive (got %d, %d, %d)", B, H, L);
+    if (Hkv <= 0 || H % Hkv != 0) return fail(ENTMAX_ERR_INVALID_ARG, "H_kv = %d must divide H = %d", Hkv, H);
     if (window < 0) return fail(ENTMAX_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
     if (window > 0 && !causal) return fail(ENTMAX_ERR_INVALID_ARG, "window > 0 requires causal attention");
     if (d != 64 && d != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
@@ -136,7 +137,7 @@ int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
     const size_t lds = ea::BwdCfg<DT, D>::lds_bytes;
     int rc = set_lds(kern, lds);
     if (rc) return rc;
-    const size_t n = static_cast<size_t>(a.B) * a.H * a.L * D;
+    const size_t n = static_cast<size_t>(a.B) * a.Hkv * a.L * D;   // dK, dV: [B, H_kv, L, d]
     const unsigned fill_blocks = static_cast<unsigned>((n / 4 + 255) / 256 + 1);
     hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dk, n);
     hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dv, n);
@@ -148,15 +149,15 @@ int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
 
 extern "C" {
 
-int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
-                    float* out, float* tau_out, int B, int H, int L, int d, int dtype, void* stream) {
+int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                        float* out, float* tau_out, int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !v || !out) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
-    int rc = check_common(B, H, L, d, dtype, causal, window);
+    int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask;
     a.out = out; a.tau = tau_out;
-    a.B = B; a.H = H; a.L = L;
+    a.B = B; a.H = H; a.L = L; a.Hkv = Hkv;
     a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = 0;
@@ -166,14 +167,14 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* 
     return d == 64 ? dispatch_fwd<ea::DT_F32, 64>(a, st) : dispatch_fwd<ea::DT_F32, 128>(a, st);
 }
 
-int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
-                      const float* tau, float* probs, int B, int H, int L, int d, int dtype, void* stream) {
+int entmax_attn_probs_gqa(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
+                          const float* tau, float* probs, int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !tau || !probs) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, tau and probs must not be NULL");
-    int rc = check_common(B, H, L, d, dtype, causal, window);
+    int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::ProbsArgs a;
     a.q = q; a.k = k; a.key_mask = key_mask; a.tau = tau; a.probs = probs;
-    a.B = B; a.H = H; a.L = L; a.causal = causal ? 1 : 0; a.window = window;
+    a.B = B; a.H = H; a.L = L; a.Hkv = Hkv; a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nrt = (L + 15) / 16;
     a.nkt = (L + ea::kBN - 1) / ea::kBN;
@@ -191,22 +192,38 @@ int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int
     return check_launch("probs");
 }
 
-int entmax_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
-                    const float* tau, const void* dout, float* dq, float* dk, float* dv,
-                    int B, int H, int L, int d, int dtype, void* stream) {
+int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                        const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                        int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv)
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk and dv must not be NULL");
-    int rc = check_common(B, H, L, d, dtype, causal, window);
+    int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.B = B; a.H = H; a.L = L; a.causal = causal ? 1 : 0; a.window = window;
+    a.B = B; a.H = H; a.L = L; a.Hkv = Hkv; a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = (L + 63) / 64;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) return d == 64 ? launch_bwd<ea::DT_BF16, 64>(a, st) : launch_bwd<ea::DT_BF16, 128>(a, st);
     return d == 64 ? launch_bwd<ea::DT_F32, 64>(a, st) : launch_bwd<ea::DT_F32, 128>(a, st);
+}
+
+int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                    float* out, float* tau_out, int B, int H, int L, int d, int dtype, void* stream) {
+    return entmax_attn_fwd_gqa(q, k, v, key_mask, causal, window, out, tau_out, B, H, H, L, d, dtype, stream);
+}
+
+int entmax_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                    const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                    int B, int H, int L, int d, int dtype, void* stream) {
+    return entmax_attn_bwd_gqa(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, H, L, d, dtype, stream);
+}
+
+int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
+                      const float* tau, float* probs, int B, int H, int L, int d, int dtype, void* stream) {
+    return entmax_attn_probs_gqa(q, k, key_mask, causal, window, tau, probs, B, H, H, L, d, dtype, stream);
 }
 
 const char* entmax_attn_status_string(int status) {

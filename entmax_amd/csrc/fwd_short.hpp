@@ -142,8 +142,9 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
     const int L = a.L;
     const size_t head_off = static_cast<size_t>(bh) * L * D;
     const T* qh = static_cast<const T*>(a.q) + head_off;
-    const T* kh = static_cast<const T*>(a.k) + head_off;
-    const T* vh = static_cast<const T*>(a.v) + head_off;
+    const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
+    const T* kh = static_cast<const T*>(a.k) + kv_off;
+    const T* vh = static_cast<const T*>(a.v) + kv_off;
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
 
     int klo, khi;

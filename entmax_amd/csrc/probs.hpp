@@ -17,6 +17,7 @@ struct ProbsArgs {
     const float* tau;
     float* probs;
     int B, H, L;
+    int Hkv;   // key/value heads (H % Hkv == 0)
     int causal, window;
     float scale;
     int nrt, nkt;   // 16-row tiles, 64-key tiles per head
@@ -39,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void probs_kernel(ProbsArgs a) {
     const int L = a.L;
     const size_t head_off = static_cast<size_t>(bh) * L * D;
     const T* qh = static_cast<const T*>(a.q) + head_off;
-    const T* kh = static_cast<const T*>(a.k) + head_off;
+    const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
+    const T* kh = static_cast<const T*>(a.k) + kv_off;
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
 
     QFrag<DT, D> qf;

@@ -95,6 +95,29 @@ int entmax_attn_probs(const void *q, const void *k,
                       const float *tau, float *probs,
                       int B, int H, int L, int d, int dtype, void *stream);
 
+/*
+ * Grouped-query variants ("ADASPLASH -- ROBERTA Benchmark Result", section 3,
+ * Step-by-Step Tensor Execution Trace: K and V have H_kv heads, each repeated
+ * for H / H_kv consecutive query heads).  k, v: [B, H_kv, L, d]; query head
+ * h uses key/value head h / (H / H_kv).  dk, dv: [B, H_kv, L, d], each the
+ * sum over the query heads of its group.  H_kv must divide H (else
+ * ENTMAX_ERR_INVALID_ARG).  With H_kv = H these are the calls above, which
+ * are implemented through them.
+ */
+int entmax_attn_fwd_gqa(const void *q, const void *k, const void *v,
+                        const uint8_t *key_mask, int causal, int window,
+                        float *out, float *tau_out,
+                        int B, int H, int H_kv, int L, int d, int dtype, void *stream);
+int entmax_attn_bwd_gqa(const void *q, const void *k, const void *v,
+                        const uint8_t *key_mask, int causal, int window,
+                        const float *tau, const void *dout,
+                        float *dq, float *dk, float *dv,
+                        int B, int H, int H_kv, int L, int d, int dtype, void *stream);
+int entmax_attn_probs_gqa(const void *q, const void *k,
+                          const uint8_t *key_mask, int causal, int window,
+                          const float *tau, float *probs,
+                          int B, int H, int H_kv, int L, int d, int dtype, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *entmax_attn_status_string(int status);
 

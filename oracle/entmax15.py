@@ -196,23 +196,27 @@ def attention_forward(q, k, v, key_mask=None, causal=False, window=0,
     (``allowed_mask``), and O_i = sum_j A_ij V_j ("RoBERTa Base with AdaSplash
     Attention", Architecture Overview).
 
-    Arguments: q, k, v [B, H, L, d] (numpy or torch, any float dtype: upcast
-    exactly to float64), key_mask [B, L] (nonzero = valid key) or None.
-    ``rows`` optionally restricts the query rows computed (same for every
-    head).  Returns a dict with 'out' [nh, r, d], 'tau' [nh, r] and, when
-    asked, 'probs' [nh, r, L]; 'heads' lists the (b, h) pairs in order.
+    Arguments: q [B, H, L, d], k, v [B, H_kv, L, d] (numpy or torch, any
+    float dtype: upcast exactly to float64; H_kv divides H, and query head h
+    reads key/value head h // (H / H_kv), the grouped-query repeat of K and V
+    in "ADASPLASH -- ROBERTA Benchmark Result", section 3), key_mask [B, L]
+    (nonzero = valid key) or None.  ``rows`` optionally restricts the query
+    rows computed (same for every head).  Returns a dict with 'out'
+    [nh, r, d], 'tau' [nh, r] and, when asked, 'probs' [nh, r, L]; 'heads'
+    lists the (b, h) pairs in order.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, L, d = q.shape
+    rep = H // k.shape[1]
     scale = 1.0 / np.sqrt(d)
     hl = _head_list(B, H, heads)
     r_idx = np.arange(L) if rows is None else np.asarray(rows)
     outs, taus, probs = [], [], []
     for (b, h) in hl:
         ok = allowed_mask(L, _key_mask_row(key_mask, b), causal, window)[r_idx]
-        s = (q[b, h, r_idx] @ k[b, h].T) * scale
+        s = (q[b, h, r_idx] @ k[b, h // rep].T) * scale
         p, tau = entmax15_exact(s, ok)
-        outs.append(p @ v[b, h])
+        outs.append(p @ v[b, h // rep])
         taus.append(tau)
         if return_probs:
             probs.append(p)
@@ -234,33 +238,45 @@ def attention_backward(q, k, v, dout, key_mask=None, causal=False, window=0,
     and through s = q k^T / sqrt(d): dq = dS k / sqrt(d), dk = dS^T q / sqrt(d).
 
     Rows are processed in chunks of ``row_chunk`` to bound memory; the sums
-    over rows for dk and dv are plain accumulations.  Returns a dict with
-    'dq', 'dk', 'dv' [nh, L, d] and 'heads'.
+    over rows for dk and dv are plain accumulations.  k and v may have
+    H_kv heads (see ``attention_forward``).  Returns a dict with 'dq', 'dk',
+    'dv' [nh, L, d] (dk, dv: the contribution of each query head), 'heads'
+    and 'dk_kv', 'dv_kv' [B, H_kv, L, d]: the contributions summed over the
+    query heads of each key/value head (the gradients of k and v when every
+    head is selected).
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     B, H, L, d = q.shape
+    Hkv = k.shape[1]
+    rep = H // Hkv
     scale = 1.0 / np.sqrt(d)
     hl = _head_list(B, H, heads)
     dqs, dks, dvs = [], [], []
+    dk_kv = np.zeros((B, Hkv, L, d))
+    dv_kv = np.zeros((B, Hkv, L, d))
     for (b, h) in hl:
         kmr = _key_mask_row(key_mask, b)
+        hk = h // rep
         dq = np.zeros((L, d))
         dk = np.zeros((L, d))
         dv = np.zeros((L, d))
         for r0 in range(0, L, row_chunk):
             r = np.arange(r0, min(L, r0 + row_chunk))
             ok = allowed_mask(L, kmr, causal, window)[r]
-            s = (q[b, h, r] @ k[b, h].T) * scale
+            s = (q[b, h, r] @ k[b, hk].T) * scale
             p, _ = entmax15_exact(s, ok)
             w = np.sqrt(p)                                  # sqrt(p), 0 off support
-            gp = dout[b, h, r] @ v[b, h].T                  # dL/dA
+            gp = dout[b, h, r] @ v[b, hk].T                 # dL/dA
             den = w.sum(axis=1, keepdims=True)
             c = np.where(den > 0, (w * gp).sum(axis=1, keepdims=True) / np.where(den > 0, den, 1.0), 0.0)
             ds = w * (gp - c)
-            dq[r] = (ds @ k[b, h]) * scale
+            dq[r] = (ds @ k[b, hk]) * scale
             dk += (ds.T @ q[b, h, r]) * scale
             dv += p.T @ dout[b, h, r]
         dqs.append(dq)
         dks.append(dk)
         dvs.append(dv)
-    return {"dq": np.stack(dqs), "dk": np.stack(dks), "dv": np.stack(dvs), "heads": hl}
+        dk_kv[b, hk] += dk
+        dv_kv[b, hk] += dv
+    return {"dq": np.stack(dqs), "dk": np.stack(dks), "dv": np.stack(dvs), "heads": hl,
+            "dk_kv": dk_kv, "dv_kv": dv_kv}

@@ -30,8 +30,9 @@ def to_gpu(inp):
 
 
 def scores64(q, k, b, h, rows):
+    # k may have fewer (grouped) heads: query head h reads k head h // (H / H_kv)
     q64 = q[b, h].to(torch.float64).cpu().numpy()
-    k64 = k[b, h].to(torch.float64).cpu().numpy()
+    k64 = k[b, h // (q.shape[1] // k.shape[1])].to(torch.float64).cpu().numpy()
     return (q64[rows] @ k64.T) / math.sqrt(q.shape[-1])
 
 
@@ -102,14 +103,21 @@ def check_backward(inp, heads=None, label="", tau=None):
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
     ref = attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], inp["key_mask"], causal, window, heads=heads)
+    grouped = k.shape[1] != H
+    assert not grouped or len(heads) == B * H, "grouped k, v: every head is needed for their gradients"
     errs = {}
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
         got_c = got.cpu().numpy()
         worst = 0.0
-        for n, (b, h) in enumerate(heads):
-            r = ref[name][n]
-            scale = max(1.0, float(np.abs(r).max()))
-            worst = max(worst, float(np.abs(got_c[b, h] - r).max()) / scale)
+        if grouped and name != "dq":
+            # dk, dv of a key/value head: the sum over its query heads
+            r = ref[name + "_kv"]
+            worst = float(np.abs(got_c - r).max()) / max(1.0, float(np.abs(r).max()))
+        else:
+            for n, (b, h) in enumerate(heads):
+                r = ref[name][n]
+                scale = max(1.0, float(np.abs(r).max()))
+                worst = max(worst, float(np.abs(got_c[b, h] - r).max()) / scale)
         errs[name] = worst
     log(f"[parity]   max scaled err dq={errs['dq']:.3g} dk={errs['dk']:.3g} dv={errs['dv']:.3g} (tol {tol})")
     for name in ("dq", "dk", "dv"):

@@ -91,3 +91,22 @@ def test_binding_validates_before_calling():
     with pytest.raises(TypeError):
         from entmax_amd._binding import _dtype_code
         _dtype_code(torch.zeros(1, dtype=torch.float16))
+
+
+def test_grouped_query_rejects_bad_kv_heads(lib):
+    # H_kv must divide H
+    for hkv in (0, -1, 3):
+        assert lib.entmax_attn_fwd_gqa(P, P, P, None, 0, 0, P, None, 1, 4, hkv, 8, 64, 1, None) == 1
+        assert lib.entmax_attn_bwd_gqa(P, P, P, None, 0, 0, P, P, P, P, P, 1, 4, hkv, 8, 64, 1, None) == 1
+        assert lib.entmax_attn_probs_gqa(P, P, None, 0, 0, P, P, 1, 4, hkv, 8, 64, 1, None) == 1
+    assert b"H_kv" in lib.entmax_attn_last_error()
+
+
+def test_binding_checks_grouped_shapes():
+    import torch
+    from entmax_amd._binding import _check_qkv
+    q = torch.zeros(1, 4, 8, 64)
+    with pytest.raises(ValueError):
+        _check_qkv(q, torch.zeros(1, 3, 8, 64))     # 3 does not divide 4
+    with pytest.raises(ValueError):
+        _check_qkv(q, torch.zeros(1, 2, 8, 64), torch.zeros(1, 4, 8, 64))   # v must match k

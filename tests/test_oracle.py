@@ -384,3 +384,51 @@ def test_jacobian_identities():
         w = np.sqrt(p)
         J_closed = np.diag(w) - np.outer(w, w) / w.sum()
         np.testing.assert_allclose(J, J_closed, atol=1e-6)
+
+
+def test_grouped_query_forward_equals_repeated_heads():
+    # "ADASPLASH -- ROBERTA Benchmark Result", section 3: with H_kv < H the
+    # key/value heads are repeated (each for H / H_kv consecutive query
+    # heads) before the scores; the oracle takes k, v with H_kv heads.
+    rng = np.random.default_rng(21)
+    B, H, Hkv, L, d = 2, 6, 2, 9, 4
+    q = rng.normal(size=(B, H, L, d)) * 1.3
+    k, v = rng.normal(size=(B, Hkv, L, d)), rng.normal(size=(B, Hkv, L, d))
+    km = (rng.random((B, L)) > 0.2).astype(np.uint8)
+    for kw in ({}, {"key_mask": km}, {"causal": True, "window": 4}):
+        g = attention_forward(q, k, v, **kw)
+        r = attention_forward(q, np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1), **kw)
+        np.testing.assert_allclose(g["out"], r["out"], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(g["tau"], r["tau"], rtol=0, atol=1e-13)
+    # distinct heads of a group see the same keys but give different rows
+    assert not np.allclose(g["out"][0], g["out"][1])
+
+
+def test_grouped_query_backward_finite_differences():
+    # the gradient of a shared key/value head sums the query heads of its
+    # group: checked against central differences of the forward
+    rng = np.random.default_rng(22)
+    B, H, Hkv, L, d = 1, 4, 2, 6, 3
+    q = rng.normal(size=(B, H, L, d)) * 1.4
+    k, v = rng.normal(size=(B, Hkv, L, d)), rng.normal(size=(B, Hkv, L, d))
+    do = rng.normal(size=(B, H, L, d))
+    g = attention_backward(q, k, v, do, causal=True)
+    h = 1e-6
+    for name, x, ref in (("k", k, g["dk_kv"]), ("v", v, g["dv_kv"])):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = {"k": k, "v": v}
+            args[name] = xp
+            fp = _loss(q, args["k"], args["v"], do, causal=True)
+            args[name] = xm
+            fm = _loss(q, args["k"], args["v"], do, causal=True)
+            num[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(ref, num, atol=3e-7, err_msg=name)
+    dqn = np.zeros_like(q)
+    for idx in np.ndindex(*q.shape):
+        xp = q.copy(); xp[idx] += h
+        xm = q.copy(); xm[idx] -= h
+        dqn[idx] = (_loss(xp, k, v, do, causal=True) - _loss(xm, k, v, do, causal=True)) / (2 * h)
+    np.testing.assert_allclose(g["dq"], dqn[0], atol=3e-7)

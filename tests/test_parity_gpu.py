@@ -175,3 +175,33 @@ def test_backward_dense_support_overflow():
     # supports of hundreds of keys: the per-row list overflows
     inp = random_inputs(1, 2, 600, 64, "f32", seed=13, qk_gain=0.3)
     check_backward(inp, label="dense support")
+
+
+# ---- grouped-query attention (key/value heads shared by groups of query heads) ----
+
+def _grouped(inp, hkv):
+    out = dict(inp)
+    out["k"] = inp["k"][:, :hkv].contiguous()
+    out["v"] = inp["v"][:, :hkv].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("L,dtype,hkv", [(128, "bf16", 1), (100, "f32", 2), (600, "bf16", 2), (2200, "bf16", 1)])
+def test_grouped_query_forward(L, dtype, hkv):
+    # spans of <= 128, 129..2048 and > 2048 keys: the three forward kernels
+    inp = _grouped(random_inputs(2, 4, L, 64, dtype, seed=31, qk_gain=1.2, key_lengths=[L, L - L // 3]), hkv)
+    heads = None if L <= 600 else [(0, 0), (0, 3), (1, 1)]
+    check_forward(inp, heads=heads, label=f"gqa H4/Hkv{hkv}", check_probs=L <= 600)
+
+
+def test_grouped_query_causal_window_forward():
+    inp = _grouped(random_inputs(2, 6, 300, 128, "bf16", seed=32), 3)
+    inp["causal"], inp["window"] = True, 32
+    check_forward(inp, label="gqa causal window")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_query_backward(dtype):
+    # dk, dv of a shared head collect the atomics of all its query heads
+    inp = _grouped(random_inputs(2, 4, 90, 64, dtype, seed=33, qk_gain=1.5, key_lengths=[90, 61]), 2)
+    check_backward(inp, label="gqa")
