@@ -91,16 +91,40 @@ def entmax15_exact(s, allowed=None):
     above = allowed & (s > tau[:, None])
     p = np.where(above, ((s - tau[:, None]) / 2.0) ** 2, 0.0)
 
-    # KKT consistency: the support found equals {j : s_j > tau}
+    # KKT consistency: the support found equals {j : s_j > tau}, up to
+    # entries tied with tau to rounding (repeated score values, as low
+    # precision inputs have, put whole tie groups at the boundary); those
+    # carry p = ((s - tau)/2)^2 of the order of the rounding squared
     supp = above.sum(axis=1)
     bad = has & (supp != kstar + 1)
     if np.any(bad):
-        # ties exactly at tau may only shrink the strict support
-        if np.any(supp[bad] > kstar[bad] + 1):
+        scale = np.maximum(1.0, np.abs(np.where(has, top, 0.0)))
+        near = np.abs(s - tau[:, None]) <= 1e-12 * scale[:, None]
+        extra = above & ~near
+        kept = extra.sum(axis=1)
+        if np.any(kept[bad] > kstar[bad] + 1):
             raise AssertionError("support search inconsistent with KKT conditions")
     if squeeze:
         return p[0], tau[0]
     return p, tau
+
+
+def entmax15_backward(s, dp, allowed=None):
+    """Gradient of the scores from the gradient of p = entmax15(s), per row.
+
+    Jacobian of "ADASPLASH -- ROBERTA Benchmark Result", section 2.4: with
+    w = sqrt(p) (zero off the support), dp/ds = diag(w) - w w^T / sum(w), so
+    ds = w * dp - w * (w . dp) / sum(w).  A row without an allowed entry has
+    ds = 0.  Returns ds with the shape of s.
+    """
+    p, _ = entmax15_exact(s, allowed)
+    p = np.atleast_2d(p)
+    dp = np.atleast_2d(np.asarray(dp, dtype=np.float64))
+    w = np.sqrt(p)
+    den = w.sum(axis=1, keepdims=True)
+    c = np.where(den > 0, (w * dp).sum(axis=1, keepdims=True) / np.where(den > 0, den, 1.0), 0.0)
+    ds = w * (dp - c)
+    return ds[0] if np.ndim(s) == 1 else ds
 
 
 def entmax15_bisect(s, allowed=None, n_iter=25):
