@@ -149,13 +149,83 @@ def cpu_baseline(name, budget_s=12.0):
     }
 
 
+def bench_rows(args):
+    """The row-wise op (forward + backward on a [R, L] score matrix), HBM-bound."""
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from threadpoolctl import threadpool_limits
+        from entmax_amd.workloads import make_row_inputs
+        from oracle import entmax15_exact
+        inp = make_row_inputs("rows")
+        s64 = inp["scores"].to(__import__("torch").float64).numpy()
+        done, t0 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while time.perf_counter() - t0 < args.cpu_budget:
+                entmax15_exact(s64[done % s64.shape[0]:done % s64.shape[0] + 256])
+                done += 256
+        dt = time.perf_counter() - t0
+        L = s64.shape[1]
+        cpu = {"value": done * L * 6 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} rows of the rows workload, forward only (float64 numpy, one thread), {dt:.1f} s"}
+    import torch
+    from entmax_amd import entmax15_rows, entmax15_rows_bwd
+    from entmax_amd.workloads import make_row_inputs
+    inp = make_row_inputs("rows")
+    R, L = inp["spec"]["R"], inp["spec"]["L"]
+    dev = torch.device("cuda:0")
+    fwd_bytes = R * L * (2 + 4) + R * 4          # read bf16 scores, write fp32 p and tau
+    bwd_bytes = R * L * 12                        # read p and dp, write ds
+    nsets = max(2, math.ceil(2 * MALL_BYTES / (fwd_bytes + R * L * 8)))
+    sets = [{"s": inp["scores"].to(dev), "dp": inp["dp"].to(dev),
+             "p": torch.empty((R, L), device=dev), "tau": torch.empty((R,), device=dev),
+             "ds": torch.empty((R, L), device=dev)} for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(s, mid=None):
+        entmax15_rows(s["s"], p=s["p"], tau=s["tau"])
+        if mid is not None:
+            mid.record()
+        entmax15_rows_bwd(s["p"], s["dp"], ds=s["ds"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    bounds = [ev() for _ in range(args.steps + 1)]
+    mids = [ev() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    bounds[0].record()
+    for i in range(args.steps):
+        step(sets[i % nsets], mids[i])
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    fwd_ms = sum(bounds[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(mids[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)) / args.steps
+    ms_per_step = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    res = {
+        "metric": "row-wise 1.5-entmax fwd+bwd: effective GB/s (HBM roofline)",
+        "value": (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rows", "R": R, "L": L, "buffer_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "rows_fwd", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": fwd_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": fwd_bytes, "launch_ms": fwd_ms},
+        "cpu_baseline": cpu,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "bwd_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="encoder",
-                    choices=["tiny", "encoder", "long", "decoder", "longctx"])
+                    choices=["tiny", "encoder", "long", "decoder", "longctx", "rows"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -170,6 +240,10 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): every (batch, head) is independent, "
               "so the path shards by heads with no communication; run it once per GPU.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "rows":
+        bench_rows(args)
+        return
 
     # The CPU baseline runs first, before anything touches the GPU.
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)

@@ -13,5 +13,7 @@ from ._binding import (  # noqa: F401
     entmax_attn_bwd,
     entmax_attn_fwd,
     entmax_attn_probs,
+    entmax15_rows,
+    entmax15_rows_bwd,
     load_library,
 )

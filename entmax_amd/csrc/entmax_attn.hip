@@ -12,6 +12,7 @@
 #include "fwd_short.hpp"
 #include "fwd_stream.hpp"
 #include "probs.hpp"
+#include "rows.hpp"
 #include "bwd.hpp"
 
 namespace {
@@ -147,6 +148,25 @@ int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+template <int DT>
+void launch_rows_fwd(const ea::RowsArgs& a, hipStream_t st) {
+    const dim3 grid((a.R + 3) / 4), block(ea::kThreads);
+    if (a.L <= 256) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 1>), grid, block, 0, st, a);
+    else if (a.L <= 512) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 2>), grid, block, 0, st, a);
+    else if (a.L <= 1024) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 4>), grid, block, 0, st, a);
+    else if (a.L <= 2048) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 8>), grid, block, 0, st, a);
+    else if (a.L <= 4096) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 16>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 0>), grid, block, 0, st, a);
+}
+
+int check_rows(int R, int L) {
+    if (R <= 0 || L <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "rows and L must be positive (got %d, %d)", R, L);
+    if (L % 4 != 0) return fail(ENTMAX_ERR_UNSUPPORTED, "L = %d is not a multiple of 4", L);
+    if (static_cast<long long>(R) * L > (1LL << 40)) return fail(ENTMAX_ERR_UNSUPPORTED, "R * L too large");
+    if ((R + 3) / 4 > (1 << 30)) return fail(ENTMAX_ERR_UNSUPPORTED, "too many rows for one launch");
+    return ENTMAX_OK;
+}
+
 extern "C" {
 
 int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
@@ -224,6 +244,35 @@ int entmax_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* 
 int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
                       const float* tau, float* probs, int B, int H, int L, int d, int dtype, void* stream) {
     return entmax_attn_probs_gqa(q, k, key_mask, causal, window, tau, probs, B, H, H, L, d, dtype, stream);
+}
+
+int entmax15_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* tau, int R, int L, int dtype,
+                      void* stream) {
+    if (!scores || !p) return fail(ENTMAX_ERR_INVALID_ARG, "scores and p must not be NULL");
+    int rc = check_rows(R, L);
+    if (rc) return rc;
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    ea::RowsArgs a;
+    a.s = scores; a.mask = mask; a.p = p; a.tau = tau; a.R = R; a.L = L;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16) launch_rows_fwd<ea::DT_BF16>(a, st);
+    else launch_rows_fwd<ea::DT_F32>(a, st);
+    return check_launch("rows_fwd");
+}
+
+int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, void* stream) {
+    if (!p || !dp || !ds) return fail(ENTMAX_ERR_INVALID_ARG, "p, dp and ds must not be NULL");
+    int rc = check_rows(R, L);
+    if (rc) return rc;
+    ea::RowsBwdArgs a;
+    a.p = p; a.dp = dp; a.ds = ds; a.R = R; a.L = L;
+    const dim3 grid((R + 3) / 4), block(ea::kThreads);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L <= 256) hipLaunchKernelGGL(ea::rows_bwd_kernel<1>, grid, block, 0, st, a);
+    else if (L <= 1024) hipLaunchKernelGGL(ea::rows_bwd_kernel<4>, grid, block, 0, st, a);
+    else if (L <= 4096) hipLaunchKernelGGL(ea::rows_bwd_kernel<16>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(ea::rows_bwd_kernel<0>, grid, block, 0, st, a);
+    return check_launch("rows_bwd");
 }
 
 const char* entmax_attn_status_string(int status) {

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                     s.a1 += y;
                     s.a2 = fmaf(y, y, s.a2);
                     col[(len < CAP ? len : CAP) * kWave] = x;   // row CAP: overflow dump
-                    len += (x > s.lo) & (x > s.lb) & (x <= s.hi) ? 1 : 0;
+                    len += ((x > s.lo) & (x > s.lb) & (x <= s.hi)) ? 1 : 0;
                 }
             }
         });

@@ -1,0 +1,269 @@
+// Row-wise 1.5-entmax on a score matrix [R, L] (row-major), forward and
+// backward: the per-row threshold solve of the attention kernels as an op of
+// its own (the pages' entmax15_bisect export, "ADASPLASH -- ROBERTA
+// Benchmark Result", section 4).
+//
+// Forward: p_j = [(s_j - tau)/2]_+^2 over the allowed entries of the row
+// (section 2.2 Theorem 1), tau from 25 bisection steps (section 2.3 Theorem 2)
+// on the bracket [max - 2, max - 2/sqrt(n)] ("DistilBERT SST-2 with AdaSplash
+// Attention" model card, Mathematical Formulation 2), run in the half-scaled
+// shifted domain x = (s - max)/2 where the bracket is [-1, -1/sqrt(n)].
+// One wave per row; lane l holds entries 256 c + 4 l .. + 3 of chunk c, so
+// every load and store is one contiguous 1 KB (fp32) block per wave.  Rows of
+// at most 256 NV entries stay in registers for all 25 steps; longer rows are
+// re-read for every step (the pages' algorithm as printed; HBM-bound).
+//
+// Backward (section 2.4 Jacobian): with w = sqrt(p),
+// ds_j = w_j (dp_j - sum_k w_k dp_k / sum_k w_k).
+#pragma once
+
+#include "col_solve.hpp"
+#include "common.hpp"
+#include "tau_solver.hpp"
+
+namespace ea {
+
+struct RowsArgs {
+    const void* s;            // [R, L] scores (fp32 or bf16)
+    const uint8_t* mask;      // [R, L], nonzero = allowed; or null
+    float* p;                 // [R, L]
+    float* tau;               // [R] (score units) or null
+    int R, L;
+};
+
+// Sum over the 64 lanes of the wave, bitwise identical in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return col4_sum(row_sum<16>(v)); }
+__device__ __forceinline__ float wave_max(float v) { return col4_max(row_max<16>(v)); }
+
+// 4 consecutive entries of row `row` starting at column j (j % 4 == 0, may
+// run past L: those read column 0 and are marked invalid by the caller)
+template <int DT>
+__device__ __forceinline__ f32x4 load4(const void* s, size_t row_off, int j, int L) {
+    const int jj = j < L ? j : 0;   // whole quads: L % 4 == 0 is required
+    if constexpr (DT == DT_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(s) + row_off + jj);
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+    } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(s) + row_off + jj);
+    }
+}
+
+__device__ __forceinline__ unsigned valid4(const uint8_t* mask, size_t row_off, int j, int L) {
+    unsigned v = 0u;
+    if (j < L) {
+        const unsigned mb = mask ? *reinterpret_cast<const unsigned*>(mask + row_off + j) : 0x01010101u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v |= ((mb >> (8 * i)) & 0xFFu) != 0u ? (1u << i) : 0u;
+    }
+    return v;
+}
+
+// NV chunks of 256 entries per row in registers (L <= 256 NV); NV = 0: any
+// L, streamed from memory at every step.
+template <int DT, int NV>
+__global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (row >= a.R) return;   // uniform per wave; no barrier below
+    const int L = a.L;
+    const size_t off = static_cast<size_t>(row) * L;
+    const int nch = NV > 0 ? NV : (L + 255) / 256;
+
+    // pass 1: row max and allowed count
+    float mraw = -kInf, cnt = 0.f;
+    f32x4 xs[NV > 0 ? NV : 1];
+    unsigned vb[NV > 0 ? NV : 1];
+    for (int c = 0; c < nch; ++c) {
+        const int j = 256 * c + 4 * lane;
+        const f32x4 v = load4<DT>(a.s, off, j, L);
+        const unsigned ok = valid4(a.mask, off, j, L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool on = (ok >> i) & 1u;
+            mraw = fmaxf(mraw, on ? v[i] : -kInf);
+            cnt += on ? 1.f : 0.f;
+        }
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q == c) { xs[q] = v; vb[q] = ok; }
+        }
+    }
+    const float m = wave_max(mraw);
+    const float n = wave_sum(cnt);
+    if (n == 0.f) {
+        // no allowed entry: p = 0, tau = +inf
+        for (int c = 0; c < nch; ++c) {
+            const int j = 256 * c + 4 * lane;
+            if (j < L) *reinterpret_cast<f32x4*>(a.p + off + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (a.tau != nullptr && lane == 0) a.tau[row] = kInf;
+        return;
+    }
+    // x = (s - m)/2 on allowed entries, -inf elsewhere
+    auto shifted = [&](const f32x4& v, unsigned ok) {
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = ((ok >> i) & 1u) ? 0.5f * (v[i] - m) : -kInf;
+        return x;
+    };
+    if constexpr (NV > 0) {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) xs[q] = shifted(xs[q], vb[q]);
+    }
+    // 25 bisection steps: g(mid) = sum [x - mid]_+^2 (each term at most 1:
+    // x <= 0 and mid >= -1), g > 1 moves the lower end.  Entries at or below
+    // the lower end never count again (every later midpoint lies above it):
+    // after the first kFirst steps, when no lane holds more than kCand
+    // entries above the lower end, the remaining steps run over those slots.
+    constexpr int kFirst = 4, kCand = 4;
+    float lo = -1.f, hi = -__builtin_amdgcn_rsqf(n);
+    auto step = [&](auto&& partial) {
+        const float mid = 0.5f * (lo + hi);
+        if (wave_sum(partial(mid)) > 1.f) lo = mid;
+        else hi = mid;
+    };
+    auto full = [&](float mid) {
+        float acc = 0.f;
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float y = relu1(xs[q][i] - mid);
+                    acc = fmaf(y, y, acc);
+                }
+        } else {
+            for (int c = 0; c < nch; ++c) {
+                const int j = 256 * c + 4 * lane;
+                const f32x4 x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, L));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float y = relu1(x[i] - mid);
+                    acc = fmaf(y, y, acc);
+                }
+            }
+        }
+        return acc;
+    };
+    int it = 0;
+    bool few = false;
+    float cs[kCand];
+    if constexpr (NV > 0) {
+        for (; it < kFirst; ++it) step(full);
+        int nc = 0;
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) cs[k] = -kInf;
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = xs[q][i];
+                const bool cand = x > lo;
+#pragma unroll
+                for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
+                nc += cand ? 1 : 0;
+            }
+        few = !__any(nc > kCand);
+    }
+    if (few) {
+        for (; it < kIters; ++it)
+            step([&](float mid) {
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < kCand; ++k) {
+                    const float y = relu1(cs[k] - mid);
+                    acc = fmaf(y, y, acc);
+                }
+                return acc;
+            });
+    } else {
+        for (; it < kIters; ++it) step(full);
+    }
+    const float t = 0.5f * (lo + hi);
+    if (a.tau != nullptr && lane == 0) a.tau[row] = 2.f * t + m;
+    for (int c = 0; c < nch; ++c) {
+        const int j = 256 * c + 4 * lane;
+        f32x4 x;
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q == c) x = xs[q];
+        } else {
+            x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, L));
+        }
+        f32x4 p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float y = relu1(x[i] - t);
+            p[i] = y * y;
+        }
+        if (j < L) *reinterpret_cast<f32x4*>(a.p + off + j) = p;
+    }
+}
+
+struct RowsBwdArgs {
+    const float* p;    // [R, L]
+    const float* dp;   // [R, L]
+    float* ds;         // [R, L]
+    int R, L;
+};
+
+// One wave per row: sum w and sum w dp, then ds = w (dp - c).  Rows of at
+// most 256 NV entries are read once and kept in registers; NV = 0 reads p
+// and dp twice.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void rows_bwd_kernel(RowsBwdArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (row >= a.R) return;
+    const int L = a.L;
+    const size_t off = static_cast<size_t>(row) * L;
+    constexpr int NR = NV > 0 ? NV : 1;
+    f32x4 ws[NR], ds_[NR];
+    float sw = 0.f, swd = 0.f;
+    const int nch = NV > 0 ? NV : (L + 255) / 256;
+    for (int c = 0; c < nch; ++c) {
+        const int j = 256 * c + 4 * lane;
+        const int jj = j < L ? j : 0;   // past L: read column 0, weight 0
+        const f32x4 p = *reinterpret_cast<const f32x4*>(a.p + off + jj);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(a.dp + off + jj);
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = j < L ? __builtin_sqrtf(p[i]) : 0.f;
+            sw += w[i];
+            swd = fmaf(w[i], d[i], swd);
+        }
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q == c) { ws[q] = w; ds_[q] = d; }
+        }
+    }
+    sw = wave_sum(sw);
+    swd = wave_sum(swd);
+    const float cc = sw > 0.f ? swd / sw : 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const int j = 256 * c + 4 * lane;
+        f32x4 w, d;
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q == c) { w = ws[q]; d = ds_[q]; }
+        } else {
+            const int jj = j < L ? j : 0;
+            const f32x4 p = *reinterpret_cast<const f32x4*>(a.p + off + jj);
+            d = *reinterpret_cast<const f32x4*>(a.dp + off + jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = __builtin_sqrtf(p[i]);
+        }
+        f32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = w[i] * (d[i] - cc);
+        if (j < L) *reinterpret_cast<f32x4*>(a.ds + off + j) = r;
+    }
+}
+
+}  // namespace ea

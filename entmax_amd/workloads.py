@@ -22,6 +22,10 @@ settings; no dataset is used):
 * ``decoder``   B8 H12 L2048 d64 bf16, N(0,1), causal with a 32-key window.
 * ``longctx``   B1 H32 L8192 d128 bf16, Q and K times 2, V and dO N(0,1);
   forward and backward.
+
+Row-wise op (``make_row_inputs``): ``rows`` is a [98304, 1024] bf16 score
+matrix (the rows of the long workload's 8 x 12 heads) drawn N(0,1), with a
+float32 N(0,1) gradient for the backward; seed 1006.
 """
 
 from dataclasses import dataclass, field
@@ -123,3 +127,16 @@ def random_inputs(B, H, L, d, dtype="bf16", seed=0, qk_gain=1.0, key_lengths=Non
     for name_, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         res[name_] = x.to(dt).contiguous().to(device)
     return res
+
+
+ROWS = {"rows": {"R": 98304, "L": 1024, "dtype": "bf16", "number": 6}}
+
+
+def make_row_inputs(name="rows", device="cpu"):
+    """Scores [R, L] (workload dtype) and an incoming gradient [R, L] float32."""
+    w = ROWS[name]
+    gen = torch.Generator().manual_seed(1000 + w["number"])
+    s = torch.randn((w["R"], w["L"]), generator=gen)
+    dp = torch.randn((w["R"], w["L"]), generator=gen)
+    return {"scores": s.to(_DTYPES[w["dtype"]]).contiguous().to(device), "dp": dp.to(device), "spec": w}
+

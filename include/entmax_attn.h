@@ -118,6 +118,27 @@ int entmax_attn_probs_gqa(const void *q, const void *k,
                           const float *tau, float *probs,
                           int B, int H, int H_kv, int L, int d, int dtype, void *stream);
 
+/*
+ * Row-wise 1.5-entmax as an op of its own (the pages' entmax15_bisect
+ * export, "ADASPLASH -- ROBERTA Benchmark Result", section 4), with the same
+ * threshold as the attention calls: scores [R, L] (dtype ENTMAX_F32 or
+ * ENTMAX_BF16, row-major), mask [R, L] uint8 (nonzero = allowed) or NULL,
+ * p [R, L] float32 with p_j = [(s_j - tau)/2]_+^2 over the allowed entries
+ * (0 elsewhere), tau [R] float32 in score units or NULL.  A row without an
+ * allowed entry gets p = 0 and tau = +inf.  L must be a multiple of 4
+ * (ENTMAX_ERR_UNSUPPORTED otherwise); pointers 16-byte aligned.  Rows of up
+ * to 4096 entries are solved in registers; longer rows are re-read from
+ * memory at each of the 25 bisection steps.
+ */
+int entmax15_rows_fwd(const void *scores, const uint8_t *mask, float *p, float *tau,
+                      int R, int L, int dtype, void *stream);
+
+/*
+ * Its backward (section 2.4 Jacobian): ds_j = w_j (dp_j - sum_k w_k dp_k /
+ * sum_k w_k) with w = sqrt(p); p, dp, ds [R, L] float32 (ds overwritten).
+ */
+int entmax15_rows_bwd(const float *p, const float *dp, float *ds, int R, int L, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *entmax_attn_status_string(int status);
 

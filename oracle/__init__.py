@@ -26,6 +26,7 @@ the variational objective and finite differences.  No function here is
 
 from .entmax15 import (  # noqa: F401
     allowed_mask,
+    entmax15_backward,
     entmax15_exact,
     entmax15_bisect,
     attention_forward,

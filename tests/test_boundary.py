@@ -18,7 +18,7 @@ def _declared_functions():
     for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(hdr).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"\b(entmax_\w+)\s*\(", text)
+        names += re.findall(r"\b(entmax\w+)\s*\(", text)
     return sorted(set(names))
 
 
