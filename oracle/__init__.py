@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for 1.5-entmax attention.
+"""Float64 CPU oracle for 1.5-entmax attention and row-wise alpha-entmax.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -17,10 +17,13 @@ Sources (the pages this follows, cited by title and section):
   (S = Q K^T / 8, O_i = sum_{A_ij > 0} A_ij V_j), Mathematical Formulation 1-2.
 * "DistilBERT SST-2 with AdaSplash Attention" model card: Mathematical
   Formulation 2 (bracket [max - 2, max - 2/sqrt(L)]) and 3 (exact zeros).
+* "ADASPLASH -- ROBERTA Benchmark Result", section 4 (the entmax_bisect
+  routine for any alpha in (1, 2]): ``entmax_alpha.py``.
 
 Every function is pinned by CPU tests in ``tests/test_oracle*.py`` against
-closed forms, brute-force support enumeration, an independent bisection,
-the variational objective and finite differences.  No function here is
+closed forms (the 1.5 closed form, sparsemax at alpha = 2), brute-force
+support enumeration, an independent bisection, the softmax limit as alpha
+goes to 1, the variational objective and finite differences.  No function here is
 "parity unpinned".
 """
 
@@ -32,4 +35,10 @@ from .entmax15 import (  # noqa: F401
     attention_forward,
     attention_backward,
     tsallis15_objective,
+)
+from .entmax_alpha import (  # noqa: F401
+    entmax_alpha_backward,
+    entmax_alpha_bisect,
+    entmax_alpha_exact,
+    tsallis_objective,
 )
