@@ -15,5 +15,7 @@ from ._binding import (  # noqa: F401
     entmax_attn_probs,
     entmax15_rows,
     entmax15_rows_bwd,
+    entmax_bisect_rows,
+    entmax_bisect_rows_bwd,
     load_library,
 )

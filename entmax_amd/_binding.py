@@ -30,6 +30,8 @@ EXPORTS = (
     "entmax_attn_probs_gqa",
     "entmax_attn_status_string",
     "entmax_attn_version",
+    "entmax_bisect_rows_bwd",
+    "entmax_bisect_rows_fwd",
 )
 
 _lib = None
@@ -69,6 +71,11 @@ def load_library(path=LIB_PATH):
     lib.entmax15_rows_fwd.restype = i32
     lib.entmax15_rows_bwd.argtypes = [fp, fp, fp, i32, i32, vp]
     lib.entmax15_rows_bwd.restype = i32
+    f32 = ctypes.c_float
+    lib.entmax_bisect_rows_fwd.argtypes = [vp, u8p, fp, fp, i32, i32, f32, i32, vp]
+    lib.entmax_bisect_rows_fwd.restype = i32
+    lib.entmax_bisect_rows_bwd.argtypes = [fp, fp, fp, i32, i32, f32, vp]
+    lib.entmax_bisect_rows_bwd.restype = i32
     lib.entmax_attn_status_string.argtypes = [i32]
     lib.entmax_attn_status_string.restype = ctypes.c_char_p
     lib.entmax_attn_last_error.argtypes = []
@@ -182,6 +189,49 @@ def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=No
                                    _ptr(probs), B, H, hkv, L, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return probs
+
+
+def entmax_bisect_rows(scores, alpha=1.5, mask=None, p=None, tau=None, want_tau=True):
+    """Row-wise alpha-entmax (alpha in (1, 2]) of a [R, L] score matrix
+    (float32 or bfloat16).
+
+    mask: [R, L] uint8 (nonzero = allowed) or None.  Returns
+    (p [R, L] float32, tau [R] float32 in score units or None), with
+    p = [(alpha - 1)(s - tau)]_+^(1/(alpha - 1)).
+    """
+    lib = load_library()
+    if scores.dim() != 2 or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous [R, L] GPU tensor")
+    R, L = scores.shape
+    if mask is not None:
+        if mask.shape != (R, L) or mask.dtype != torch.uint8 or mask.device != scores.device:
+            raise ValueError("mask must be a [R, L] uint8 tensor on the scores' device")
+        mask = mask.contiguous()
+    if p is None:
+        p = torch.empty((R, L), dtype=torch.float32, device=scores.device)
+    if tau is None and want_tau:
+        tau = torch.empty((R,), dtype=torch.float32, device=scores.device)
+    rc = lib.entmax_bisect_rows_fwd(_ptr(scores), _ptr(mask), _ptr(p), _ptr(tau), R, L, float(alpha),
+                                    _dtype_code(scores), _stream(scores))
+    _check(lib, rc)
+    return p, tau
+
+
+def entmax_bisect_rows_bwd(p, dp, alpha=1.5, ds=None):
+    """Gradient of the scores of ``entmax_bisect_rows`` from the gradient of p
+    (float32 [R, L]); alpha must be the forward's."""
+    lib = load_library()
+    for name, t in (("p", p), ("dp", dp)):
+        if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [R, L] float32 GPU tensor")
+    if dp.shape != p.shape:
+        raise ValueError("dp must match p")
+    R, L = p.shape
+    if ds is None:
+        ds = torch.empty((R, L), dtype=torch.float32, device=p.device)
+    rc = lib.entmax_bisect_rows_bwd(_ptr(p), _ptr(dp), _ptr(ds), R, L, float(alpha), _stream(p))
+    _check(lib, rc)
+    return ds
 
 
 def entmax15_rows(scores, mask=None, p=None, tau=None, want_tau=True):

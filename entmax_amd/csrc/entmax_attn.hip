@@ -148,15 +148,36 @@ int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+template <int DT, bool GEN>
+void launch_rows_fwd_g(const ea::RowsArgs& a, hipStream_t st) {
+    const dim3 grid((a.R + 3) / 4), block(ea::kThreads);
+    if (a.L <= 256) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 1, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 512) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 2, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 1024) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 4, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 2048) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 8, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 4096) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 16, GEN>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 0, GEN>), grid, block, 0, st, a);
+}
+
+// alpha = 1.5 takes the instantiation that squares instead of calling powers
 template <int DT>
 void launch_rows_fwd(const ea::RowsArgs& a, hipStream_t st) {
+    if (a.alpha == 1.5f) launch_rows_fwd_g<DT, false>(a, st);
+    else launch_rows_fwd_g<DT, true>(a, st);
+}
+
+template <bool GEN>
+void launch_rows_bwd_g(const ea::RowsBwdArgs& a, hipStream_t st) {
     const dim3 grid((a.R + 3) / 4), block(ea::kThreads);
-    if (a.L <= 256) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 1>), grid, block, 0, st, a);
-    else if (a.L <= 512) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 2>), grid, block, 0, st, a);
-    else if (a.L <= 1024) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 4>), grid, block, 0, st, a);
-    else if (a.L <= 2048) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 8>), grid, block, 0, st, a);
-    else if (a.L <= 4096) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 16>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 0>), grid, block, 0, st, a);
+    if (a.L <= 256) hipLaunchKernelGGL((ea::rows_bwd_kernel<1, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 1024) hipLaunchKernelGGL((ea::rows_bwd_kernel<4, GEN>), grid, block, 0, st, a);
+    else if (a.L <= 4096) hipLaunchKernelGGL((ea::rows_bwd_kernel<16, GEN>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((ea::rows_bwd_kernel<0, GEN>), grid, block, 0, st, a);
+}
+
+void launch_rows_bwd(const ea::RowsBwdArgs& a, hipStream_t st) {
+    if (a.alpha == 1.5f) launch_rows_bwd_g<false>(a, st);
+    else launch_rows_bwd_g<true>(a, st);
 }
 
 int check_rows(int R, int L) {
@@ -246,33 +267,39 @@ int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int
     return entmax_attn_probs_gqa(q, k, key_mask, causal, window, tau, probs, B, H, H, L, d, dtype, stream);
 }
 
-int entmax15_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* tau, int R, int L, int dtype,
-                      void* stream) {
+int entmax_bisect_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* tau, int R, int L, float alpha,
+                           int dtype, void* stream) {
     if (!scores || !p) return fail(ENTMAX_ERR_INVALID_ARG, "scores and p must not be NULL");
+    if (!(alpha > 1.f && alpha <= 2.f)) return fail(ENTMAX_ERR_INVALID_ARG, "alpha = %g outside (1, 2]", alpha);
     int rc = check_rows(R, L);
     if (rc) return rc;
     if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
     ea::RowsArgs a;
-    a.s = scores; a.mask = mask; a.p = p; a.tau = tau; a.R = R; a.L = L;
+    a.s = scores; a.mask = mask; a.p = p; a.tau = tau; a.R = R; a.L = L; a.alpha = alpha;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) launch_rows_fwd<ea::DT_BF16>(a, st);
     else launch_rows_fwd<ea::DT_F32>(a, st);
     return check_launch("rows_fwd");
 }
 
-int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, void* stream) {
+int entmax_bisect_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, float alpha, void* stream) {
     if (!p || !dp || !ds) return fail(ENTMAX_ERR_INVALID_ARG, "p, dp and ds must not be NULL");
+    if (!(alpha > 1.f && alpha <= 2.f)) return fail(ENTMAX_ERR_INVALID_ARG, "alpha = %g outside (1, 2]", alpha);
     int rc = check_rows(R, L);
     if (rc) return rc;
     ea::RowsBwdArgs a;
-    a.p = p; a.dp = dp; a.ds = ds; a.R = R; a.L = L;
-    const dim3 grid((R + 3) / 4), block(ea::kThreads);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (L <= 256) hipLaunchKernelGGL(ea::rows_bwd_kernel<1>, grid, block, 0, st, a);
-    else if (L <= 1024) hipLaunchKernelGGL(ea::rows_bwd_kernel<4>, grid, block, 0, st, a);
-    else if (L <= 4096) hipLaunchKernelGGL(ea::rows_bwd_kernel<16>, grid, block, 0, st, a);
-    else hipLaunchKernelGGL(ea::rows_bwd_kernel<0>, grid, block, 0, st, a);
+    a.p = p; a.dp = dp; a.ds = ds; a.R = R; a.L = L; a.alpha = alpha;
+    launch_rows_bwd(a, static_cast<hipStream_t>(stream));
     return check_launch("rows_bwd");
+}
+
+int entmax15_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* tau, int R, int L, int dtype,
+                      void* stream) {
+    return entmax_bisect_rows_fwd(scores, mask, p, tau, R, L, 1.5f, dtype, stream);
+}
+
+int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, void* stream) {
+    return entmax_bisect_rows_bwd(p, dp, ds, R, L, 1.5f, stream);
 }
 
 const char* entmax_attn_status_string(int status) {

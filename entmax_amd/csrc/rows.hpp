@@ -1,19 +1,20 @@
-// Row-wise 1.5-entmax on a score matrix [R, L] (row-major), forward and
+// Row-wise alpha-entmax on a score matrix [R, L] (row-major), forward and
 // backward: the per-row threshold solve of the attention kernels as an op of
-// its own (the pages' entmax15_bisect export, "ADASPLASH -- ROBERTA
-// Benchmark Result", section 4).
+// its own (the pages' entmax_bisect and entmax15_bisect exports, "ADASPLASH --
+// ROBERTA Benchmark Result", section 4), for alpha in (1, 2].
 //
-// Forward: p_j = [(s_j - tau)/2]_+^2 over the allowed entries of the row
-// (section 2.2 Theorem 1), tau from 25 bisection steps (section 2.3 Theorem 2)
-// on the bracket [max - 2, max - 2/sqrt(n)] ("DistilBERT SST-2 with AdaSplash
-// Attention" model card, Mathematical Formulation 2), run in the half-scaled
-// shifted domain x = (s - max)/2 where the bracket is [-1, -1/sqrt(n)].
+// Forward at alpha = 1.5: p_j = [(s_j - tau)/2]_+^2 over the allowed entries
+// of the row (section 2.2 Theorem 1), tau from 25 bisection steps (section
+// 2.3 Theorem 2) on the bracket [max - 2, max - 2/sqrt(n)] ("DistilBERT
+// SST-2 with AdaSplash Attention" model card, Mathematical Formulation 2),
+// run in the half-scaled shifted domain x = (s - max)/2 where the bracket is
+// [-1, -1/sqrt(n)].  Other alphas use the same steps with the powers below.
 // One wave per row; lane l holds entries 256 c + 4 l .. + 3 of chunk c, so
 // every load and store is one contiguous 1 KB (fp32) block per wave.  Rows of
 // at most 256 NV entries stay in registers for all 25 steps; longer rows are
 // re-read for every step (the pages' algorithm as printed; HBM-bound).
 //
-// Backward (section 2.4 Jacobian): with w = sqrt(p),
+// Backward (section 2.4 Jacobian): with w = sqrt(p) at alpha = 1.5,
 // ds_j = w_j (dp_j - sum_k w_k dp_k / sum_k w_k).
 #pragma once
 
@@ -29,7 +30,18 @@ struct RowsArgs {
     float* p;                 // [R, L]
     float* tau;               // [R] (score units) or null
     int R, L;
+    float alpha;              // in (1, 2]; 1.5 unless GEN
 };
+
+// General alpha ("ADASPLASH -- ROBERTA Benchmark Result", section 2.1, and
+// the entmax_bisect routine of section 4): p_j = [(alpha - 1)(s_j - max) - t]_+
+// ^ (1/(alpha - 1)), t with sum p = 1, in the domain x = (alpha - 1)(s - max)
+// <= 0 where the bracket [-1, -n^(1 - alpha)] holds (at -1 the maximum alone
+// gives 1; at -n^(1-alpha) each of the n terms is at most 1/n).  Powers of y
+// in [0, 1] by the hardware base-2 exponential and logarithm (about 1 ulp).
+__device__ __forceinline__ float pow01(float y, float e) {
+    return y > 0.f ? __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(y)) : 0.f;
+}
 
 // Sum over the 64 lanes of the wave, bitwise identical in every lane.
 __device__ __forceinline__ float wave_sum(float v) { return col4_sum(row_sum<16>(v)); }
@@ -61,8 +73,12 @@ __device__ __forceinline__ unsigned valid4(const uint8_t* mask, size_t row_off, 
 
 // NV chunks of 256 entries per row in registers (L <= 256 NV); NV = 0: any
 // L, streamed from memory at every step.
-template <int DT, int NV>
+template <int DT, int NV, bool GEN>
 __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
+    const float am1 = GEN ? a.alpha - 1.f : 0.5f;        // alpha - 1
+    const float beta = GEN ? 1.f / (a.alpha - 1.f) : 2.f;   // 1 / (alpha - 1)
+    // [y]^beta: a square for alpha = 1.5
+    auto pw = [&](float y) { return GEN ? pow01(y, beta) : y * y; };
     const int lane = threadIdx.x % kWave;
     const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (row >= a.R) return;   // uniform per wave; no barrier below
@@ -105,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
     auto shifted = [&](const f32x4& v, unsigned ok) {
         f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = ((ok >> i) & 1u) ? 0.5f * (v[i] - m) : -kInf;
+        for (int i = 0; i < 4; ++i) x[i] = ((ok >> i) & 1u) ? am1 * (v[i] - m) : -kInf;
         return x;
     };
     if constexpr (NV > 0) {
@@ -118,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
     // after the first kFirst steps, when no lane holds more than kCand
     // entries above the lower end, the remaining steps run over those slots.
     constexpr int kFirst = 4, kCand = 4;
-    float lo = -1.f, hi = -__builtin_amdgcn_rsqf(n);
+    float lo = -1.f, hi = GEN ? -__builtin_amdgcn_exp2f(-am1 * __builtin_amdgcn_logf(n)) : -__builtin_amdgcn_rsqf(n);
     auto step = [&](auto&& partial) {
         const float mid = 0.5f * (lo + hi);
         if (wave_sum(partial(mid)) > 1.f) lo = mid;
@@ -131,8 +147,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
             for (int q = 0; q < NV; ++q)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float y = relu1(xs[q][i] - mid);
-                    acc = fmaf(y, y, acc);
+                    acc += pw(relu1(xs[q][i] - mid));
                 }
         } else {
             for (int c = 0; c < nch; ++c) {
@@ -140,8 +155,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
                 const f32x4 x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, L));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float y = relu1(x[i] - mid);
-                    acc = fmaf(y, y, acc);
+                    acc += pw(relu1(x[i] - mid));
                 }
             }
         }
@@ -173,8 +187,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int k = 0; k < kCand; ++k) {
-                    const float y = relu1(cs[k] - mid);
-                    acc = fmaf(y, y, acc);
+                    acc += pw(relu1(cs[k] - mid));
                 }
                 return acc;
             });
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
         for (; it < kIters; ++it) step(full);
     }
     const float t = 0.5f * (lo + hi);
-    if (a.tau != nullptr && lane == 0) a.tau[row] = 2.f * t + m;
+    if (a.tau != nullptr && lane == 0) a.tau[row] = m + t * beta;   // score units: p = [(alpha-1)(s - tau)]_+^beta
     for (int c = 0; c < nch; ++c) {
         const int j = 256 * c + 4 * lane;
         f32x4 x;
@@ -195,10 +208,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
         }
         f32x4 p;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float y = relu1(x[i] - t);
-            p[i] = y * y;
-        }
+        for (int i = 0; i < 4; ++i) p[i] = pw(relu1(x[i] - t));
         if (j < L) *reinterpret_cast<f32x4*>(a.p + off + j) = p;
     }
 }
@@ -208,13 +218,19 @@ struct RowsBwdArgs {
     const float* dp;   // [R, L]
     float* ds;         // [R, L]
     int R, L;
+    float alpha;       // in (1, 2]; 1.5 unless GEN
 };
 
 // One wave per row: sum w and sum w dp, then ds = w (dp - c).  Rows of at
 // most 256 NV entries are read once and kept in registers; NV = 0 reads p
 // and dp twice.
-template <int NV>
+// General alpha: dp_i/ds_j = w_i (delta_ij - w_j / sum w) with w = p^(2 - alpha)
+// on the support (differentiating p = [(alpha-1)(s - tau)]_+^(1/(alpha-1))
+// under sum p = 1); w = sqrt(p) for alpha = 1.5.
+template <int NV, bool GEN>
 __global__ __launch_bounds__(kThreads) void rows_bwd_kernel(RowsBwdArgs a) {
+    const float e = 2.f - a.alpha;
+    auto wt = [&](float p) { return GEN ? pow01(p, e) : __builtin_sqrtf(p); };
     const int lane = threadIdx.x % kWave;
     const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (row >= a.R) return;
@@ -232,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void rows_bwd_kernel(RowsBwdArgs a) {
         f32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            w[i] = j < L ? __builtin_sqrtf(p[i]) : 0.f;
+            w[i] = j < L ? wt(p[i]) : 0.f;
             sw += w[i];
             swd = fmaf(w[i], d[i], swd);
         }
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void rows_bwd_kernel(RowsBwdArgs a) {
             const f32x4 p = *reinterpret_cast<const f32x4*>(a.p + off + jj);
             d = *reinterpret_cast<const f32x4*>(a.dp + off + jj);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = __builtin_sqrtf(p[i]);
+            for (int i = 0; i < 4; ++i) w[i] = wt(p[i]);
         }
         f32x4 r;
 #pragma unroll

@@ -139,6 +139,21 @@ int entmax15_rows_fwd(const void *scores, const uint8_t *mask, float *p, float *
  */
 int entmax15_rows_bwd(const float *p, const float *dp, float *ds, int R, int L, void *stream);
 
+/*
+ * The same for a general alpha in (1, 2] (section 2.1 defines alpha-entmax
+ * through the Tsallis entropy; section 4 gives its bisection): p_j =
+ * [(alpha - 1)(s_j - tau)]_+^(1/(alpha - 1)) over the allowed entries with
+ * sum p = 1, tau in score units, 25 bisection steps on the bracket
+ * [max - 1/(alpha-1), max - n^(1-alpha)/(alpha-1)].  alpha = 2 is sparsemax;
+ * alpha = 1.5 gives the calls above (which are these with alpha = 1.5).
+ * Backward: ds_j = w_j (dp_j - sum_k w_k dp_k / sum_k w_k), w = p^(2 - alpha)
+ * on the support.  alpha outside (1, 2] returns ENTMAX_ERR_INVALID_ARG.
+ */
+int entmax_bisect_rows_fwd(const void *scores, const uint8_t *mask, float *p, float *tau,
+                           int R, int L, float alpha, int dtype, void *stream);
+int entmax_bisect_rows_bwd(const float *p, const float *dp, float *ds, int R, int L, float alpha,
+                           void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *entmax_attn_status_string(int status);
 

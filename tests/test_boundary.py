@@ -110,3 +110,16 @@ def test_binding_checks_grouped_shapes():
         _check_qkv(q, torch.zeros(1, 3, 8, 64))     # 3 does not divide 4
     with pytest.raises(ValueError):
         _check_qkv(q, torch.zeros(1, 2, 8, 64), torch.zeros(1, 4, 8, 64))   # v must match k
+
+
+def test_rows_reject_bad_arguments(lib):
+    # alpha outside (1, 2], null pointers, L not a multiple of 4
+    for a in (1.0, 0.9, 2.01, float("nan")):
+        assert lib.entmax_bisect_rows_fwd(P, None, P, None, 4, 8, a, 0, None) == 1
+        assert lib.entmax_bisect_rows_bwd(P, P, P, 4, 8, a, None) == 1
+    assert b"alpha" in lib.entmax_attn_last_error()
+    assert lib.entmax_bisect_rows_fwd(None, None, P, None, 4, 8, 1.5, 0, None) == 1
+    assert lib.entmax_bisect_rows_fwd(P, None, P, None, 4, 10, 1.5, 0, None) == 2
+    assert lib.entmax_bisect_rows_fwd(P, None, P, None, 4, 8, 1.5, 5, None) == 2
+    assert lib.entmax15_rows_fwd(P, None, P, None, 0, 8, 0, None) == 1
+    assert lib.entmax15_rows_bwd(P, None, P, 4, 8, None) == 1
