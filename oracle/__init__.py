@@ -34,6 +34,7 @@ from .entmax15 import (  # noqa: F401
     entmax15_bisect,
     attention_forward,
     attention_backward,
+    attention_decode,
     tsallis15_objective,
 )
 from .entmax_alpha import (  # noqa: F401

@@ -467,3 +467,42 @@ def test_exact_handles_tied_scores():
     _, tb = entmax15_bisect(s, n_iter=60)
     np.testing.assert_allclose(tau, tb, atol=1e-10)
     np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window,hkv", [(0, 4), (32, 4), (5, 2), (0, 1)])
+def test_decode_is_last_row_of_causal_forward(window, hkv):
+    # one new query against a cache = the last row of causal (windowed)
+    # attention over the cached prefix, computed through allowed_mask
+    from oracle import attention_decode, attention_forward
+    rng = np.random.default_rng(window + 10 * hkv)
+    B, H, S, d = 4, 4, 70, 16
+    q = rng.normal(size=(B, H, d))
+    kc = rng.normal(size=(B, hkv, S, d))
+    vc = rng.normal(size=(B, hkv, S, d))
+    seqlens = np.array([S, 1, 37, 0])
+    out, tau = attention_decode(q, kc, vc, seqlens, window)
+    assert np.all(out[3] == 0) and np.all(np.isinf(tau[3]))
+    for b in range(3):
+        n = seqlens[b]
+        qf = rng.normal(size=(1, H, n, d))
+        qf[0, :, n - 1] = q[b]
+        ref = attention_forward(qf, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], causal=True, window=window,
+                                rows=[n - 1])
+        np.testing.assert_allclose(out[b], ref["out"][:, 0], atol=1e-12)
+        np.testing.assert_allclose(tau[b], ref["tau"][:, 0], atol=1e-12)
+
+
+def test_decode_window_one_is_own_value():
+    # W = 1: only the query's own key; p = 1 there, so O = v_own and
+    # ((s - tau)/2)^2 = 1 gives tau = s - 2
+    from oracle import attention_decode
+    rng = np.random.default_rng(2)
+    q = rng.normal(size=(2, 3, 8))
+    kc = rng.normal(size=(2, 3, 10, 8))
+    vc = rng.normal(size=(2, 3, 10, 8))
+    out, tau = attention_decode(q, kc, vc, [10, 4], window=1)
+    for b, n in ((0, 10), (1, 4)):
+        for h in range(3):
+            np.testing.assert_allclose(out[b, h], vc[b, h, n - 1], atol=1e-14)
+            s = q[b, h] @ kc[b, h, n - 1] / np.sqrt(8)
+            assert abs(tau[b, h] - (s - 2.0)) < 1e-12
