@@ -219,13 +219,80 @@ def bench_rows(args):
     print(json.dumps(res))
 
 
+def bench_decode(args):
+    """Decode time: one new query per sequence against a key/value cache
+    (four launches per call), HBM-bound."""
+    import torch
+    from entmax_amd import decode_workspace_bytes, entmax_attn_decode
+    from entmax_amd.workloads import make_decode_inputs
+    inp = make_decode_inputs(args.workload)
+    w = inp["spec"]
+    B, H, Hkv, S, d, W = w["B"], w["H"], w["Hkv"], w["S"], w["d"], w["window"]
+    span = min(W, S) if W > 0 else S
+    esz = 2 if w["dtype"] == "bf16" else 4
+    # q, the span's K and V rows, O and tau, each moved once
+    alg_bytes = B * H * d * esz + 2 * B * Hkv * span * d * esz + B * H * (d + 1) * 4
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from threadpoolctl import threadpool_limits
+        from oracle import attention_decode
+        done, t0 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while time.perf_counter() - t0 < args.cpu_budget:
+                b = done % B
+                attention_decode(inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1],
+                                 inp["seqlens"][b:b + 1].numpy(), W)
+                done += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": done * alg_bytes / B / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} sequences of the {args.workload} workload (float64 numpy, one thread), {dt:.1f} s"}
+    dev = torch.device("cuda:0")
+    cache_bytes = 2 * B * Hkv * S * d * esz
+    nsets = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
+    ws_bytes = decode_workspace_bytes(B, H, S, d, W)
+    sets = [{"q": inp["q"].to(dev), "k": inp["k"].to(dev), "v": inp["v"].to(dev), "sl": inp["seqlens"].to(dev),
+             "ws": torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+             "out": torch.empty((B, H, d), device=dev), "tau": torch.empty((B, H), device=dev)}
+            for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(s):
+        entmax_attn_decode(s["q"], s["k"], s["v"], s["sl"], W, out=s["out"], tau=s["tau"], workspace=s["ws"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    bounds = [ev() for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    bounds[0].record()
+    for i in range(args.steps):
+        step(sets[i % nsets])
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    ms = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode-time 1.5-entmax attention: effective GB/s (HBM roofline)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": Hkv, "S": S, "d": d, "window": W,
+                   "buffer_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "decode (scores, tau, P V, reduce: four launches)",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": alg_bytes, "launch_ms": ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="encoder",
-                    choices=["tiny", "encoder", "long", "decoder", "longctx", "rows"])
+                    choices=["tiny", "encoder", "long", "decoder", "longctx", "rows", "decode", "decode_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -243,6 +310,9 @@ def main():
 
     if args.workload == "rows":
         bench_rows(args)
+        return
+    if args.workload in ("decode", "decode_long"):
+        bench_decode(args)
         return
 
     # The CPU baseline runs first, before anything touches the GPU.

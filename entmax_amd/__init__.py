@@ -10,7 +10,9 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     EntmaxError,
+    decode_workspace_bytes,
     entmax_attn_bwd,
+    entmax_attn_decode,
     entmax_attn_fwd,
     entmax_attn_probs,
     entmax15_rows,

@@ -1,0 +1,237 @@
+// Decode-time forward: one new query per sequence against a key/value cache
+// (the causal decoders of "ADASPLASH -- ROBERTA Benchmark Result", section 3,
+// with the splash window of the decoder configuration in section 7.1).
+//
+// Sequence b holds n_b cached positions; its query sits at n_b - 1 and may
+// attend keys [lo_b, n_b), lo_b = max(0, n_b - W) with a window W > 0, else
+// 0.  The span is split into chunks of 256 keys so that a long cache spreads
+// over many workgroups (a decode step has few query rows: the work is the
+// HBM read of K and V).  Four launches:
+//   1. dec_scores: per (chunk, b, key/value head, group of up to 16 query
+//      heads): S = q K^T / sqrt(d) on MFMA, written to a float32 row per
+//      query head, plus each row's maximum over the chunk.
+//   2. tau per row by the row-wise solver (rows.hpp) over the first n_b - lo_b
+//      entries of each score row.
+//   3. dec_pv: per chunk, skipped whole (no V read) when no row of the group
+//      has a score above its tau in the chunk; else the chunk's partial
+//      O = P V on float32 MFMA.
+//   4. dec_reduce: O = sum of the partials of the chunks that hold a score
+//      above tau (the same test as step 3), one wave per row.
+#pragma once
+
+#include "col_solve.hpp"
+#include "common.hpp"
+
+namespace ea {
+
+constexpr int kDecChunk = 256;   // keys per workgroup, 64 per wave
+
+struct DecArgs {
+    const void* q;        // [B, H, d]
+    const void* k;        // [B, Hkv, S, d]
+    const void* v;        // [B, Hkv, S, d]
+    const int* seqlens;   // [B]
+    float* out;           // [B, H, d]
+    float* tau_out;       // [B, H] or null
+    // workspace
+    float* sbuf;          // [B H, P] scores, P = nch * 256
+    float* cmax;          // [B H, nch] chunk maxima
+    float* part;          // [B H, nch, d] partial outputs
+    float* tau;           // [B H]
+    int* row_len;         // [B H] span length of each row
+    int B, H, Hkv, S, window;
+    int nch, P;           // chunks of the longest possible span; row pitch of sbuf
+    float scale;
+};
+
+// Keys [lo, n) of sequence b's cache that its query may attend.
+__device__ __forceinline__ void dec_span(const DecArgs& a, int b, int* lo, int* n) {
+    int len = a.seqlens[b];
+    len = len < 0 ? 0 : (len > a.S ? a.S : len);
+    *n = len;
+    *lo = (a.window > 0 && len > a.window) ? len - a.window : 0;
+}
+
+// Query heads [h0, h1) served by key/value head kvh in group z (16 per group).
+__device__ __forceinline__ void dec_heads(const DecArgs& a, int kvh, int z, int* h0, int* h1) {
+    const int G = a.H / a.Hkv;
+    *h0 = kvh * G + 16 * z;
+    const int e = kvh * G + G;
+    *h1 = *h0 + 16 < e ? *h0 + 16 : e;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void dec_scores_kernel(DecArgs a) {
+    using T = typename InT<DT>::type;
+    const int chunk = blockIdx.x, bk = blockIdx.y;
+    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+    int h0, h1, lo, n;
+    dec_heads(a, kvh, blockIdx.z, &h0, &h1);
+    dec_span(a, b, &lo, &n);
+    const int span = n - lo;
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
+    if (chunk == 0 && tid < h1 - h0) a.row_len[b * a.H + h0 + tid] = span;
+    if (kDecChunk * chunk >= span) return;   // uniform over the workgroup
+
+    // A operand: query heads h0 + c (zero rows past h1)
+    QFrag<DT, D> qf;
+    qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(b) * a.H * D, h0 + c, h1, g);
+    const T* kh = static_cast<const T*>(a.k) + static_cast<size_t>(bk) * a.S * D;
+
+    float mx[4] = {-kInf, -kInf, -kInf, -kInf};
+    const int r0 = kDecChunk * chunk + 64 * wv;   // first key of this wave, relative to lo
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = r0 + 16 * t + c;            // this lane's key (column c of the tile)
+        const bool ok = r < span;
+        // rows past the span read key n - 1 (valid: span > 0) and are masked
+        const f32x4 acc = qf.tile(kh, ok ? lo + r : n - 1, n, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = h0 + 4 * g + i;
+            const float s = ok ? acc[i] * a.scale : -kInf;
+            if (h < h1) a.sbuf[static_cast<size_t>(b * a.H + h) * a.P + r] = s;
+            mx[i] = fmaxf(mx[i], s);
+        }
+    }
+    __shared__ float red[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = group_max<16>(mx[i]);
+        if (c == 0) red[wv][4 * g + i] = m;
+    }
+    __syncthreads();
+    if (tid < h1 - h0) {
+        const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        a.cmax[static_cast<size_t>(b * a.H + h0 + tid) * a.nch + chunk] = m;
+    }
+}
+
+// Feature f of the output tile: lane c of feature tile ct serves feature
+// c (D/16) + ct, so that each lane reads D/16 consecutive features of a V row.
+template <int DT, int D> struct VRow;
+template <int D> struct VRow<DT_BF16, D> {
+    static constexpr int N = D / 16;
+    float f[N];
+    __device__ __forceinline__ void load(const uint16_t* row, int c) {
+        const uint16_t* p = row + N * c;
+        if constexpr (N == 8) {
+            const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = __uint_as_float(u[e] << 16);
+                f[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+            }
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            f[0] = __uint_as_float(u.x << 16);
+            f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+            f[2] = __uint_as_float(u.y << 16);
+            f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+        }
+    }
+};
+template <int D> struct VRow<DT_F32, D> {
+    static constexpr int N = D / 16;
+    float f[N];
+    __device__ __forceinline__ void load(const float* row, int c) {
+        const float* p = row + N * c;
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(p + e);
+            f[e] = u[0]; f[e + 1] = u[1]; f[e + 2] = u[2]; f[e + 3] = u[3];
+        }
+    }
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
+    using T = typename InT<DT>::type;
+    constexpr int NF = D / 16;
+    const int chunk = blockIdx.x, bk = blockIdx.y;
+    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+    int h0, h1, lo, n;
+    dec_heads(a, kvh, blockIdx.z, &h0, &h1);
+    dec_span(a, b, &lo, &n);
+    const int span = n - lo;
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
+    if (kDecChunk * chunk >= span) return;   // uniform
+    // skip the chunk when every row's scores in it lie at or below its tau
+    bool act = false;
+    if (tid < h1 - h0) {
+        const int row = b * a.H + h0 + tid;
+        act = a.cmax[static_cast<size_t>(row) * a.nch + chunk] > a.tau[row];
+    }
+    if (!__syncthreads_or(act)) return;
+
+    // lane (g, c): A[c][g] = p of query head h0 + c at key r0 + 16 g + s
+    // (step s); B[g][c] = V at that key, features c NF .. c NF + NF - 1
+    const int r0 = kDecChunk * chunk + 64 * wv;
+    const int hq = h0 + c;
+    float p[16];
+    {
+        const bool rok = hq < h1;
+        const int row = b * a.H + (rok ? hq : h0);
+        const float tq = a.tau[row];
+        const float* sp = a.sbuf + static_cast<size_t>(row) * a.P + r0 + 16 * g;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(sp + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y = relu1(0.5f * (s4[i] - tq));
+                p[e + i] = rok ? y * y : 0.f;   // keys past the span hold -inf: p = 0
+            }
+        }
+    }
+    const T* vh = static_cast<const T*>(a.v) + static_cast<size_t>(bk) * a.S * D;
+    f32x4 o[NF];
+#pragma unroll
+    for (int ct = 0; ct < NF; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int r = r0 + 16 * g + s;
+        VRow<DT, D> vr;
+        vr.load(vh + static_cast<size_t>(r < span ? lo + r : n - 1) * D, c);   // past the span: p = 0
+#pragma unroll
+        for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(p[s], vr.f[ct], o[ct]);
+    }
+    // lane (g, c) holds O[query 4 g + i][feature c NF + ct]; sum the four waves
+    __shared__ float red[4][16][D];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NF; ++ct) red[wv][4 * g + i][c * NF + ct] = o[ct][i];
+    __syncthreads();
+    const int ng = h1 - h0;
+    for (int e = tid; e < ng * D; e += kThreads) {
+        const int qh = e / D, f = e - qh * D;
+        const float sum = (red[0][qh][f] + red[1][qh][f]) + (red[2][qh][f] + red[3][qh][f]);
+        a.part[(static_cast<size_t>(b * a.H + h0 + qh) * a.nch + chunk) * D + f] = sum;
+    }
+}
+
+// One wave per row: O = sum over the chunks holding a score above tau.
+template <int D>
+__global__ __launch_bounds__(kThreads) void dec_reduce_kernel(DecArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (row >= a.B * a.H) return;
+    const int span = a.row_len[row];
+    const float t = a.tau[row];
+    const int nc = (span + kDecChunk - 1) / kDecChunk;
+    float acc[D / 64];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+    for (int ch = 0; ch < nc; ++ch) {
+        if (!(a.cmax[static_cast<size_t>(row) * a.nch + ch] > t)) continue;   // uniform
+        const float* pp = a.part + (static_cast<size_t>(row) * a.nch + ch) * D;
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) acc[e] += pp[64 * e + lane];
+    }
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) a.out[static_cast<size_t>(row) * D + 64 * e + lane] = acc[e];
+    if (a.tau_out != nullptr && lane == 0) a.tau_out[row] = t;
+}
+
+}  // namespace ea

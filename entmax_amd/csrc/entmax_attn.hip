@@ -14,6 +14,7 @@
 #include "probs.hpp"
 #include "rows.hpp"
 #include "bwd.hpp"
+#include "decode.hpp"
 
 namespace {
 
@@ -150,7 +151,19 @@ int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
 
 template <int DT, bool GEN>
 void launch_rows_fwd_g(const ea::RowsArgs& a, hipStream_t st) {
-    const dim3 grid((a.R + 3) / 4), block(ea::kThreads);
+    const dim3 block(ea::kThreads);
+    if (a.R < 1024 && a.L > 1024) {
+        // few long rows (fewer than one wave per SIMD): a workgroup per row
+        constexpr int T = ea::kThreads;
+        const dim3 grid(a.R);
+        if (a.L <= 2048) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 2, GEN, T>), grid, block, 0, st, a);
+        else if (a.L <= 4096) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 4, GEN, T>), grid, block, 0, st, a);
+        else if (a.L <= 8192) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 8, GEN, T>), grid, block, 0, st, a);
+        else if (a.L <= 16384) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 16, GEN, T>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 0, GEN, T>), grid, block, 0, st, a);
+        return;
+    }
+    const dim3 grid((a.R + 3) / 4);
     if (a.L <= 256) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 1, GEN>), grid, block, 0, st, a);
     else if (a.L <= 512) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 2, GEN>), grid, block, 0, st, a);
     else if (a.L <= 1024) hipLaunchKernelGGL((ea::rows_fwd_kernel<DT, 4, GEN>), grid, block, 0, st, a);
@@ -178,6 +191,54 @@ void launch_rows_bwd_g(const ea::RowsBwdArgs& a, hipStream_t st) {
 void launch_rows_bwd(const ea::RowsBwdArgs& a, hipStream_t st) {
     if (a.alpha == 1.5f) launch_rows_bwd_g<false>(a, st);
     else launch_rows_bwd_g<true>(a, st);
+}
+
+// Workspace of the decode path: byte offsets of its arrays (each 256-byte
+// aligned) for the longest span the arguments allow.
+struct DecLayout {
+    int nch, P;
+    size_t sbuf, cmax, part, tau, rlen, total;
+};
+
+DecLayout dec_layout(int B, int H, int S, int d, int window) {
+    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    DecLayout l;
+    const int span = (window > 0 && window < S) ? window : S;
+    l.nch = (span + ea::kDecChunk - 1) / ea::kDecChunk;
+    l.P = l.nch * ea::kDecChunk;
+    const size_t rows = static_cast<size_t>(B) * H;
+    l.sbuf = 0;
+    l.cmax = l.sbuf + al(rows * l.P * sizeof(float));
+    l.part = l.cmax + al(rows * l.nch * sizeof(float));
+    l.tau = l.part + al(rows * l.nch * d * sizeof(float));
+    l.rlen = l.tau + al(rows * sizeof(float));
+    l.total = l.rlen + al(rows * sizeof(int));
+    return l;
+}
+
+int check_decode(int B, int H, int Hkv, int S, int d, int dtype, int window) {
+    if (B <= 0 || H <= 0 || S <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, S must be positive (got %d, %d, %d)", B, H, S);
+    if (Hkv <= 0 || H % Hkv != 0) return fail(ENTMAX_ERR_INVALID_ARG, "H_kv = %d must divide H = %d", Hkv, H);
+    if (window < 0) return fail(ENTMAX_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+    if (d != 64 && d != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
+    if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (S > (1 << 24)) return fail(ENTMAX_ERR_UNSUPPORTED, "S = %d exceeds 2^24", S);
+    if (static_cast<long long>(B) * Hkv > 65535) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H_kv exceeds 65535");
+    if (static_cast<long long>(B) * H * (S + 255) > (1LL << 36)) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H * S too large");
+    return ENTMAX_OK;
+}
+
+template <int DT, int D>
+void launch_decode(const ea::DecArgs& a, hipStream_t st) {
+    const int G = a.H / a.Hkv;
+    const dim3 grid(a.nch, a.B * a.Hkv, (G + 15) / 16), block(ea::kThreads);
+    hipLaunchKernelGGL((ea::dec_scores_kernel<DT, D>), grid, block, 0, st, a);
+    ea::RowsArgs r;
+    r.s = a.sbuf; r.mask = nullptr; r.p = nullptr; r.tau = a.tau; r.R = a.B * a.H; r.L = a.P; r.alpha = 1.5f;
+    r.row_len = a.row_len;
+    launch_rows_fwd<ea::DT_F32>(r, st);
+    hipLaunchKernelGGL((ea::dec_pv_kernel<DT, D>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((ea::dec_reduce_kernel<D>), dim3((a.B * a.H + 3) / 4), block, 0, st, a);
 }
 
 int check_rows(int R, int L) {
@@ -300,6 +361,43 @@ int entmax15_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* 
 
 int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, void* stream) {
     return entmax_bisect_rows_bwd(p, dp, ds, R, L, 1.5f, stream);
+}
+
+size_t entmax_attn_decode_workspace_size(int B, int H, int S, int d, int window) {
+    if (B <= 0 || H <= 0 || S <= 0 || d <= 0 || window < 0) return 0;
+    return dec_layout(B, H, S, d, window).total;
+}
+
+int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, int window,
+                       float* out, float* tau_out, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                       int S, int d, int dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens, out and workspace must not be NULL");
+    int rc = check_decode(B, H, Hkv, S, d, dtype, window);
+    if (rc) return rc;
+    const DecLayout l = dec_layout(B, H, S, d, window);
+    if (workspace_bytes < l.total)
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    ea::DecArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens; a.out = out; a.tau_out = tau_out;
+    a.sbuf = reinterpret_cast<float*>(ws + l.sbuf);
+    a.cmax = reinterpret_cast<float*>(ws + l.cmax);
+    a.part = reinterpret_cast<float*>(ws + l.part);
+    a.tau = reinterpret_cast<float*>(ws + l.tau);
+    a.row_len = reinterpret_cast<int*>(ws + l.rlen);
+    a.B = B; a.H = H; a.Hkv = Hkv; a.S = S; a.window = window; a.nch = l.nch; a.P = l.P;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16) {
+        if (d == 64) launch_decode<ea::DT_BF16, 64>(a, st);
+        else launch_decode<ea::DT_BF16, 128>(a, st);
+    } else {
+        if (d == 64) launch_decode<ea::DT_F32, 64>(a, st);
+        else launch_decode<ea::DT_F32, 128>(a, st);
+    }
+    return check_launch("decode");
 }
 
 const char* entmax_attn_status_string(int status) {

@@ -9,10 +9,11 @@
 // SST-2 with AdaSplash Attention" model card, Mathematical Formulation 2),
 // run in the half-scaled shifted domain x = (s - max)/2 where the bracket is
 // [-1, -1/sqrt(n)].  Other alphas use the same steps with the powers below.
-// One wave per row; lane l holds entries 256 c + 4 l .. + 3 of chunk c, so
-// every load and store is one contiguous 1 KB (fp32) block per wave.  Rows of
-// at most 256 NV entries stay in registers for all 25 steps; longer rows are
-// re-read for every step (the pages' algorithm as printed; HBM-bound).
+// One wave per row (a workgroup per row when there are few long rows); lane
+// l holds entries 256 c + 4 l .. + 3 of chunk c (1024 c + 4 l with a
+// workgroup), so every load and store is one contiguous block per wave.
+// Rows of at most 16 chunks stay in registers for all 25 steps; longer rows
+// are re-read for every step (the pages' algorithm as printed; HBM-bound).
 //
 // Backward (section 2.4 Jacobian): with w = sqrt(p) at alpha = 1.5,
 // ds_j = w_j (dp_j - sum_k w_k dp_k / sum_k w_k).
@@ -27,10 +28,13 @@ namespace ea {
 struct RowsArgs {
     const void* s;            // [R, L] scores (fp32 or bf16)
     const uint8_t* mask;      // [R, L], nonzero = allowed; or null
-    float* p;                 // [R, L]
+    float* p;                 // [R, L] or null (tau only)
     float* tau;               // [R] (score units) or null
-    int R, L;
+    int R, L;                 // rows; row pitch (elements, a multiple of 4)
     float alpha;              // in (1, 2]; 1.5 unless GEN
+    // [R] or null: row r takes part in the row only in its first
+    // min(row_len[r], L) entries (the rest count as not allowed)
+    const int* row_len = nullptr;
 };
 
 // General alpha ("ADASPLASH -- ROBERTA Benchmark Result", section 2.1, and
@@ -61,39 +65,68 @@ __device__ __forceinline__ f32x4 load4(const void* s, size_t row_off, int j, int
     }
 }
 
-__device__ __forceinline__ unsigned valid4(const uint8_t* mask, size_t row_off, int j, int L) {
+// Allowed bits of entries j .. j + 3 (j % 4 == 0): below the row's length
+// n and, with a mask, nonzero there (the mask has the row pitch, so whole
+// quads below n are in bounds)
+__device__ __forceinline__ unsigned valid4(const uint8_t* mask, size_t row_off, int j, int n) {
     unsigned v = 0u;
-    if (j < L) {
+    if (j < n) {
         const unsigned mb = mask ? *reinterpret_cast<const unsigned*>(mask + row_off + j) : 0x01010101u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v |= ((mb >> (8 * i)) & 0xFFu) != 0u ? (1u << i) : 0u;
+        for (int i = 0; i < 4; ++i) v |= (((mb >> (8 * i)) & 0xFFu) != 0u && j + i < n) ? (1u << i) : 0u;
     }
     return v;
 }
 
-// NV chunks of 256 entries per row in registers (L <= 256 NV); NV = 0: any
-// L, streamed from memory at every step.
-template <int DT, int NV, bool GEN>
+// TPR threads per row: a wave (many rows), or the whole workgroup (few long
+// rows, as at decode time: sums then go through LDS, one barrier each).
+// NV chunks of 4 TPR entries per row in registers (L <= 4 TPR NV); NV = 0:
+// any L, streamed from memory at every step.
+template <int DT, int NV, bool GEN, int TPR = kWave>
 __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
+    static_assert(TPR == kWave || TPR == kThreads, "a wave or a workgroup per row");
+    constexpr int CH = 4 * TPR;   // entries per chunk
     const float am1 = GEN ? a.alpha - 1.f : 0.5f;        // alpha - 1
     const float beta = GEN ? 1.f / (a.alpha - 1.f) : 2.f;   // 1 / (alpha - 1)
     // [y]^beta: a square for alpha = 1.5
     auto pw = [&](float y) { return GEN ? pow01(y, beta) : y * y; };
-    const int lane = threadIdx.x % kWave;
-    const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (row >= a.R) return;   // uniform per wave; no barrier below
+    const int lane = threadIdx.x % TPR;   // position within the row's threads
+    const int row = TPR == kWave ? blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave)
+                                 : static_cast<int>(blockIdx.x);
+    if (row >= a.R) return;   // uniform over the row's threads
     const int L = a.L;
+    const int Lr = a.row_len != nullptr ? min(max(a.row_len[row], 0), L) : L;   // entries of this row
     const size_t off = static_cast<size_t>(row) * L;
-    const int nch = NV > 0 ? NV : (L + 255) / 256;
+    const int nch = NV > 0 ? NV : (Lr + CH - 1) / CH;   // chunks the solve reads
+    // reductions over the row's threads, bitwise identical in all of them
+    __shared__ float xch[2][kThreads / kWave];
+    int par = 0;
+    auto across = [&](float w, bool is_max) {
+        if (threadIdx.x % kWave == 0) xch[par][threadIdx.x / kWave] = w;
+        __syncthreads();
+        const float* s = xch[par];
+        par ^= 1;   // the next reduction writes the other slot set
+        return is_max ? fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) : (s[0] + s[1]) + (s[2] + s[3]);
+    };
+    auto rsum = [&](float v) {
+        const float w = wave_sum(v);
+        if constexpr (TPR == kWave) return w;
+        else return across(w, false);
+    };
+    auto rmax = [&](float v) {
+        const float w = wave_max(v);
+        if constexpr (TPR == kWave) return w;
+        else return across(w, true);
+    };
 
     // pass 1: row max and allowed count
     float mraw = -kInf, cnt = 0.f;
     f32x4 xs[NV > 0 ? NV : 1];
     unsigned vb[NV > 0 ? NV : 1];
     for (int c = 0; c < nch; ++c) {
-        const int j = 256 * c + 4 * lane;
+        const int j = CH * c + 4 * lane;
         const f32x4 v = load4<DT>(a.s, off, j, L);
-        const unsigned ok = valid4(a.mask, off, j, L);
+        const unsigned ok = valid4(a.mask, off, j, Lr);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool on = (ok >> i) & 1u;
@@ -106,13 +139,14 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
                 if (q == c) { xs[q] = v; vb[q] = ok; }
         }
     }
-    const float m = wave_max(mraw);
-    const float n = wave_sum(cnt);
+    const float m = rmax(mraw);
+    const float n = rsum(cnt);
+    const int ncw = NV > 0 ? NV : (L + CH - 1) / CH;    // chunks of p written
     if (n == 0.f) {
         // no allowed entry: p = 0, tau = +inf
-        for (int c = 0; c < nch; ++c) {
-            const int j = 256 * c + 4 * lane;
-            if (j < L) *reinterpret_cast<f32x4*>(a.p + off + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < ncw; ++c) {
+            const int j = CH * c + 4 * lane;
+            if (a.p != nullptr && j < L) *reinterpret_cast<f32x4*>(a.p + off + j) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (a.tau != nullptr && lane == 0) a.tau[row] = kInf;
         return;
@@ -137,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
     float lo = -1.f, hi = GEN ? -__builtin_amdgcn_exp2f(-am1 * __builtin_amdgcn_logf(n)) : -__builtin_amdgcn_rsqf(n);
     auto step = [&](auto&& partial) {
         const float mid = 0.5f * (lo + hi);
-        if (wave_sum(partial(mid)) > 1.f) lo = mid;
+        if (rsum(partial(mid)) > 1.f) lo = mid;
         else hi = mid;
     };
     auto full = [&](float mid) {
@@ -151,8 +185,8 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
                 }
         } else {
             for (int c = 0; c < nch; ++c) {
-                const int j = 256 * c + 4 * lane;
-                const f32x4 x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, L));
+                const int j = CH * c + 4 * lane;
+                const f32x4 x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, Lr));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     acc += pw(relu1(x[i] - mid));
@@ -179,7 +213,8 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
                 for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
                 nc += cand ? 1 : 0;
             }
-        few = !__any(nc > kCand);
+        if constexpr (TPR == kWave) few = !__any(nc > kCand);
+        else few = !__syncthreads_or(nc > kCand);
     }
     if (few) {
         for (; it < kIters; ++it)
@@ -196,15 +231,16 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
     }
     const float t = 0.5f * (lo + hi);
     if (a.tau != nullptr && lane == 0) a.tau[row] = m + t * beta;   // score units: p = [(alpha-1)(s - tau)]_+^beta
-    for (int c = 0; c < nch; ++c) {
-        const int j = 256 * c + 4 * lane;
+    if (a.p == nullptr) return;
+    for (int c = 0; c < ncw; ++c) {
+        const int j = CH * c + 4 * lane;
         f32x4 x;
         if constexpr (NV > 0) {
 #pragma unroll
             for (int q = 0; q < NV; ++q)
                 if (q == c) x = xs[q];
         } else {
-            x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, L));
+            x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, Lr));
         }
         f32x4 p;
 #pragma unroll

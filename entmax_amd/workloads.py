@@ -23,6 +23,14 @@ settings; no dataset is used):
 * ``longctx``   B1 H32 L8192 d128 bf16, Q and K times 2, V and dO N(0,1);
   forward and backward.
 
+Decode time (``make_decode_inputs``): one new query per sequence against a
+full key/value cache, q [B, H, d], caches [B, H, S, d], seqlens = S:
+
+* ``decode``       the decoder workload's shape (B8 H12 S2048 d64 bf16,
+  N(0,1)) with its 32-key window; seed 1007.
+* ``decode_long``  the long-context shape (B1 H32 S8192 d128 bf16, q and k
+  times 2) without a window, every cached key allowed; seed 1008.
+
 Row-wise op (``make_row_inputs``): ``rows`` is a [98304, 1024] bf16 score
 matrix (the rows of the long workload's 8 x 12 heads) drawn N(0,1), with a
 float32 N(0,1) gradient for the backward; seed 1006.
@@ -140,3 +148,25 @@ def make_row_inputs(name="rows", device="cpu"):
     dp = torch.randn((w["R"], w["L"]), generator=gen)
     return {"scores": s.to(_DTYPES[w["dtype"]]).contiguous().to(device), "dp": dp.to(device), "spec": w}
 
+
+
+DECODE = {
+    "decode": {"B": 8, "H": 12, "Hkv": 12, "S": 2048, "d": 64, "dtype": "bf16", "window": 32,
+               "qk_gain": 1.0, "number": 7},
+    "decode_long": {"B": 1, "H": 32, "Hkv": 32, "S": 8192, "d": 128, "dtype": "bf16", "window": 0,
+                    "qk_gain": 2.0, "number": 8},
+}
+
+
+def make_decode_inputs(name, device="cpu"):
+    """q [B, H, d], k_cache, v_cache [B, H_kv, S, d] (workload dtype) and
+    seqlens [B] int32 (every cache full)."""
+    w = DECODE[name]
+    gen = torch.Generator().manual_seed(1000 + w["number"])
+    q = torch.randn((w["B"], w["H"], w["d"]), generator=gen) * w["qk_gain"]
+    k = torch.randn((w["B"], w["Hkv"], w["S"], w["d"]), generator=gen) * w["qk_gain"]
+    v = torch.randn((w["B"], w["Hkv"], w["S"], w["d"]), generator=gen)
+    dt = _DTYPES[w["dtype"]]
+    seqlens = torch.full((w["B"],), w["S"], dtype=torch.int32)
+    return {"q": q.to(dt).to(device), "k": k.to(dt).to(device), "v": v.to(dt).to(device),
+            "seqlens": seqlens.to(device), "spec": w}

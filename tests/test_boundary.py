@@ -123,3 +123,23 @@ def test_rows_reject_bad_arguments(lib):
     assert lib.entmax_bisect_rows_fwd(P, None, P, None, 4, 8, 1.5, 5, None) == 2
     assert lib.entmax15_rows_fwd(P, None, P, None, 0, 8, 0, None) == 1
     assert lib.entmax15_rows_bwd(P, None, P, 4, 8, None) == 1
+
+
+def test_decode_rejects_bad_arguments(lib):
+    ws = lib.entmax_attn_decode_workspace_size(2, 4, 64, 64, 0)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.entmax_attn_decode_workspace_size(0, 4, 64, 64, 0) == 0
+    W = ctypes.c_void_p(256)
+    ok = [P, P, P, P, 0, P, None, W, ws, 2, 4, 4, 64, 64, 1, None]
+    for i in (0, 1, 2, 3, 5, 7):
+        a = list(ok)
+        a[i] = None
+        assert lib.entmax_attn_decode(*a) == 1
+    bad = {8: ws - 1, 11: 3, 4: -1, 13: 96, 14: 7}
+    for i, val in bad.items():
+        a = list(ok)
+        a[i] = val
+        assert lib.entmax_attn_decode(*a) == (2 if i in (13, 14) else 1), i
+    a = list(ok)
+    a[7] = ctypes.c_void_p(272)      # not 256-byte aligned
+    assert lib.entmax_attn_decode(*a) == 1

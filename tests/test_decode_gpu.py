@@ -1,0 +1,97 @@
+"""GPU parity of decode-time attention (entmax_attn_decode through the C ABI)
+against the float64 oracle ``attention_decode``: absolute error <= 1e-5
+(float32 inputs) or 2e-3 (bfloat16 inputs) on O and tau, tau = +inf exactly
+for empty caches."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_decode
+from tests.parity_util import TOL, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _inputs(B, H, Hkv, S, d, dtype, gain, seed, seqlens):
+    gen = torch.Generator().manual_seed(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = (torch.randn((B, H, d), generator=gen) * gain).to(dt)
+    k = torch.randn((B, Hkv, S, d), generator=gen).to(dt)
+    v = torch.randn((B, Hkv, S, d), generator=gen).to(dt)
+    return q, k, v, torch.tensor(seqlens, dtype=torch.int32)
+
+
+def _check(q, k, v, sl, window, dtype, out, tau):
+    ref_o, ref_t = attention_decode(q, k, v, sl.numpy(), window)
+    o, t = out.cpu().numpy(), tau.cpu().numpy()
+    assert np.array_equal(np.isinf(t), np.isinf(ref_t))
+    fin = np.isfinite(ref_t)
+    err_o = float(np.abs(o - ref_o).max())
+    err_t = float(np.abs(t[fin] - ref_t[fin]).max()) if fin.any() else 0.0
+    log(f"[decode]   max err O={err_o:.3g} tau={err_t:.3g}")
+    assert err_o <= TOL[dtype] and err_t <= TOL[dtype]
+
+
+CASES = [
+    # (dtype, d, H, Hkv, S, window, gain)
+    ("f32", 64, 4, 4, 40, 0, 1.0),
+    ("f32", 64, 4, 4, 40, 32, 1.0),
+    ("f32", 128, 8, 2, 300, 0, 2.0),
+    ("f32", 64, 20, 1, 1100, 0, 1.0),
+    ("f32", 128, 4, 4, 1100, 32, 2.0),
+    ("bf16", 64, 4, 4, 40, 32, 1.0),
+    ("bf16", 64, 12, 12, 300, 0, 1.0),
+    ("bf16", 128, 8, 2, 1100, 0, 2.0),
+    ("bf16", 64, 20, 1, 600, 32, 1.0),
+    ("bf16", 128, 32, 8, 2100, 0, 2.0),
+    ("bf16", 64, 6, 3, 513, 300, 1.0),
+]
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv,S,window,gain", CASES)
+def test_decode_matches_oracle(dtype, d, H, Hkv, S, window, gain):
+    from entmax_amd import entmax_attn_decode
+    rng = np.random.default_rng(S + d + H)
+    seqlens = [S, 1, int(rng.integers(2, S)), 0, min(S, 33)]
+    q, k, v, sl = _inputs(5, H, Hkv, S, d, dtype, gain, seed=S * 7 + H, seqlens=seqlens)
+    log(f"[decode] {dtype} d{d} H{H} Hkv{Hkv} S{S} W{window} seqlens {seqlens}")
+    out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), window)
+    torch.cuda.synchronize()
+    _check(q, k, v, sl, window, dtype, out, tau)
+
+
+def test_decode_long_cache():
+    # the long-context shape at decode time: 8192 cached keys, grouped queries
+    from entmax_amd import entmax_attn_decode
+    q, k, v, sl = _inputs(2, 32, 8, 8192, 128, "bf16", 2.0, seed=5, seqlens=[8192, 5000])
+    log("[decode] bf16 d128 H32 Hkv8 S8192 W0")
+    out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0)
+    torch.cuda.synchronize()
+    _check(q, k, v, sl, 0, "bf16", out, tau)
+
+
+def test_decode_reuses_workspace():
+    # a second, smaller call on the same workspace sees nothing of the first
+    from entmax_amd import decode_workspace_bytes, entmax_attn_decode
+    ws = torch.empty((decode_workspace_bytes(3, 8, 900, 64, 0),), dtype=torch.uint8, device="cuda")
+    for S, seqlens in ((900, [900, 700, 3]), (500, [10, 499, 0])):
+        q, k, v, sl = _inputs(3, 8, 4, S, 64, "bf16", 1.0, seed=S, seqlens=seqlens)
+        log(f"[decode] workspace reuse S{S} seqlens {seqlens}")
+        out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, workspace=ws)
+        torch.cuda.synchronize()
+        _check(q, k, v, sl, 0, "bf16", out, tau)
+
+
+def test_decode_rejects_small_workspace():
+    from entmax_amd import EntmaxError, decode_workspace_bytes, entmax_attn_decode
+    q, k, v, sl = _inputs(2, 4, 4, 64, 64, "f32", 1.0, seed=1, seqlens=[64, 10])
+    ws = torch.empty((decode_workspace_bytes(2, 4, 64, 64, 0) - 256,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(EntmaxError):
+        entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, workspace=ws)
