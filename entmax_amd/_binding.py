@@ -79,7 +79,7 @@ def load_library(path=LIB_PATH):
     lib.entmax_bisect_rows_bwd.argtypes = [fp, fp, fp, i32, i32, f32, vp]
     lib.entmax_bisect_rows_bwd.restype = i32
     sz = ctypes.c_size_t
-    lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.entmax_attn_decode_workspace_size.restype = sz
     lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_decode.restype = i32
@@ -198,9 +198,9 @@ def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=No
     return probs
 
 
-def decode_workspace_bytes(B, H, S, d, window=0):
+def decode_workspace_bytes(B, H, H_kv, S, d, window=0):
     """Bytes of device workspace ``entmax_attn_decode`` needs."""
-    return int(load_library().entmax_attn_decode_workspace_size(B, H, S, d, int(window)))
+    return int(load_library().entmax_attn_decode_workspace_size(B, H, H_kv, S, d, int(window)))
 
 
 def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=None, workspace=None,
@@ -227,7 +227,7 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
     if seqlens.shape != (B,) or seqlens.dtype != torch.int32 or seqlens.device != q.device:
         raise ValueError("seqlens must be a [B] int32 tensor on q's device")
     hkv, S = k_cache.shape[1], k_cache.shape[2]
-    need = decode_workspace_bytes(B, H, S, d, window)
+    need = decode_workspace_bytes(B, H, hkv, S, d, window)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
     if out is None:

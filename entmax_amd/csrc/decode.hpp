@@ -211,26 +211,48 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
     }
 }
 
-// One wave per row: O = sum over the chunks holding a score above tau.
+// One wave per row: O = sum over the chunks holding a score above tau, in
+// chunk order.  Lane l tests chunk c0 + l; the partials of the active chunks
+// are then loaded four at a time, so that their loads are in flight together.
 template <int D>
 __global__ __launch_bounds__(kThreads) void dec_reduce_kernel(DecArgs a) {
+    constexpr int E = D / 64;
     const int lane = threadIdx.x % kWave;
     const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (row >= a.B * a.H) return;
     const int span = a.row_len[row];
     const float t = a.tau[row];
     const int nc = (span + kDecChunk - 1) / kDecChunk;
-    float acc[D / 64];
+    const float* pr = a.part + static_cast<size_t>(row) * a.nch * D;
+    float acc[E];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-    for (int ch = 0; ch < nc; ++ch) {
-        if (!(a.cmax[static_cast<size_t>(row) * a.nch + ch] > t)) continue;   // uniform
-        const float* pp = a.part + (static_cast<size_t>(row) * a.nch + ch) * D;
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += kWave) {
+        const int ch = c0 + lane;
+        const bool act = ch < nc && a.cmax[static_cast<size_t>(row) * a.nch + ch] > t;
+        unsigned long long m = __ballot(act);
+        while (m != 0ull) {
+            int idx[4];
+            bool ok[4];
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) acc[e] += pp[64 * e + lane];
+            for (int u = 0; u < 4; ++u) {
+                ok[u] = m != 0ull;
+                idx[u] = ok[u] ? c0 + __builtin_ctzll(m) : c0;
+                m = ok[u] ? m & (m - 1ull) : m;
+            }
+            float v[4][E];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[u][e] = pr[static_cast<size_t>(idx[u]) * D + 64 * e + lane];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] += ok[u] ? v[u][e] : 0.f;   // unused slots: discarded
+        }
     }
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) a.out[static_cast<size_t>(row) * D + 64 * e + lane] = acc[e];
+    for (int e = 0; e < E; ++e) a.out[static_cast<size_t>(row) * D + 64 * e + lane] = acc[e];
     if (a.tau_out != nullptr && lane == 0) a.tau_out[row] = t;
 }
 

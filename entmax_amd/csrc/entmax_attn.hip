@@ -200,7 +200,7 @@ struct DecLayout {
     size_t sbuf, cmax, part, tau, rlen, total;
 };
 
-DecLayout dec_layout(int B, int H, int S, int d, int window) {
+DecLayout dec_layout(int B, int H, int S, int d, int window) {  // any H_kv
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     DecLayout l;
     const int span = (window > 0 && window < S) ? window : S;
@@ -363,8 +363,8 @@ int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, 
     return entmax_bisect_rows_bwd(p, dp, ds, R, L, 1.5f, stream);
 }
 
-size_t entmax_attn_decode_workspace_size(int B, int H, int S, int d, int window) {
-    if (B <= 0 || H <= 0 || S <= 0 || d <= 0 || window < 0) return 0;
+size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int S, int d, int window) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || S <= 0 || d <= 0 || window < 0) return 0;
     return dec_layout(B, H, S, d, window).total;
 }
 

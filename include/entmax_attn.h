@@ -171,16 +171,17 @@ int entmax_bisect_rows_bwd(const float *p, const float *dp, float *ds, int R, in
  *  - out: [B, H, d] float32; tau_out: [B, H] float32 (score units) or NULL.
  *    A sequence with n_b = 0 gets O = 0 and tau = +inf.
  *  - workspace: caller-owned DEVICE memory, 256-byte aligned, of at least
- *    entmax_attn_decode_workspace_size(B, H, S, d, window) bytes (scores of
- *    the span, per-chunk maxima and partial outputs); its contents need no
- *    initialisation and are scratch after the call.  Two calls in flight
- *    must not share a workspace.
+ *    entmax_attn_decode_workspace_size(B, H, H_kv, S, d, window) bytes
+ *    (scores of the span, per-chunk maxima, partial outputs and completion
+ *    counters); its contents need no initialisation and are scratch after
+ *    the call.  Two calls in flight must not share a workspace.
  *  - Supported: d in {64, 128}; dtype ENTMAX_F32 or ENTMAX_BF16;
  *    S <= 2^24; B * H_kv <= 65535.  A too small or misaligned workspace
  *    returns ENTMAX_ERR_INVALID_ARG.
- * entmax_attn_decode_workspace_size returns 0 for non-positive sizes.
+ * entmax_attn_decode_workspace_size returns 0 for non-positive sizes or an
+ * H_kv that does not divide H.
  */
-size_t entmax_attn_decode_workspace_size(int B, int H, int S, int d, int window);
+size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int S, int d, int window);
 int entmax_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
                        int window, float *out, float *tau_out, void *workspace, size_t workspace_bytes,
                        int B, int H, int H_kv, int S, int d, int dtype, void *stream);

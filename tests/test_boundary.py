@@ -126,9 +126,10 @@ def test_rows_reject_bad_arguments(lib):
 
 
 def test_decode_rejects_bad_arguments(lib):
-    ws = lib.entmax_attn_decode_workspace_size(2, 4, 64, 64, 0)
+    ws = lib.entmax_attn_decode_workspace_size(2, 4, 4, 64, 64, 0)
     assert ws > 0 and ws % 256 == 0
-    assert lib.entmax_attn_decode_workspace_size(0, 4, 64, 64, 0) == 0
+    assert lib.entmax_attn_decode_workspace_size(0, 4, 4, 64, 64, 0) == 0
+    assert lib.entmax_attn_decode_workspace_size(2, 4, 3, 64, 64, 0) == 0
     W = ctypes.c_void_p(256)
     ok = [P, P, P, P, 0, P, None, W, ws, 2, 4, 4, 64, 64, 1, None]
     for i in (0, 1, 2, 3, 5, 7):

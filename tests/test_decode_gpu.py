@@ -80,7 +80,7 @@ def test_decode_long_cache():
 def test_decode_reuses_workspace():
     # a second, smaller call on the same workspace sees nothing of the first
     from entmax_amd import decode_workspace_bytes, entmax_attn_decode
-    ws = torch.empty((decode_workspace_bytes(3, 8, 900, 64, 0),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((decode_workspace_bytes(3, 8, 4, 900, 64, 0),), dtype=torch.uint8, device="cuda")
     for S, seqlens in ((900, [900, 700, 3]), (500, [10, 499, 0])):
         q, k, v, sl = _inputs(3, 8, 4, S, 64, "bf16", 1.0, seed=S, seqlens=seqlens)
         log(f"[decode] workspace reuse S{S} seqlens {seqlens}")
@@ -92,6 +92,6 @@ def test_decode_reuses_workspace():
 def test_decode_rejects_small_workspace():
     from entmax_amd import EntmaxError, decode_workspace_bytes, entmax_attn_decode
     q, k, v, sl = _inputs(2, 4, 4, 64, 64, "f32", 1.0, seed=1, seqlens=[64, 10])
-    ws = torch.empty((decode_workspace_bytes(2, 4, 64, 64, 0) - 256,), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((decode_workspace_bytes(2, 4, 4, 64, 64, 0) - 256,), dtype=torch.uint8, device="cuda")
     with pytest.raises(EntmaxError):
         entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, workspace=ws)
