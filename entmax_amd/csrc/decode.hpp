@@ -17,10 +17,17 @@
 //      O = P V on float32 MFMA.
 //   4. dec_reduce: O = sum of the partials of the chunks that hold a score
 //      above tau (the same test as step 3), one wave per row.
+// Spans of at most 256 keys (the splash window, short caches) take one
+// launch instead: dec_short_kernel keeps the scores of its group in LDS,
+// solves each row with one wave and forms O directly.
 #pragma once
+
+#include <type_traits>
+#include <utility>
 
 #include "col_solve.hpp"
 #include "common.hpp"
+#include "rows.hpp"
 
 namespace ea {
 
@@ -108,40 +115,35 @@ __global__ __launch_bounds__(kThreads) void dec_scores_kernel(DecArgs a) {
 }
 
 // Feature f of the output tile: lane c of feature tile ct serves feature
-// c (D/16) + ct, so that each lane reads D/16 consecutive features of a V row.
+// c (D/16) + ct, so that each lane reads D/16 consecutive features of a V row
+// (kept raw; f(ct) converts).
 template <int DT, int D> struct VRow;
 template <int D> struct VRow<DT_BF16, D> {
     static constexpr int N = D / 16;
-    float f[N];
+    unsigned w[N / 2];
     __device__ __forceinline__ void load(const uint16_t* row, int c) {
         const uint16_t* p = row + N * c;
         if constexpr (N == 8) {
             const u32x4 u = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[2 * e] = __uint_as_float(u[e] << 16);
-                f[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-            }
+            w[0] = u[0]; w[1] = u[1]; w[2] = u[2]; w[3] = u[3];
         } else {
             const uint2 u = *reinterpret_cast<const uint2*>(p);
-            f[0] = __uint_as_float(u.x << 16);
-            f[1] = __uint_as_float(u.x & 0xFFFF0000u);
-            f[2] = __uint_as_float(u.y << 16);
-            f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+            w[0] = u.x; w[1] = u.y;
         }
+    }
+    __device__ __forceinline__ float f(int e) const {
+        return __uint_as_float((e & 1) ? (w[e / 2] & 0xFFFF0000u) : (w[e / 2] << 16));
     }
 };
 template <int D> struct VRow<DT_F32, D> {
     static constexpr int N = D / 16;
-    float f[N];
+    f32x4 w[N / 4];
     __device__ __forceinline__ void load(const float* row, int c) {
         const float* p = row + N * c;
 #pragma unroll
-        for (int e = 0; e < N; e += 4) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(p + e);
-            f[e] = u[0]; f[e + 1] = u[1]; f[e + 2] = u[2]; f[e + 3] = u[3];
-        }
+        for (int e = 0; e < N / 4; ++e) w[e] = *reinterpret_cast<const f32x4*>(p + 4 * e);
     }
+    __device__ __forceinline__ float f(int e) const { return w[e / 4][e % 4]; }
 };
 
 template <int DT, int D>
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
         VRow<DT, D> vr;
         vr.load(vh + static_cast<size_t>(r < span ? lo + r : n - 1) * D, c);   // past the span: p = 0
 #pragma unroll
-        for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(p[s], vr.f[ct], o[ct]);
+        for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(p[s], vr.f(ct), o[ct]);
     }
     // lane (g, c) holds O[query 4 g + i][feature c NF + ct]; sum the four waves
     __shared__ float red[4][16][D];
@@ -254,6 +256,127 @@ __global__ __launch_bounds__(kThreads) void dec_reduce_kernel(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) a.out[static_cast<size_t>(row) * D + 64 * e + lane] = acc[e];
     if (a.tau_out != nullptr && lane == 0) a.tau_out[row] = t;
+}
+
+// Whole decode step for spans of at most 256 keys: one workgroup per
+// (b, key/value head, group of up to 16 query heads).  Scores into LDS as
+// in dec_scores; wave w solves rows w, w + 4, ... (one f32x4 per lane, the
+// register bisection of the row-wise op) and overwrites them with p; then
+// P V as in dec_pv, summed over the four waves.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
+    using T = typename InT<DT>::type;
+    constexpr int NF = D / 16;
+    constexpr int SP = kDecChunk + 4;             // LDS row pitch of the scores
+    const int bk = blockIdx.x;
+    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+    int h0, h1, lo, n;
+    dec_heads(a, kvh, blockIdx.y, &h0, &h1);
+    dec_span(a, b, &lo, &n);
+    const int span = n - lo;                      // <= 256 (checked by the host)
+    const int ng = h1 - h0;
+    const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
+    if (span == 0) {   // uniform: nothing to attend
+        for (int e = tid; e < ng * D; e += kThreads) a.out[static_cast<size_t>(b * a.H + h0) * D + e] = 0.f;
+        if (a.tau_out != nullptr && tid < ng) a.tau_out[b * a.H + h0 + tid] = kInf;
+        return;
+    }
+    __shared__ float Ss[16][SP];
+    __shared__ float red[4][16][D];
+
+    // 1. scores of keys 64 w .. 64 w + 63 of the span (-inf past it)
+    {
+        QFrag<DT, D> qf;
+        qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(b) * a.H * D, h0 + c, h1, g);
+        const T* kh = static_cast<const T*>(a.k) + static_cast<size_t>(bk) * a.S * D;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = 64 * wv + 16 * t + c;
+            const bool live = 64 * wv + 16 * t < span;   // uniform: the tile holds a key of the span
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (live) acc = qf.tile(kh, r < span ? lo + r : n - 1, n, g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ss[4 * g + i][r] = r < span ? acc[i] * a.scale : -kInf;
+        }
+    }
+    __syncthreads();
+
+    // V rows of this wave's keys, in flight during the solve
+    const bool pv_live = 64 * wv < span;   // uniform
+    VRow<DT, D> vr[16];
+    if (pv_live) {
+        const T* vh = static_cast<const T*>(a.v) + static_cast<size_t>(bk) * a.S * D;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int r = 64 * wv + 16 * g + s;
+            vr[s].load(vh + static_cast<size_t>(r < span ? lo + r : n - 1) * D, c);   // past the span: p = 0
+        }
+    }
+
+    // 2. tau per row; p = [(s - tau)/2]_+^2 replaces the scores
+    auto sq = [](float y) { return y * y; };
+    auto solve_row = [&](f32x4 (&xs)[1], int valid_base, auto&& rmax, auto&& rsum, auto tpr) {
+        constexpr int TPR = decltype(tpr)::value;
+        const float m = rmax(fmaxf(fmaxf(xs[0][0], xs[0][1]), fmaxf(xs[0][2], xs[0][3])));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[0][i] = valid_base + i < span ? 0.5f * (xs[0][i] - m) : -kInf;
+        const float tt = bisect_regs<1, false, TPR>(xs, static_cast<float>(span), 0.5f, sq, rsum);
+        f32x4 p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float y = relu1(xs[0][i] - tt);
+            p[i] = y * y;
+        }
+        return std::pair<f32x4, float>(p, m + 2.f * tt);
+    };
+    if (span <= 64) {
+        // one row per 16 lanes: wave w solves rows 4 w .. 4 w + 3 at once
+        const int hr = 4 * wv + g, l = lane % 16;
+        if (4 * wv < ng) {   // uniform
+            f32x4 xs[1];
+            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[hr][4 * l]);
+            const auto r = solve_row(xs, 4 * l, [](float v) { return row_max<16>(v); },
+                                     [](float v) { return row_sum<16>(v); }, std::integral_constant<int, 16>());
+            if (hr < ng) {
+                *reinterpret_cast<f32x4*>(&Ss[hr][4 * l]) = r.first;
+                if (l == 0 && a.tau_out != nullptr) a.tau_out[b * a.H + h0 + hr] = r.second;
+            }
+        }
+    } else {
+        // one row per wave: wave w solves rows w, w + 4, ...
+        for (int hr = wv; hr < ng; hr += 4) {
+            f32x4 xs[1];
+            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[hr][4 * lane]);
+            const auto r = solve_row(xs, 4 * lane, [](float v) { return wave_max(v); },
+                                     [](float v) { return wave_sum(v); }, std::integral_constant<int, kWave>());
+            *reinterpret_cast<f32x4*>(&Ss[hr][4 * lane]) = r.first;
+            if (lane == 0 && a.tau_out != nullptr) a.tau_out[b * a.H + h0 + hr] = r.second;
+        }
+    }
+    __syncthreads();
+
+    // 3. O = P V: lane (g, c) holds p of query head h0 + c at key 64 w + 16 g + s
+    f32x4 o[NF];
+#pragma unroll
+    for (int ct = 0; ct < NF; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (pv_live) {
+        const float* pr = &Ss[c < ng ? c : 0][64 * wv + 16 * g];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const float ps = c < ng ? pr[s] : 0.f;   // keys past the span hold p = 0
+#pragma unroll
+            for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(ps, vr[s].f(ct), o[ct]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NF; ++ct) red[wv][4 * g + i][c * NF + ct] = o[ct][i];
+    __syncthreads();
+    for (int e = tid; e < ng * D; e += kThreads) {
+        const int qh = e / D, f = e - qh * D;
+        a.out[static_cast<size_t>(b * a.H + h0 + qh) * D + f] = (red[0][qh][f] + red[1][qh][f]) + (red[2][qh][f] + red[3][qh][f]);
+    }
 }
 
 }  // namespace ea

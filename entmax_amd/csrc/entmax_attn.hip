@@ -231,7 +231,12 @@ int check_decode(int B, int H, int Hkv, int S, int d, int dtype, int window) {
 template <int DT, int D>
 void launch_decode(const ea::DecArgs& a, hipStream_t st) {
     const int G = a.H / a.Hkv;
-    const dim3 grid(a.nch, a.B * a.Hkv, (G + 15) / 16), block(ea::kThreads);
+    const dim3 block(ea::kThreads);
+    if (a.nch == 1) {   // every span fits one chunk: one launch
+        hipLaunchKernelGGL((ea::dec_short_kernel<DT, D>), dim3(a.B * a.Hkv, (G + 15) / 16), block, 0, st, a);
+        return;
+    }
+    const dim3 grid(a.nch, a.B * a.Hkv, (G + 15) / 16);
     hipLaunchKernelGGL((ea::dec_scores_kernel<DT, D>), grid, block, 0, st, a);
     ea::RowsArgs r;
     r.s = a.sbuf; r.mask = nullptr; r.p = nullptr; r.tau = a.tau; r.R = a.B * a.H; r.L = a.P; r.alpha = 1.5f;

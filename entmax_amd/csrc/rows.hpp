@@ -78,6 +78,73 @@ __device__ __forceinline__ unsigned valid4(const uint8_t* mask, size_t row_off, 
     return v;
 }
 
+// Upper end of the bracket in the scaled shifted domain: -n^(1 - alpha)
+// (-1/sqrt(n) at alpha = 1.5).
+template <bool GEN>
+__device__ __forceinline__ float bracket_hi(float n, float am1) {
+    return GEN ? -__builtin_amdgcn_exp2f(-am1 * __builtin_amdgcn_logf(n)) : -__builtin_amdgcn_rsqf(n);
+}
+
+// 25 bisection steps on t for a row held in registers, NV quads per thread:
+// x = (alpha - 1)(s - max), -inf where not allowed, n >= 1 allowed entries.
+// g(mid) = sum [x - mid]_+^(1/(alpha-1)) (each term at most 1: x <= 0 and
+// mid >= -1), g > 1 moves the lower end; returns the final midpoint.
+// Entries at or below the lower end never count again (every later midpoint
+// lies above it): after the first kFirst steps, when no thread holds more
+// than kCand entries above the lower end, the remaining steps run over those
+// slots.  pw: y -> y^(1/(alpha-1)); rsum: sum over the row's TPR threads,
+// bitwise identical in all of them.  TPR <= 64: the threads of a wave take
+// the same path (several rows per wave with TPR < 64).
+template <int NV, bool GEN, int TPR, class PW, class RSum>
+__device__ __forceinline__ float bisect_regs(const f32x4 (&xs)[NV], float n, float am1, PW pw, RSum rsum) {
+    constexpr int kFirst = 4, kCand = 4;
+    float lo = -1.f, hi = bracket_hi<GEN>(n, am1);
+    auto step = [&](auto&& partial) {
+        const float mid = 0.5f * (lo + hi);
+        if (rsum(partial(mid)) > 1.f) lo = mid;
+        else hi = mid;
+    };
+    auto full = [&](float mid) {
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc += pw(relu1(xs[q][i] - mid));
+        return acc;
+    };
+    int it = 0;
+    for (; it < kFirst; ++it) step(full);
+    float cs[kCand];
+    int nc = 0;
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) cs[k] = -kInf;
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = xs[q][i];
+            const bool cand = x > lo;
+#pragma unroll
+            for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
+            nc += cand ? 1 : 0;
+        }
+    bool few;
+    if constexpr (TPR <= kWave) few = !__any(nc > kCand);   // over the wave (all its rows)
+    else few = !__syncthreads_or(nc > kCand);
+    if (few) {
+        for (; it < kIters; ++it)
+            step([&](float mid) {
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < kCand; ++k) acc += pw(relu1(cs[k] - mid));
+                return acc;
+            });
+    } else {
+        for (; it < kIters; ++it) step(full);
+    }
+    return 0.5f * (lo + hi);
+}
+
 // TPR threads per row: a wave (many rows), or the whole workgroup (few long
 // rows, as at decode time: sums then go through LDS, one barrier each).
 // NV chunks of 4 TPR entries per row in registers (L <= 4 TPR NV); NV = 0:
@@ -162,74 +229,26 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
 #pragma unroll
         for (int q = 0; q < NV; ++q) xs[q] = shifted(xs[q], vb[q]);
     }
-    // 25 bisection steps: g(mid) = sum [x - mid]_+^2 (each term at most 1:
-    // x <= 0 and mid >= -1), g > 1 moves the lower end.  Entries at or below
-    // the lower end never count again (every later midpoint lies above it):
-    // after the first kFirst steps, when no lane holds more than kCand
-    // entries above the lower end, the remaining steps run over those slots.
-    constexpr int kFirst = 4, kCand = 4;
-    float lo = -1.f, hi = GEN ? -__builtin_amdgcn_exp2f(-am1 * __builtin_amdgcn_logf(n)) : -__builtin_amdgcn_rsqf(n);
-    auto step = [&](auto&& partial) {
-        const float mid = 0.5f * (lo + hi);
-        if (rsum(partial(mid)) > 1.f) lo = mid;
-        else hi = mid;
-    };
-    auto full = [&](float mid) {
-        float acc = 0.f;
-        if constexpr (NV > 0) {
-#pragma unroll
-            for (int q = 0; q < NV; ++q)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc += pw(relu1(xs[q][i] - mid));
-                }
-        } else {
+    float t;
+    if constexpr (NV > 0) {
+        t = bisect_regs<NV, GEN, TPR>(xs, n, am1, pw, rsum);
+    } else {
+        // rows longer than the registers hold: every step re-reads the row
+        float lo = -1.f, hi = bracket_hi<GEN>(n, am1);
+        for (int it = 0; it < kIters; ++it) {
+            const float mid = 0.5f * (lo + hi);
+            float acc = 0.f;
             for (int c = 0; c < nch; ++c) {
                 const int j = CH * c + 4 * lane;
                 const f32x4 x = shifted(load4<DT>(a.s, off, j, L), valid4(a.mask, off, j, Lr));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc += pw(relu1(x[i] - mid));
-                }
+                for (int i = 0; i < 4; ++i) acc += pw(relu1(x[i] - mid));
             }
+            if (rsum(acc) > 1.f) lo = mid;
+            else hi = mid;
         }
-        return acc;
-    };
-    int it = 0;
-    bool few = false;
-    float cs[kCand];
-    if constexpr (NV > 0) {
-        for (; it < kFirst; ++it) step(full);
-        int nc = 0;
-#pragma unroll
-        for (int k = 0; k < kCand; ++k) cs[k] = -kInf;
-#pragma unroll
-        for (int q = 0; q < NV; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = xs[q][i];
-                const bool cand = x > lo;
-#pragma unroll
-                for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
-                nc += cand ? 1 : 0;
-            }
-        if constexpr (TPR == kWave) few = !__any(nc > kCand);
-        else few = !__syncthreads_or(nc > kCand);
+        t = 0.5f * (lo + hi);
     }
-    if (few) {
-        for (; it < kIters; ++it)
-            step([&](float mid) {
-                float acc = 0.f;
-#pragma unroll
-                for (int k = 0; k < kCand; ++k) {
-                    acc += pw(relu1(cs[k] - mid));
-                }
-                return acc;
-            });
-    } else {
-        for (; it < kIters; ++it) step(full);
-    }
-    const float t = 0.5f * (lo + hi);
     if (a.tau != nullptr && lane == 0) a.tau[row] = m + t * beta;   // score units: p = [(alpha-1)(s - tau)]_+^beta
     if (a.p == nullptr) return;
     for (int c = 0; c < ncw; ++c) {

@@ -95,3 +95,28 @@ def test_decode_rejects_small_workspace():
     ws = torch.empty((decode_workspace_bytes(2, 4, 4, 64, 64, 0) - 256,), dtype=torch.uint8, device="cuda")
     with pytest.raises(EntmaxError):
         entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, workspace=ws)
+
+
+def test_decode_in_a_graph_replays_like_eager():
+    # captured in a HIP graph (no memset nodes: the path writes every
+    # workspace word it reads), every replay matches the eager call
+    from entmax_amd import decode_workspace_bytes, entmax_attn_decode
+    for S, window in ((2048, 32), (1100, 0)):
+        q, k, v, sl = _inputs(4, 8, 2, S, 64, "bf16", 1.0, seed=S + window, seqlens=[S, 5, 0, S // 2])
+        q, k, v, sl = q.cuda(), k.cuda(), v.cuda(), sl.cuda()
+        log(f"[decode] graph S{S} W{window}")
+        ws = torch.empty((decode_workspace_bytes(4, 8, 2, S, 64, window),), dtype=torch.uint8, device="cuda")
+        ref_o, ref_t = entmax_attn_decode(q, k, v, sl, window, workspace=ws)
+        out = torch.empty_like(ref_o)
+        tau = torch.empty_like(ref_t)
+        entmax_attn_decode(q, k, v, sl, window, out=out, tau=tau, workspace=ws)   # warm-up outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            entmax_attn_decode(q, k, v, sl, window, out=out, tau=tau, workspace=ws)
+        for _ in range(3):
+            out.fill_(7.0)
+            tau.fill_(7.0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(tau, ref_t)
