@@ -307,37 +307,46 @@ def attention_backward(q, k, v, dout, key_mask=None, causal=False, window=0,
 
 
 def attention_decode(q, k_cache, v_cache, seqlens, window=0):
-    """1.5-entmax attention for one new query per sequence against a key/value
-    cache (decode time for the causal decoders of "ADASPLASH -- ROBERTA
-    Benchmark Result", section 3, with the splash window of section 7.1's
-    decoder configuration).
+    """1.5-entmax attention for the newest queries of each sequence against a
+    key/value cache (decode time for the causal decoders of "ADASPLASH --
+    ROBERTA Benchmark Result", section 3, with the splash window of section
+    7.1's decoder configuration).
 
-    Arguments: q [B, H, d]; k_cache, v_cache [B, H_kv, S, d] (H_kv divides H,
-    grouped-query repeat as in ``attention_forward``); seqlens [B]: the cache
-    of sequence b holds n_b = seqlens[b] valid positions (clamped to [0, S]),
-    the last of them the new token's own key and value, so the query sits at
-    position n_b - 1.  Causality allows every cached key; window W > 0
-    allows keys j > n_b - 1 - W only (W keys including the query's own).
-    Scores q . k_j / sqrt(d), 1.5-entmax over the allowed keys, O = A V.
+    Arguments: q [B, H, d] (one new query per sequence) or [B, H, Lq, d];
+    k_cache, v_cache [B, H_kv, S, d] (H_kv divides H, grouped-query repeat as
+    in ``attention_forward``); seqlens [B]: the cache of sequence b holds
+    n_b = seqlens[b] valid positions (clamped to [0, S]), the newest Lq of
+    them the queries' own keys and values, so query i sits at position
+    n_b - Lq + i (the queries are the last Lq positions of the sequence).
+    Causality allows keys j <= that position; window W > 0 allows keys
+    j > position - W only (W keys including the query's own).  Scores
+    q . k_j / sqrt(d), 1.5-entmax over the allowed keys, O = A V.
 
-    Returns (out [B, H, d], tau [B, H]); a sequence with n_b = 0 gets O = 0
-    and tau = +inf.
+    Returns (out, tau) shaped like q without / with its last axis; a query
+    with no allowed key (its position below 0) gets O = 0 and tau = +inf.
     """
     q, k, v = _as64(q), _as64(k_cache), _as64(v_cache)
-    B, H, d = q.shape
+    single = q.ndim == 3
+    if single:
+        q = q[:, :, None, :]
+    B, H, Lq, d = q.shape
     S = k.shape[2]
     rep = H // k.shape[1]
     sl = np.asarray(seqlens.detach().cpu().numpy() if hasattr(seqlens, "detach") else seqlens)
-    out = np.zeros((B, H, d))
-    tau = np.full((B, H), np.inf)
+    out = np.zeros((B, H, Lq, d))
+    tau = np.full((B, H, Lq), np.inf)
     for b in range(B):
         n = int(min(max(int(sl[b]), 0), S))
-        lo = max(0, n - window) if window > 0 else 0
-        if n == 0:
-            continue
-        for h in range(H):
-            s = (k[b, h // rep, lo:n] @ q[b, h]) / np.sqrt(d)
-            p, t = entmax15_exact(s)
-            out[b, h] = p @ v[b, h // rep, lo:n]
-            tau[b, h] = t
+        for i in range(Lq):
+            pos = n - Lq + i
+            if pos < 0:
+                continue
+            lo = max(0, pos - window + 1) if window > 0 else 0
+            for h in range(H):
+                s = (k[b, h // rep, lo:pos + 1] @ q[b, h, i]) / np.sqrt(d)
+                p, t = entmax15_exact(s)
+                out[b, h, i] = p @ v[b, h // rep, lo:pos + 1]
+                tau[b, h, i] = t
+    if single:
+        return out[:, :, 0], tau[:, :, 0]
     return out, tau

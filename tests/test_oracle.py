@@ -506,3 +506,28 @@ def test_decode_window_one_is_own_value():
             np.testing.assert_allclose(out[b, h], vc[b, h, n - 1], atol=1e-14)
             s = q[b, h] @ kc[b, h, n - 1] / np.sqrt(8)
             assert abs(tau[b, h] - (s - 2.0)) < 1e-12
+
+
+@pytest.mark.parametrize("window,hkv", [(0, 2), (6, 4)])
+def test_decode_several_queries_are_the_last_rows_of_causal_forward(window, hkv):
+    # Lq new queries at the end of each cached sequence = the last Lq rows
+    # of causal (windowed) attention over the prefix; a sequence shorter than
+    # Lq leaves its first queries without keys
+    from oracle import attention_decode, attention_forward
+    rng = np.random.default_rng(40 + window)
+    B, H, S, d, Lq = 3, 4, 50, 16, 5
+    q = rng.normal(size=(B, H, Lq, d))
+    kc = rng.normal(size=(B, hkv, S, d))
+    vc = rng.normal(size=(B, hkv, S, d))
+    seqlens = np.array([S, 23, 3])
+    out, tau = attention_decode(q, kc, vc, seqlens, window)
+    for b in range(B):
+        n = seqlens[b]
+        qf = rng.normal(size=(1, H, n, d))
+        m = min(n, Lq)
+        qf[0, :, n - m:] = q[b, :, Lq - m:]
+        ref = attention_forward(qf, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], causal=True, window=window,
+                                rows=np.arange(n - m, n))
+        np.testing.assert_allclose(out[b, :, Lq - m:], ref["out"], atol=1e-12)
+        np.testing.assert_allclose(tau[b, :, Lq - m:], ref["tau"], atol=1e-12)
+        assert np.all(out[b, :, :Lq - m] == 0) and np.all(np.isinf(tau[b, :, :Lq - m]))
