@@ -79,9 +79,9 @@ def load_library(path=LIB_PATH):
     lib.entmax_bisect_rows_bwd.argtypes = [fp, fp, fp, i32, i32, f32, vp]
     lib.entmax_bisect_rows_bwd.restype = i32
     sz = ctypes.c_size_t
-    lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.entmax_attn_decode_workspace_size.restype = sz
-    lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_decode.restype = i32
     lib.entmax_attn_status_string.argtypes = [i32]
     lib.entmax_attn_status_string.restype = ctypes.c_char_p
@@ -198,27 +198,29 @@ def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=No
     return probs
 
 
-def decode_workspace_bytes(B, H, H_kv, S, d, window=0):
+def decode_workspace_bytes(B, H, H_kv, S, d, window=0, Lq=1):
     """Bytes of device workspace ``entmax_attn_decode`` needs."""
-    return int(load_library().entmax_attn_decode_workspace_size(B, H, H_kv, S, d, int(window)))
+    return int(load_library().entmax_attn_decode_workspace_size(B, H, H_kv, Lq, S, d, int(window)))
 
 
 def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=None, workspace=None,
                        want_tau=True):
-    """Decode-time 1.5-entmax attention: one new query per sequence against
-    a key/value cache.
+    """Decode-time 1.5-entmax attention: the newest queries of each sequence
+    against a key/value cache.
 
-    q [B, H, d]; k_cache, v_cache [B, H_kv, S, d] (same dtype, float32 or
-    bfloat16); seqlens [B] int32 on the GPU (valid cache positions per
-    sequence, the new token's included); window 0 (all cached keys) or
+    q [B, H, d] (one new token) or [B, H, Lq, d]; k_cache, v_cache
+    [B, H_kv, S, d] (same dtype, float32 or bfloat16); seqlens [B] int32 on
+    the GPU (valid cache positions per sequence, the new tokens' included:
+    query i sits at seqlens[b] - Lq + i); window 0 (every earlier key) or
     W > 0.  workspace: a uint8 GPU tensor of at least
     ``decode_workspace_bytes`` bytes, or None to allocate one.  Returns
-    (out [B, H, d] float32, tau [B, H] float32 or None).
+    (out float32 shaped like q, tau float32 shaped like q without d, or None).
     """
     lib = load_library()
-    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B, H, d]; k_cache and v_cache [B, H_kv, S, d] of one shape")
-    B, H, d = q.shape
+    if q.dim() not in (3, 4) or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d] or [B, H, Lq, d]; k_cache and v_cache [B, H_kv, S, d] of one shape")
+    B, H, d = q.shape[0], q.shape[1], q.shape[-1]
+    Lq = 1 if q.dim() == 3 else q.shape[2]
     if k_cache.shape[0] != B or k_cache.shape[3] != d or H % k_cache.shape[1] != 0:
         raise ValueError("k_cache must be [B, H_kv, S, d] with H_kv dividing H")
     for name, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
@@ -227,16 +229,16 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
     if seqlens.shape != (B,) or seqlens.dtype != torch.int32 or seqlens.device != q.device:
         raise ValueError("seqlens must be a [B] int32 tensor on q's device")
     hkv, S = k_cache.shape[1], k_cache.shape[2]
-    need = decode_workspace_bytes(B, H, hkv, S, d, window)
+    need = decode_workspace_bytes(B, H, hkv, S, d, window, Lq)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if tau is None and want_tau:
-        tau = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        tau = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     rc = lib.entmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens.contiguous()), int(window),
                                 _ptr(out), _ptr(tau), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                B, H, hkv, S, d, _dtype_code(q), _stream(q))
+                                B, H, hkv, Lq, S, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return out, tau
 

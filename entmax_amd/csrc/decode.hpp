@@ -1,17 +1,20 @@
-// Decode-time forward: one new query per sequence against a key/value cache
-// (the causal decoders of "ADASPLASH -- ROBERTA Benchmark Result", section 3,
-// with the splash window of the decoder configuration in section 7.1).
+// Decode-time forward: the newest Lq queries of each sequence against a
+// key/value cache (the causal decoders of "ADASPLASH -- ROBERTA Benchmark
+// Result", section 3, with the splash window of the decoder configuration in
+// section 7.1); Lq = 1 is one decode step, Lq > 1 a chunk of new tokens.
 //
-// Sequence b holds n_b cached positions; its query sits at n_b - 1 and may
-// attend keys [lo_b, n_b), lo_b = max(0, n_b - W) with a window W > 0, else
-// 0.  The span is split into chunks of 256 keys so that a long cache spreads
-// over many workgroups (a decode step has few query rows: the work is the
-// HBM read of K and V).  Four launches:
-//   1. dec_scores: per (chunk, b, key/value head, group of up to 16 query
-//      heads): S = q K^T / sqrt(d) on MFMA, written to a float32 row per
-//      query head, plus each row's maximum over the chunk.
-//   2. tau per row by the row-wise solver (rows.hpp) over the first n_b - lo_b
-//      entries of each score row.
+// Sequence b holds n_b cached positions, the queries' own included: query i
+// sits at position n_b - Lq + i and may attend keys j <= that position (and
+// j > position - W with a window W > 0).  The rows of a workgroup are the
+// (query head, query) pairs that share one key/value head, 16 at a time.
+// The keys any of them may attend, [lo_b, n_b), are split into chunks of 256
+// so that a long cache spreads over many workgroups (a decode step has few
+// query rows: the work is the HBM read of K and V).  Scores of keys a row
+// may not attend are -inf, which the row solver counts as not allowed.
+//   1. dec_scores: per (chunk, b, key/value head, row group): S = q K^T /
+//      sqrt(d) on MFMA, written to a float32 row per query row, plus each
+//      row's maximum over the chunk.
+//   2. tau per row by the row-wise solver (rows.hpp).
 //   3. dec_pv: per chunk, skipped whole (no V read) when no row of the group
 //      has a score above its tau in the chunk; else the chunk's partial
 //      O = P V on float32 MFMA.
@@ -19,7 +22,7 @@
 //      above tau (the same test as step 3), one wave per row.
 // Spans of at most 256 keys (the splash window, short caches) take one
 // launch instead: dec_short_kernel keeps the scores of its group in LDS,
-// solves each row with one wave and forms O directly.
+// solves each row with one wave (or 16 lanes) and forms O directly.
 #pragma once
 
 #include <type_traits>
@@ -34,55 +37,64 @@ namespace ea {
 constexpr int kDecChunk = 256;   // keys per workgroup, 64 per wave
 
 struct DecArgs {
-    const void* q;        // [B, H, d]
+    const void* q;        // [B, H, Lq, d]
     const void* k;        // [B, Hkv, S, d]
     const void* v;        // [B, Hkv, S, d]
     const int* seqlens;   // [B]
-    float* out;           // [B, H, d]
-    float* tau_out;       // [B, H] or null
-    // workspace
-    float* sbuf;          // [B H, P] scores, P = nch * 256
-    float* cmax;          // [B H, nch] chunk maxima
-    float* part;          // [B H, nch, d] partial outputs
-    float* tau;           // [B H]
-    int* row_len;         // [B H] span length of each row
-    int B, H, Hkv, S, window;
+    float* out;           // [B, H, Lq, d]
+    float* tau_out;       // [B, H, Lq] or null
+    // workspace (rows: the B H Lq query rows in the order of out)
+    float* sbuf;          // [rows, P] scores, P = nch * 256
+    float* cmax;          // [rows, nch] chunk maxima
+    float* part;          // [rows, nch, d] partial outputs
+    float* tau;           // [rows]
+    int* row_len;         // [rows] span length of the row's sequence
+    int B, H, Hkv, Lq, S, window;
     int nch, P;           // chunks of the longest possible span; row pitch of sbuf
     float scale;
 };
 
-// Keys [lo, n) of sequence b's cache that its query may attend.
+// Keys [lo, n) of sequence b's cache that any of its queries may attend.
 __device__ __forceinline__ void dec_span(const DecArgs& a, int b, int* lo, int* n) {
     int len = a.seqlens[b];
     len = len < 0 ? 0 : (len > a.S ? a.S : len);
     *n = len;
-    *lo = (a.window > 0 && len > a.window) ? len - a.window : 0;
+    const int first = len - a.Lq;   // position of query 0
+    *lo = (a.window > 0 && first - a.window + 1 > 0) ? first - a.window + 1 : 0;
 }
 
-// Query heads [h0, h1) served by key/value head kvh in group z (16 per group).
-__device__ __forceinline__ void dec_heads(const DecArgs& a, int kvh, int z, int* h0, int* h1) {
-    const int G = a.H / a.Hkv;
-    *h0 = kvh * G + 16 * z;
-    const int e = kvh * G + G;
-    *h1 = *h0 + 16 < e ? *h0 + 16 : e;
+// Group z of the rows served by one key/value head: local rows [j0, j1) of
+// its G Lq (query head, query) pairs; the key/value head's rows start at
+// global row bk G Lq.
+__device__ __forceinline__ void dec_rows(const DecArgs& a, int z, int* j0, int* j1) {
+    const int GL = (a.H / a.Hkv) * a.Lq;
+    *j0 = 16 * z;
+    *j1 = *j0 + 16 < GL ? *j0 + 16 : GL;
+}
+
+// Key k may be attended by local row j (query j % Lq) of a sequence of n.
+__device__ __forceinline__ bool dec_allowed(const DecArgs& a, int n, int j, int k) {
+    const int pos = n - a.Lq + j % a.Lq;
+    return k <= pos && (a.window <= 0 || k > pos - a.window);
 }
 
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void dec_scores_kernel(DecArgs a) {
     using T = typename InT<DT>::type;
     const int chunk = blockIdx.x, bk = blockIdx.y;
-    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-    int h0, h1, lo, n;
-    dec_heads(a, kvh, blockIdx.z, &h0, &h1);
+    const int b = bk / a.Hkv;
+    const int rb = bk * (a.H / a.Hkv) * a.Lq;   // first global row of this key/value head
+    int j0, j1, lo, n;
+    dec_rows(a, blockIdx.z, &j0, &j1);
     dec_span(a, b, &lo, &n);
     const int span = n - lo;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
-    if (chunk == 0 && tid < h1 - h0) a.row_len[b * a.H + h0 + tid] = span;
+    if (chunk == 0 && tid < j1 - j0) a.row_len[rb + j0 + tid] = span;
     if (kDecChunk * chunk >= span) return;   // uniform over the workgroup
 
-    // A operand: query heads h0 + c (zero rows past h1)
+    // A operand: rows j0 + c (zero rows past j1)
     QFrag<DT, D> qf;
-    qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(b) * a.H * D, h0 + c, h1, g);
+    qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(rb) * D, j0 + c, j1, g);
     const T* kh = static_cast<const T*>(a.k) + static_cast<size_t>(bk) * a.S * D;
 
     float mx[4] = {-kInf, -kInf, -kInf, -kInf};
@@ -91,13 +103,13 @@ __global__ __launch_bounds__(kThreads) void dec_scores_kernel(DecArgs a) {
     for (int t = 0; t < 4; ++t) {
         const int r = r0 + 16 * t + c;            // this lane's key (column c of the tile)
         const bool ok = r < span;
-        // rows past the span read key n - 1 (valid: span > 0) and are masked
+        // keys past the span read key n - 1 (valid: span > 0) and are masked
         const f32x4 acc = qf.tile(kh, ok ? lo + r : n - 1, n, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int h = h0 + 4 * g + i;
-            const float s = ok ? acc[i] * a.scale : -kInf;
-            if (h < h1) a.sbuf[static_cast<size_t>(b * a.H + h) * a.P + r] = s;
+            const int j = j0 + 4 * g + i;
+            const float s = ok && dec_allowed(a, n, j, lo + r) ? acc[i] * a.scale : -kInf;
+            if (j < j1) a.sbuf[static_cast<size_t>(rb + j) * a.P + r] = s;
             mx[i] = fmaxf(mx[i], s);
         }
     }
@@ -108,9 +120,9 @@ __global__ __launch_bounds__(kThreads) void dec_scores_kernel(DecArgs a) {
         if (c == 0) red[wv][4 * g + i] = m;
     }
     __syncthreads();
-    if (tid < h1 - h0) {
+    if (tid < j1 - j0) {
         const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-        a.cmax[static_cast<size_t>(b * a.H + h0 + tid) * a.nch + chunk] = m;
+        a.cmax[static_cast<size_t>(rb + j0 + tid) * a.nch + chunk] = m;
     }
 }
 
@@ -151,29 +163,29 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
     using T = typename InT<DT>::type;
     constexpr int NF = D / 16;
     const int chunk = blockIdx.x, bk = blockIdx.y;
-    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-    int h0, h1, lo, n;
-    dec_heads(a, kvh, blockIdx.z, &h0, &h1);
+    const int b = bk / a.Hkv;
+    const int rb = bk * (a.H / a.Hkv) * a.Lq;
+    int j0, j1, lo, n;
+    dec_rows(a, blockIdx.z, &j0, &j1);
     dec_span(a, b, &lo, &n);
     const int span = n - lo;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
     if (kDecChunk * chunk >= span) return;   // uniform
     // skip the chunk when every row's scores in it lie at or below its tau
     bool act = false;
-    if (tid < h1 - h0) {
-        const int row = b * a.H + h0 + tid;
+    if (tid < j1 - j0) {
+        const int row = rb + j0 + tid;
         act = a.cmax[static_cast<size_t>(row) * a.nch + chunk] > a.tau[row];
     }
     if (!__syncthreads_or(act)) return;
 
-    // lane (g, c): A[c][g] = p of query head h0 + c at key r0 + 16 g + s
-    // (step s); B[g][c] = V at that key, features c NF .. c NF + NF - 1
+    // lane (g, c): A[c][g] = p of row j0 + c at key r0 + 16 g + s (step s);
+    // B[g][c] = V at that key, features c NF .. c NF + NF - 1
     const int r0 = kDecChunk * chunk + 64 * wv;
-    const int hq = h0 + c;
     float p[16];
     {
-        const bool rok = hq < h1;
-        const int row = b * a.H + (rok ? hq : h0);
+        const bool rok = j0 + c < j1;
+        const int row = rb + (rok ? j0 + c : j0);
         const float tq = a.tau[row];
         const float* sp = a.sbuf + static_cast<size_t>(row) * a.P + r0 + 16 * g;
 #pragma unroll
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float y = relu1(0.5f * (s4[i] - tq));
-                p[e + i] = rok ? y * y : 0.f;   // keys past the span hold -inf: p = 0
+                p[e + i] = rok ? y * y : 0.f;   // keys not attended hold -inf: p = 0
             }
         }
     }
@@ -198,18 +210,18 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(p[s], vr.f(ct), o[ct]);
     }
-    // lane (g, c) holds O[query 4 g + i][feature c NF + ct]; sum the four waves
+    // lane (g, c) holds O[row 4 g + i][feature c NF + ct]; sum the four waves
     __shared__ float red[4][16][D];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int ct = 0; ct < NF; ++ct) red[wv][4 * g + i][c * NF + ct] = o[ct][i];
     __syncthreads();
-    const int ng = h1 - h0;
+    const int ng = j1 - j0;
     for (int e = tid; e < ng * D; e += kThreads) {
-        const int qh = e / D, f = e - qh * D;
-        const float sum = (red[0][qh][f] + red[1][qh][f]) + (red[2][qh][f] + red[3][qh][f]);
-        a.part[(static_cast<size_t>(b * a.H + h0 + qh) * a.nch + chunk) * D + f] = sum;
+        const int jr = e / D, f = e - jr * D;
+        const float sum = (red[0][jr][f] + red[1][jr][f]) + (red[2][jr][f] + red[3][jr][f]);
+        a.part[(static_cast<size_t>(rb + j0 + jr) * a.nch + chunk) * D + f] = sum;
     }
 }
 
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void dec_reduce_kernel(DecArgs a) {
     constexpr int E = D / 64;
     const int lane = threadIdx.x % kWave;
     const int row = blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (row >= a.B * a.H) return;
+    if (row >= a.B * a.H * a.Lq) return;
     const int span = a.row_len[row];
     const float t = a.tau[row];
     const int nc = (span + kDecChunk - 1) / kDecChunk;
@@ -259,35 +271,37 @@ __global__ __launch_bounds__(kThreads) void dec_reduce_kernel(DecArgs a) {
 }
 
 // Whole decode step for spans of at most 256 keys: one workgroup per
-// (b, key/value head, group of up to 16 query heads).  Scores into LDS as
-// in dec_scores; wave w solves rows w, w + 4, ... (one f32x4 per lane, the
-// register bisection of the row-wise op) and overwrites them with p; then
-// P V as in dec_pv, summed over the four waves.
+// (b, key/value head, group of up to 16 rows).  Scores into LDS as in
+// dec_scores; each row is solved by the register bisection of the row-wise
+// op (one f32x4 per lane: 16 lanes per row when the span is at most 64
+// keys, four rows per wave at once, else a wave per row) and overwritten
+// with p; then P V as in dec_pv, summed over the four waves.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
     using T = typename InT<DT>::type;
     constexpr int NF = D / 16;
     constexpr int SP = kDecChunk + 4;             // LDS row pitch of the scores
     const int bk = blockIdx.x;
-    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-    int h0, h1, lo, n;
-    dec_heads(a, kvh, blockIdx.y, &h0, &h1);
+    const int b = bk / a.Hkv;
+    const int rb = bk * (a.H / a.Hkv) * a.Lq;
+    int j0, j1, lo, n;
+    dec_rows(a, blockIdx.y, &j0, &j1);
     dec_span(a, b, &lo, &n);
     const int span = n - lo;                      // <= 256 (checked by the host)
-    const int ng = h1 - h0;
+    const int ng = j1 - j0;
     const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave, g = lane / 16, c = lane % 16;
     if (span == 0) {   // uniform: nothing to attend
-        for (int e = tid; e < ng * D; e += kThreads) a.out[static_cast<size_t>(b * a.H + h0) * D + e] = 0.f;
-        if (a.tau_out != nullptr && tid < ng) a.tau_out[b * a.H + h0 + tid] = kInf;
+        for (int e = tid; e < ng * D; e += kThreads) a.out[static_cast<size_t>(rb + j0) * D + e] = 0.f;
+        if (a.tau_out != nullptr && tid < ng) a.tau_out[rb + j0 + tid] = kInf;
         return;
     }
     __shared__ float Ss[16][SP];
     __shared__ float red[4][16][D];
 
-    // 1. scores of keys 64 w .. 64 w + 63 of the span (-inf past it)
+    // 1. scores of keys 64 w .. 64 w + 63 of the span (-inf where not attended)
     {
         QFrag<DT, D> qf;
-        qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(b) * a.H * D, h0 + c, h1, g);
+        qf.load(static_cast<const T*>(a.q) + static_cast<size_t>(rb) * D, j0 + c, j1, g);
         const T* kh = static_cast<const T*>(a.k) + static_cast<size_t>(bk) * a.S * D;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -296,7 +310,8 @@ __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (live) acc = qf.tile(kh, r < span ? lo + r : n - 1, n, g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Ss[4 * g + i][r] = r < span ? acc[i] * a.scale : -kInf;
+            for (int i = 0; i < 4; ++i)
+                Ss[4 * g + i][r] = r < span && dec_allowed(a, n, j0 + 4 * g + i, lo + r) ? acc[i] * a.scale : -kInf;
         }
     }
     __syncthreads();
@@ -313,14 +328,21 @@ __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
         }
     }
 
-    // 2. tau per row; p = [(s - tau)/2]_+^2 replaces the scores
+    // 2. tau per row; p = [(s - tau)/2]_+^2 replaces the scores.  Entries of
+    // -inf are keys the row may not attend: they do not count in n.
     auto sq = [](float y) { return y * y; };
-    auto solve_row = [&](f32x4 (&xs)[1], int valid_base, auto&& rmax, auto&& rsum, auto tpr) {
+    auto solve_row = [&](f32x4 (&xs)[1], auto&& rmax, auto&& rsum, auto tpr) {
         constexpr int TPR = decltype(tpr)::value;
-        const float m = rmax(fmaxf(fmaxf(xs[0][0], xs[0][1]), fmaxf(xs[0][2], xs[0][3])));
+        float cnt = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[0][i] = valid_base + i < span ? 0.5f * (xs[0][i] - m) : -kInf;
-        const float tt = bisect_regs<1, false, TPR>(xs, static_cast<float>(span), 0.5f, sq, rsum);
+        for (int i = 0; i < 4; ++i) cnt += xs[0][i] > -kInf ? 1.f : 0.f;
+        const float nr = rsum(cnt);
+        const float m = rmax(fmaxf(fmaxf(xs[0][0], xs[0][1]), fmaxf(xs[0][2], xs[0][3])));
+        if (nr == 0.f)   // no key: p = 0, tau = +inf (uniform over the row's lanes)
+            return std::pair<f32x4, float>(f32x4{0.f, 0.f, 0.f, 0.f}, kInf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[0][i] = xs[0][i] > -kInf ? 0.5f * (xs[0][i] - m) : -kInf;
+        const float tt = bisect_regs<1, false, TPR>(xs, nr, 0.5f, sq, rsum);
         f32x4 p;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -331,31 +353,31 @@ __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
     };
     if (span <= 64) {
         // one row per 16 lanes: wave w solves rows 4 w .. 4 w + 3 at once
-        const int hr = 4 * wv + g, l = lane % 16;
+        const int jr = 4 * wv + g, l = lane % 16;
         if (4 * wv < ng) {   // uniform
             f32x4 xs[1];
-            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[hr][4 * l]);
-            const auto r = solve_row(xs, 4 * l, [](float v) { return row_max<16>(v); },
+            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[jr][4 * l]);
+            const auto r = solve_row(xs, [](float v) { return row_max<16>(v); },
                                      [](float v) { return row_sum<16>(v); }, std::integral_constant<int, 16>());
-            if (hr < ng) {
-                *reinterpret_cast<f32x4*>(&Ss[hr][4 * l]) = r.first;
-                if (l == 0 && a.tau_out != nullptr) a.tau_out[b * a.H + h0 + hr] = r.second;
+            if (jr < ng) {
+                *reinterpret_cast<f32x4*>(&Ss[jr][4 * l]) = r.first;
+                if (l == 0 && a.tau_out != nullptr) a.tau_out[rb + j0 + jr] = r.second;
             }
         }
     } else {
         // one row per wave: wave w solves rows w, w + 4, ...
-        for (int hr = wv; hr < ng; hr += 4) {
+        for (int jr = wv; jr < ng; jr += 4) {
             f32x4 xs[1];
-            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[hr][4 * lane]);
-            const auto r = solve_row(xs, 4 * lane, [](float v) { return wave_max(v); },
+            xs[0] = *reinterpret_cast<const f32x4*>(&Ss[jr][4 * lane]);
+            const auto r = solve_row(xs, [](float v) { return wave_max(v); },
                                      [](float v) { return wave_sum(v); }, std::integral_constant<int, kWave>());
-            *reinterpret_cast<f32x4*>(&Ss[hr][4 * lane]) = r.first;
-            if (lane == 0 && a.tau_out != nullptr) a.tau_out[b * a.H + h0 + hr] = r.second;
+            *reinterpret_cast<f32x4*>(&Ss[jr][4 * lane]) = r.first;
+            if (lane == 0 && a.tau_out != nullptr) a.tau_out[rb + j0 + jr] = r.second;
         }
     }
     __syncthreads();
 
-    // 3. O = P V: lane (g, c) holds p of query head h0 + c at key 64 w + 16 g + s
+    // 3. O = P V: lane (g, c) holds p of row j0 + c at key 64 w + 16 g + s
     f32x4 o[NF];
 #pragma unroll
     for (int ct = 0; ct < NF; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -363,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
         const float* pr = &Ss[c < ng ? c : 0][64 * wv + 16 * g];
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-            const float ps = c < ng ? pr[s] : 0.f;   // keys past the span hold p = 0
+            const float ps = c < ng ? pr[s] : 0.f;   // keys not attended hold p = 0
 #pragma unroll
             for (int ct = 0; ct < NF; ++ct) o[ct] = mfma_f32(ps, vr[s].f(ct), o[ct]);
         }
@@ -374,8 +396,8 @@ __global__ __launch_bounds__(kThreads) void dec_short_kernel(DecArgs a) {
         for (int ct = 0; ct < NF; ++ct) red[wv][4 * g + i][c * NF + ct] = o[ct][i];
     __syncthreads();
     for (int e = tid; e < ng * D; e += kThreads) {
-        const int qh = e / D, f = e - qh * D;
-        a.out[static_cast<size_t>(b * a.H + h0 + qh) * D + f] = (red[0][qh][f] + red[1][qh][f]) + (red[2][qh][f] + red[3][qh][f]);
+        const int jr = e / D, f = e - jr * D;
+        a.out[static_cast<size_t>(rb + j0 + jr) * D + f] = (red[0][jr][f] + red[1][jr][f]) + (red[2][jr][f] + red[3][jr][f]);
     }
 }
 

@@ -200,13 +200,16 @@ struct DecLayout {
     size_t sbuf, cmax, part, tau, rlen, total;
 };
 
-DecLayout dec_layout(int B, int H, int S, int d, int window) {  // any H_kv
+DecLayout dec_layout(int B, int H, int Lq, int S, int d, int window) {  // any H_kv
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     DecLayout l;
-    const int span = (window > 0 && window < S) ? window : S;
+    // keys any of the Lq queries may attend: the window of the first query
+    // widened by the Lq - 1 later ones
+    const long long wide = static_cast<long long>(window) + Lq - 1;
+    const int span = (window > 0 && wide < S) ? static_cast<int>(wide) : S;
     l.nch = (span + ea::kDecChunk - 1) / ea::kDecChunk;
     l.P = l.nch * ea::kDecChunk;
-    const size_t rows = static_cast<size_t>(B) * H;
+    const size_t rows = static_cast<size_t>(B) * H * Lq;
     l.sbuf = 0;
     l.cmax = l.sbuf + al(rows * l.P * sizeof(float));
     l.part = l.cmax + al(rows * l.nch * sizeof(float));
@@ -216,34 +219,36 @@ DecLayout dec_layout(int B, int H, int S, int d, int window) {  // any H_kv
     return l;
 }
 
-int check_decode(int B, int H, int Hkv, int S, int d, int dtype, int window) {
+int check_decode(int B, int H, int Hkv, int Lq, int S, int d, int dtype, int window) {
     if (B <= 0 || H <= 0 || S <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, S must be positive (got %d, %d, %d)", B, H, S);
+    if (Lq <= 0 || Lq > S) return fail(ENTMAX_ERR_INVALID_ARG, "Lq = %d outside [1, S = %d]", Lq, S);
     if (Hkv <= 0 || H % Hkv != 0) return fail(ENTMAX_ERR_INVALID_ARG, "H_kv = %d must divide H = %d", Hkv, H);
     if (window < 0) return fail(ENTMAX_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
     if (d != 64 && d != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
     if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
     if (S > (1 << 24)) return fail(ENTMAX_ERR_UNSUPPORTED, "S = %d exceeds 2^24", S);
     if (static_cast<long long>(B) * Hkv > 65535) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H_kv exceeds 65535");
-    if (static_cast<long long>(B) * H * (S + 255) > (1LL << 36)) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H * S too large");
+    if (static_cast<long long>(B) * H * Lq * (S + 255) > (1LL << 36)) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H * Lq * S too large");
+    if ((static_cast<long long>(H / Hkv) * Lq + 15) / 16 > 65535) return fail(ENTMAX_ERR_UNSUPPORTED, "H / H_kv * Lq too large");
     return ENTMAX_OK;
 }
 
 template <int DT, int D>
 void launch_decode(const ea::DecArgs& a, hipStream_t st) {
-    const int G = a.H / a.Hkv;
+    const int nz = ((a.H / a.Hkv) * a.Lq + 15) / 16;   // groups of 16 query rows per key/value head
     const dim3 block(ea::kThreads);
     if (a.nch == 1) {   // every span fits one chunk: one launch
-        hipLaunchKernelGGL((ea::dec_short_kernel<DT, D>), dim3(a.B * a.Hkv, (G + 15) / 16), block, 0, st, a);
+        hipLaunchKernelGGL((ea::dec_short_kernel<DT, D>), dim3(a.B * a.Hkv, nz), block, 0, st, a);
         return;
     }
-    const dim3 grid(a.nch, a.B * a.Hkv, (G + 15) / 16);
+    const dim3 grid(a.nch, a.B * a.Hkv, nz);
     hipLaunchKernelGGL((ea::dec_scores_kernel<DT, D>), grid, block, 0, st, a);
     ea::RowsArgs r;
-    r.s = a.sbuf; r.mask = nullptr; r.p = nullptr; r.tau = a.tau; r.R = a.B * a.H; r.L = a.P; r.alpha = 1.5f;
+    r.s = a.sbuf; r.mask = nullptr; r.p = nullptr; r.tau = a.tau; r.R = a.B * a.H * a.Lq; r.L = a.P; r.alpha = 1.5f;
     r.row_len = a.row_len;
     launch_rows_fwd<ea::DT_F32>(r, st);
     hipLaunchKernelGGL((ea::dec_pv_kernel<DT, D>), grid, block, 0, st, a);
-    hipLaunchKernelGGL((ea::dec_reduce_kernel<D>), dim3((a.B * a.H + 3) / 4), block, 0, st, a);
+    hipLaunchKernelGGL((ea::dec_reduce_kernel<D>), dim3((a.B * a.H * a.Lq + 3) / 4), block, 0, st, a);
 }
 
 int check_rows(int R, int L) {
@@ -368,19 +373,19 @@ int entmax15_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, 
     return entmax_bisect_rows_bwd(p, dp, ds, R, L, 1.5f, stream);
 }
 
-size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int S, int d, int window) {
-    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || S <= 0 || d <= 0 || window < 0) return 0;
-    return dec_layout(B, H, S, d, window).total;
+size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int S, int d, int window) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || Lq <= 0 || S <= 0 || d <= 0 || window < 0) return 0;
+    return dec_layout(B, H, Lq, S, d, window).total;
 }
 
 int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, int window,
                        float* out, float* tau_out, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
-                       int S, int d, int dtype, void* stream) {
+                       int Lq, int S, int d, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens, out and workspace must not be NULL");
-    int rc = check_decode(B, H, Hkv, S, d, dtype, window);
+    int rc = check_decode(B, H, Hkv, Lq, S, d, dtype, window);
     if (rc) return rc;
-    const DecLayout l = dec_layout(B, H, S, d, window);
+    const DecLayout l = dec_layout(B, H, Lq, S, d, window);
     if (workspace_bytes < l.total)
         return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
@@ -392,7 +397,7 @@ int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, 
     a.part = reinterpret_cast<float*>(ws + l.part);
     a.tau = reinterpret_cast<float*>(ws + l.tau);
     a.row_len = reinterpret_cast<int*>(ws + l.rlen);
-    a.B = B; a.H = H; a.Hkv = Hkv; a.S = S; a.window = window; a.nch = l.nch; a.P = l.P;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.S = S; a.window = window; a.nch = l.nch; a.P = l.P;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) {

@@ -33,7 +33,8 @@ struct RowsArgs {
     int R, L;                 // rows; row pitch (elements, a multiple of 4)
     float alpha;              // in (1, 2]; 1.5 unless GEN
     // [R] or null: row r takes part in the row only in its first
-    // min(row_len[r], L) entries (the rest count as not allowed)
+    // min(row_len[r], L) entries (the rest count as not allowed); entries
+    // of -inf never count
     const int* row_len = nullptr;
 };
 
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void rows_fwd_kernel(RowsArgs a) {
         const unsigned ok = valid4(a.mask, off, j, Lr);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool on = (ok >> i) & 1u;
+            const bool on = ((ok >> i) & 1u) && v[i] > -kInf;   // -inf: not allowed
             mraw = fmaxf(mraw, on ? v[i] : -kInf);
             cnt += on ? 1.f : 0.f;
         }

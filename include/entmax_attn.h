@@ -155,38 +155,39 @@ int entmax_bisect_rows_bwd(const float *p, const float *dp, float *ds, int R, in
                            void *stream);
 
 /*
- * Decode-time forward: one new query per sequence against a key/value cache
- * (the causal decoders of "ADASPLASH -- ROBERTA Benchmark Result", section 3,
- * with the splash window of the decoder configuration in section 7.1).
+ * Decode-time forward: the newest Lq queries of each sequence against a
+ * key/value cache (the causal decoders of "ADASPLASH -- ROBERTA Benchmark
+ * Result", section 3, with the splash window of the decoder configuration in
+ * section 7.1).  Lq = 1 is one decode step; Lq > 1 a chunk of new tokens
+ * (query length below key length).
  *
- *  - q: [B, H, d] of `dtype`, the new token's query per head.
+ *  - q: [B, H, Lq, d] of `dtype`, the new tokens' queries per head.
  *  - k_cache, v_cache: [B, H_kv, S, d] of `dtype` (H_kv divides H; query head
  *    h reads key/value head h / (H / H_kv)).
  *  - seqlens: [B] int32, DEVICE memory: sequence b holds n_b = seqlens[b]
- *    valid cache positions, the new token's own key and value included (at
- *    n_b - 1); values outside [0, S] are clamped to it.
- *  - window: 0 = every cached key is allowed (causality holds by
- *    construction); W > 0 = only keys j > n_b - 1 - W (W keys including the
- *    query's own).
- *  - out: [B, H, d] float32; tau_out: [B, H] float32 (score units) or NULL.
- *    A sequence with n_b = 0 gets O = 0 and tau = +inf.
+ *    valid cache positions, the new tokens' own keys and values included
+ *    (values outside [0, S] are clamped to it).  Query i sits at position
+ *    n_b - Lq + i: it may attend keys j <= n_b - Lq + i, and with window
+ *    W > 0 only keys j > n_b - Lq + i - W (W keys including its own).
+ *  - out: [B, H, Lq, d] float32; tau_out: [B, H, Lq] float32 (score units) or
+ *    NULL.  A query with no key to attend (n_b - Lq + i < 0) gets O = 0 and
+ *    tau = +inf.
  *  - workspace: caller-owned DEVICE memory, 256-byte aligned, of at least
- *    entmax_attn_decode_workspace_size(B, H, H_kv, S, d, window) bytes
- *    (scores of the span, per-chunk maxima, partial outputs and completion
- *    counters); its contents need no initialisation and are scratch after
- *    the call.  Two calls in flight must not share a workspace.
+ *    entmax_attn_decode_workspace_size(B, H, H_kv, Lq, S, d, window) bytes
+ *    (scores of the span, per-chunk maxima, partial outputs); its contents
+ *    need no initialisation and are scratch after the call.  Two calls in
+ *    flight must not share a workspace.
  *  - Supported: d in {64, 128}; dtype ENTMAX_F32 or ENTMAX_BF16;
- *    S <= 2^24; B * H_kv <= 65535.  A too small or misaligned workspace
- *    returns ENTMAX_ERR_INVALID_ARG.
+ *    1 <= Lq <= S <= 2^24; B * H_kv <= 65535.  A too small or misaligned
+ *    workspace returns ENTMAX_ERR_INVALID_ARG.
  * entmax_attn_decode_workspace_size returns 0 for non-positive sizes or an
  * H_kv that does not divide H.
  */
-size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int S, int d, int window);
+size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int S, int d, int window);
 int entmax_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
                        int window, float *out, float *tau_out, void *workspace, size_t workspace_bytes,
-                       int B, int H, int H_kv, int S, int d, int dtype, void *stream);
+                       int B, int H, int H_kv, int Lq, int S, int d, int dtype, void *stream);
 
-/* Human-readable name of a status code (static storage, never NULL). */
 const char *entmax_attn_status_string(int status);
 
 /* Message describing the most recent failure on the calling thread

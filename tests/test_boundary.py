@@ -126,21 +126,25 @@ def test_rows_reject_bad_arguments(lib):
 
 
 def test_decode_rejects_bad_arguments(lib):
-    ws = lib.entmax_attn_decode_workspace_size(2, 4, 4, 64, 64, 0)
+    ws = lib.entmax_attn_decode_workspace_size(2, 4, 4, 1, 64, 64, 0)
     assert ws > 0 and ws % 256 == 0
-    assert lib.entmax_attn_decode_workspace_size(0, 4, 4, 64, 64, 0) == 0
-    assert lib.entmax_attn_decode_workspace_size(2, 4, 3, 64, 64, 0) == 0
+    assert lib.entmax_attn_decode_workspace_size(0, 4, 4, 1, 64, 64, 0) == 0
+    assert lib.entmax_attn_decode_workspace_size(2, 4, 3, 1, 64, 64, 0) == 0
+    assert lib.entmax_attn_decode_workspace_size(2, 4, 4, 0, 64, 64, 0) == 0
     W = ctypes.c_void_p(256)
-    ok = [P, P, P, P, 0, P, None, W, ws, 2, 4, 4, 64, 64, 1, None]
+    ok = [P, P, P, P, 0, P, None, W, ws, 2, 4, 4, 1, 64, 64, 1, None]
     for i in (0, 1, 2, 3, 5, 7):
         a = list(ok)
         a[i] = None
         assert lib.entmax_attn_decode(*a) == 1
-    bad = {8: ws - 1, 11: 3, 4: -1, 13: 96, 14: 7}
+    bad = {8: ws - 1, 11: 3, 4: -1, 12: 0, 14: 96, 15: 7}
     for i, val in bad.items():
         a = list(ok)
         a[i] = val
-        assert lib.entmax_attn_decode(*a) == (2 if i in (13, 14) else 1), i
+        assert lib.entmax_attn_decode(*a) == (2 if i in (14, 15) else 1), i
+    a = list(ok)
+    a[12] = 65           # Lq above S
+    assert lib.entmax_attn_decode(*a) == 1
     a = list(ok)
     a[7] = ctypes.c_void_p(272)      # not 256-byte aligned
     assert lib.entmax_attn_decode(*a) == 1

@@ -80,7 +80,7 @@ def test_decode_long_cache():
 def test_decode_reuses_workspace():
     # a second, smaller call on the same workspace sees nothing of the first
     from entmax_amd import decode_workspace_bytes, entmax_attn_decode
-    ws = torch.empty((decode_workspace_bytes(3, 8, 4, 900, 64, 0),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((decode_workspace_bytes(3, 8, 4, 900, 64, 0, 1),), dtype=torch.uint8, device="cuda")
     for S, seqlens in ((900, [900, 700, 3]), (500, [10, 499, 0])):
         q, k, v, sl = _inputs(3, 8, 4, S, 64, "bf16", 1.0, seed=S, seqlens=seqlens)
         log(f"[decode] workspace reuse S{S} seqlens {seqlens}")
@@ -92,7 +92,7 @@ def test_decode_reuses_workspace():
 def test_decode_rejects_small_workspace():
     from entmax_amd import EntmaxError, decode_workspace_bytes, entmax_attn_decode
     q, k, v, sl = _inputs(2, 4, 4, 64, 64, "f32", 1.0, seed=1, seqlens=[64, 10])
-    ws = torch.empty((decode_workspace_bytes(2, 4, 4, 64, 64, 0) - 256,), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((decode_workspace_bytes(2, 4, 4, 64, 64, 0, 1) - 256,), dtype=torch.uint8, device="cuda")
     with pytest.raises(EntmaxError):
         entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, workspace=ws)
 
@@ -120,3 +120,34 @@ def test_decode_in_a_graph_replays_like_eager():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(out, ref_o) and torch.equal(tau, ref_t)
+
+
+MULTI = [
+    # (dtype, d, H, Hkv, Lq, S, window)
+    ("f32", 64, 4, 4, 2, 40, 32),
+    ("bf16", 64, 8, 2, 5, 300, 32),
+    ("bf16", 128, 8, 2, 5, 300, 0),
+    ("f32", 64, 6, 3, 17, 600, 32),
+    ("bf16", 64, 4, 1, 40, 700, 32),
+    ("bf16", 64, 12, 12, 3, 2048, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv,Lq,S,window", MULTI)
+def test_decode_several_queries(dtype, d, H, Hkv, Lq, S, window):
+    # Lq new tokens per sequence (query length below key length); the
+    # shortest sequence holds fewer positions than queries
+    from entmax_amd import entmax_attn_decode
+    rng = np.random.default_rng(Lq * S + H)
+    seqlens = [S, max(1, Lq // 2), int(rng.integers(Lq, S)), 0]
+    gen = torch.Generator().manual_seed(S + Lq)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn((4, H, Lq, d), generator=gen).to(dt)
+    k = torch.randn((4, Hkv, S, d), generator=gen).to(dt)
+    v = torch.randn((4, Hkv, S, d), generator=gen).to(dt)
+    sl = torch.tensor(seqlens, dtype=torch.int32)
+    log(f"[decode] {dtype} d{d} H{H} Hkv{Hkv} Lq{Lq} S{S} W{window} seqlens {seqlens}")
+    out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), window)
+    torch.cuda.synchronize()
+    assert out.shape == q.shape and tau.shape == q.shape[:-1]
+    _check(q, k, v, sl, window, dtype, out, tau)
