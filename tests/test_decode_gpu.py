@@ -151,3 +151,17 @@ def test_decode_several_queries(dtype, d, H, Hkv, Lq, S, window):
     torch.cuda.synchronize()
     assert out.shape == q.shape and tau.shape == q.shape[:-1]
     _check(q, k, v, sl, window, dtype, out, tau)
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_long"])
+def test_decode_bench_workloads(name):
+    # the inputs and launch configuration bench.py times, every row checked
+    from entmax_amd import entmax_attn_decode
+    from entmax_amd.workloads import make_decode_inputs
+    inp = make_decode_inputs(name)
+    w = inp["spec"]
+    log(f"[decode] bench workload {name}")
+    out, tau = entmax_attn_decode(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["seqlens"].cuda(),
+                                  w["window"])
+    torch.cuda.synchronize()
+    _check(inp["q"], inp["k"], inp["v"], inp["seqlens"], w["window"], w["dtype"], out, tau)

@@ -138,3 +138,23 @@ def test_bisect_rows_backward(alpha, L):
     err = float(np.abs(ds.cpu().numpy() - ref).max()) / max(1.0, float(np.abs(ref).max()))
     log(f"[rows]   scaled err {err:.3g}")
     assert err <= TOL["f32"]
+
+
+def test_rows_bench_workload_sampled():
+    # the [98304, 1024] score matrix bench.py times, 96 sampled rows checked
+    from entmax_amd import entmax15_rows, entmax15_rows_bwd
+    from entmax_amd.workloads import make_row_inputs
+    inp = make_row_inputs("rows")
+    log("[rows] bench workload R98304 L1024")
+    s = inp["scores"].cuda()
+    p, tau = entmax15_rows(s)
+    ds = entmax15_rows_bwd(p, inp["dp"].cuda())
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(s.shape[0], 96, replace=False)
+    s64 = inp["scores"][rows].to(torch.float64).numpy()
+    p_ref, tau_ref = entmax15_exact(s64)
+    assert float(np.abs(p.cpu().numpy()[rows] - p_ref).max()) <= TOL["bf16"]
+    assert float(np.abs(tau.cpu().numpy()[rows] - tau_ref).max()) <= TOL["bf16"]
+    ref = entmax15_backward(s64, inp["dp"][rows].to(torch.float64).numpy())
+    err = float(np.abs(ds.cpu().numpy()[rows] - ref).max()) / max(1.0, float(np.abs(ref).max()))
+    assert err <= TOL["f32"]
