@@ -48,8 +48,14 @@ __device__ __forceinline__ float pow01(float y, float e) {
     return y > 0.f ? __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(y)) : 0.f;
 }
 
-// Sum over the 64 lanes of the wave, bitwise identical in every lane.
-__device__ __forceinline__ float wave_sum(float v) { return col4_sum(row_sum<16>(v)); }
+// Sum over the 64 lanes of the wave, bitwise identical in every lane.  The
+// empty asm keeps the compiler from fusing a product that forms v into the
+// first cross-lane addition: each lane would then round its own product
+// differently from its neighbour's, and the lanes would disagree.
+__device__ __forceinline__ float wave_sum(float v) {
+    asm volatile("" : "+v"(v));
+    return col4_sum(row_sum<16>(v));
+}
 __device__ __forceinline__ float wave_max(float v) { return col4_max(row_max<16>(v)); }
 
 // 4 consecutive entries of row `row` starting at column j (j % 4 == 0, may
@@ -132,6 +138,51 @@ __device__ __forceinline__ float bisect_regs(const f32x4 (&xs)[NV], float n, flo
     bool few;
     if constexpr (TPR <= kWave) few = !__any(nc > kCand);   // over the wave (all its rows)
     else few = !__syncthreads_or(nc > kCand);
+    if constexpr (TPR == kThreads) {
+        // a workgroup per row: when the whole row holds at most 64
+        // candidates, wave 0 takes the remaining steps alone, without a
+        // barrier per step.  The candidates are gathered in thread order (a
+        // prefix sum of the counts), so the result does not depend on timing.
+        __shared__ float gath[kWave];
+        __shared__ int wtot[kThreads / kWave];
+        __shared__ float fin[2];
+        const int wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+        int inc = nc;   // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(inc, o, kWave);
+            inc += ln >= o ? y : 0;
+        }
+        if (ln == kWave - 1) wtot[wv] = inc;
+        __syncthreads();
+        int base = 0, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kThreads / kWave; ++w2) {
+            base += w2 < wv ? wtot[w2] : 0;
+            tot += wtot[w2];
+        }
+        if (few && tot <= kWave) {   // uniform over the workgroup
+            const int off = base + inc - nc;
+#pragma unroll
+            for (int k = 0; k < kCand; ++k)
+                if (k < nc) gath[off + k] = cs[k];
+            __syncthreads();
+            if (wv == 0) {
+                const float x = ln < tot ? gath[ln] : -kInf;
+                for (; it < kIters; ++it) {
+                    const float mid = 0.5f * (lo + hi);
+                    if (wave_sum(pw(relu1(x - mid))) > 1.f) lo = mid;
+                    else hi = mid;
+                }
+                if (ln == 0) {
+                    fin[0] = lo;
+                    fin[1] = hi;
+                }
+            }
+            __syncthreads();
+            return 0.5f * (fin[0] + fin[1]);
+        }
+    }
     if (few) {
         for (; it < kIters; ++it)
             step([&](float mid) {
