@@ -136,8 +136,9 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
             float s[4][4];
             float thr_s[4];   // each row's current threshold m - 2, in the units of s
             bool any = false;
-            auto products = [&](auto causal_tag) {
+            auto products = [&](auto causal_tag, auto full_tag) {
                 constexpr bool CAUSAL = decltype(causal_tag)::value;
+                constexpr bool FULL = decltype(full_tag)::value;   // every key of the chunk valid
                 float tm[4] = {-kInf, -kInf, -kInf, -kInf};
 #pragma unroll
                 for (int c16 = 0; c16 < 4; ++c16) {
@@ -161,6 +162,8 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                             // scaled scores, masks per element, count per element
                             s[c16][i] = score(key, kv, acc, i);
                             nl[i] += s[c16][i] > -kInf ? 1.f : 0.f;
+                        } else if constexpr (FULL) {
+                            s[c16][i] = acc[i];   // raw accumulator (scaled where kept)
                         } else {
                             // raw accumulators (scaled only where they are kept);
                             // rows past L are never written out
@@ -182,13 +185,13 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                     // threshold only keeps more candidates)
                     const float thr = CAUSAL ? m[i] - 2.f : (m[i] - 2.f) * inv_scale - 1e-6f * fabsf(m[i] * inv_scale);
                     thr_s[i] = thr;
-#pragma unroll
-                    for (int c16 = 0; c16 < 4; ++c16) any |= s[c16][i] > thr;
+                    any |= tm[i] > thr;   // this lane's largest entry of the row decides
                 }
             };
             const bool raw = !(a.causal || a.window > 0);   // s holds unscaled accumulators
-            if (a.causal || a.window > 0) products(std::true_type{});
-            else products(std::false_type{});
+            if (a.causal || a.window > 0) products(std::true_type{}, std::false_type{});
+            else if (M == ~0ull) products(std::false_type{}, std::true_type{});
+            else products(std::false_type{}, std::false_type{});
             if (!__any(any)) return;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
