@@ -241,12 +241,15 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                     const float x = fmaf(sv[t][i], c2, -mc2);
                     const float u = (x - lo) * iw;
                     const float cf = x > lo_eff ? floorf(fminf(u, 8.f)) : 9.f;
-                    // offset in [0, 1] (clamped: the dump cell's is meaningless)
-                    const float r = __builtin_amdgcn_fmed3f(cf == 8.f ? x - hi : u - cf, 0.f, 1.f);
+                    // offset in [0, 1]: the fraction of u in cells 0-7 (u - cf,
+                    // exactly), x - hi in [0, 1] in cell 8; the dump cell's
+                    // lies in [0, 1) and is never read
+                    const float r = cf == 8.f ? x - hi : __builtin_amdgcn_fractf(u);
+                    const float rk = r * kFix;
                     unsigned* h = hist + static_cast<int>(cf) * (3 * kWave);
                     lds_add(h, 1u);
-                    lds_add(h + kWave, static_cast<unsigned>(r * kFix));
-                    lds_add(h + 2 * kWave, static_cast<unsigned>(r * r * kFix));
+                    lds_add(h + kWave, static_cast<unsigned>(rk));
+                    lds_add(h + 2 * kWave, static_cast<unsigned>(r * rk));
                 }
             }
         });
