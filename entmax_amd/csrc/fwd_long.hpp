@@ -226,6 +226,10 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
         const float w = (hi - lo) * 0.125f;          // cell width (power-of-two scaling)
         const float iw = 8.f / (hi - lo);
         const float lo_eff = fmaxf(lo, s.lb);
+        // u = (x - lo) / w straight from the raw accumulator (x = sv c2 - mc2);
+        // entries with u at or below u_eff (x at or below lo_eff) are dumped
+        const float ua = c2 * iw, ub = -(mc2 + lo) * iw;
+        const float u_eff = (lo_eff - lo) * iw;
         constexpr float kFix = 4194304.f;            // 2^22
 #pragma unroll
         for (int k = 0; k < kCells * 3; ++k) hist[k * kWave] = 0u;
@@ -238,15 +242,16 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                 if (!ok[t]) continue;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float x = fmaf(sv[t][i], c2, -mc2);
-                    const float u = (x - lo) * iw;
-                    const float cf = x > lo_eff ? floorf(fminf(u, 8.f)) : 9.f;
-                    // offset in [0, 1]: the fraction of u in cells 0-7 (u - cf,
-                    // exactly), x - hi in [0, 1] in cell 8; the dump cell's
-                    // lies in [0, 1) and is never read
-                    const float r = cf == 8.f ? x - hi : __builtin_amdgcn_fractf(u);
+                    const float u = fmaf(sv[t][i], ua, ub);
+                    int ci = static_cast<int>(u);   // the cell, for u > u_eff >= 0
+                    ci = ci < 8 ? ci : 8;
+                    ci = u > u_eff ? ci : 9;
+                    // offset in [0, 1]: the fraction of u in cells 0-7, x - hi
+                    // = (u - 8) w in [0, 1] in cell 8; the dump cell's lies
+                    // in [0, 1) and is never read
+                    const float r = ci == 8 ? (u - 8.f) * w : __builtin_amdgcn_fractf(u);
                     const float rk = r * kFix;
-                    unsigned* h = hist + static_cast<int>(cf) * (3 * kWave);
+                    unsigned* h = hist + ci * (3 * kWave);
                     lds_add(h, 1u);
                     lds_add(h + kWave, static_cast<unsigned>(rk));
                     lds_add(h + 2 * kWave, static_cast<unsigned>(r * rk));
