@@ -317,6 +317,7 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
         s.a1 = 0.f;
         s.a2 = 0.f;
         len = 0;
+        const float lo_eff = fmaxf(s.lo, s.lb);
         stream(false, [&](int ch, const char* kb, const char*, unsigned long long M) {
             f32x4 sv[NTC];
             bool ok[NTC];
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                     s.a1 += y;
                     s.a2 = fmaf(y, y, s.a2);
                     col[(len < CAP ? len : CAP) * kWave] = x;   // row CAP: overflow dump
-                    len += ((x > s.lo) & (x > s.lb) & (x <= s.hi)) ? 1 : 0;
+                    len += ((x > lo_eff) & (x <= s.hi)) ? 1 : 0;
                 }
             }
         });
