@@ -31,8 +31,11 @@ template <int D, int CAP>
 struct StreamCfg {
     static constexpr int BM = 64;
     static constexpr int TPR = kThreads / BM;   // 4 lanes per row in the solve
+    // list row stride: CAP + 4 words puts rows 4 apart (the rows of one lane
+    // group) and consecutive rows (the solve's lanes) on different LDS banks
+    static constexpr int LST = CAP + 4;
     static constexpr size_t lds_bytes =
-        static_cast<size_t>(BM) * CAP * (sizeof(float) + sizeof(uint16_t)) +
+        static_cast<size_t>(BM) * LST * (sizeof(float) + sizeof(uint16_t)) +
         sizeof(float) * 3 * BM + sizeof(int) * 2 * BM;
     // one K chunk buffer (ChunkStream<.., 1>): with CAP = 80 a bf16 workgroup
     // takes under a third of the LDS
@@ -52,14 +55,14 @@ template <int DT, int D, int CAP>
 __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef StreamCfg<D, CAP> C;
-    constexpr int BM = C::BM, TPR = C::TPR;
+    constexpr int BM = C::BM, TPR = C::TPR, LST = C::LST;
     extern __shared__ float lds[];
-    float* lv = lds;                                   // [BM][CAP] candidate scores
-    float* rowm = lv + BM * CAP;                       // [BM] row max
+    float* lv = lds;                                   // [BM][LST] candidate scores (CAP used per row)
+    float* rowm = lv + BM * LST;                       // [BM] row max
     float* rowts = rowm + BM;                          // [BM] shifted tau
     int* rown = reinterpret_cast<int*>(rowts + BM + BM);            // [BM] allowed count
     int* rowc = rown + BM;                             // [BM] list length, -1 = overflow
-    uint16_t* lk = reinterpret_cast<uint16_t*>(rowc + BM);         // [BM][CAP] keys
+    uint16_t* lk = reinterpret_cast<uint16_t*>(rowc + BM);         // [BM][LST] keys
     float* kbufs = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + C::lds_bytes);   // K chunk buffers
 
     const int total = a.B * a.H * a.nqt;
@@ -217,15 +220,15 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                     for (int chh = 0; chh < maxch; ++chh) {
                         const int idx = 16 * chh + c;
                         const bool in = idx < tot;
-                        const float v = in ? lv[rl * CAP + idx] : -kInf;
-                        const uint16_t kk = in ? lk[rl * CAP + idx] : static_cast<uint16_t>(0);
+                        const float v = in ? lv[rl * LST + idx] : -kInf;
+                        const uint16_t kk = in ? lk[rl * LST + idx] : static_cast<uint16_t>(0);
                         const bool keep = in && v > thr;
                         int rank, tot2;
                         group_rank(__ballot(keep), g, c, &rank, &tot2);
                         wave_sync();
                         if (keep) {
-                            lv[rl * CAP + wr + rank] = v;
-                            lk[rl * CAP + wr + rank] = kk;
+                            lv[rl * LST + wr + rank] = v;
+                            lk[rl * LST + wr + rank] = kk;
                         }
                         wave_sync();
                         wr += tot2;
@@ -242,8 +245,8 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                     group_rank(bal[c16], g, c, &rank, &tot2);
                     const int slot = cnt[i] + rank;
                     if (pred && slot < CAP) {
-                        lv[rl * CAP + slot] = raw ? s[c16][i] * a.scale : s[c16][i];
-                        lk[rl * CAP + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
+                        lv[rl * LST + slot] = raw ? s[c16][i] * a.scale : s[c16][i];
+                        lk[rl * LST + slot] = static_cast<uint16_t>(kbase + 16 * c16 + c);
                     }
                     cnt[i] += tot2;
                 }
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
         const int nr = rown[r];
         const int len = rowc[r];
         const float mm = rowm[r];
-        const float* vrow = lv + r * CAP;
+        const float* vrow = lv + r * LST;
         const int nel = len > 0 ? (len + TPR - 1) / TPR : 0;
         auto get = [&](int i) {
             const int idx = sub + TPR * i;
@@ -293,10 +296,10 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
     auto flush = [&](int i, int len, float mm, float ts) {
         const int rl = r0 + 4 * g + i;
         for (int e = 0; e < len; ++e) {
-            const float x = (lv[rl * CAP + e] - mm) - ts;
+            const float x = (lv[rl * LST + e] - mm) - ts;
             if (x > 0.f) {
                 const float p = 0.25f * x * x;
-                const int key = lk[rl * CAP + e];
+                const int key = lk[rl * LST + e];
                 const T* vr = vh + static_cast<size_t>(key) * D + DPL * c;
                 if constexpr (DT == DT_BF16) {
 #pragma unroll
@@ -395,8 +398,8 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                     int rank, tot2;
                     group_rank(__ballot(pred), g, c, &rank, &tot2);
                     if (pred) {
-                        lv[rl * CAP + cnt[i] + rank] = sc;
-                        lk[rl * CAP + cnt[i] + rank] = static_cast<uint16_t>(key);
+                        lv[rl * LST + cnt[i] + rank] = sc;
+                        lk[rl * LST + cnt[i] + rank] = static_cast<uint16_t>(key);
                     }
                     cnt[i] += tot2;
                 }
