@@ -306,7 +306,7 @@ def attention_backward(q, k, v, dout, key_mask=None, causal=False, window=0,
             "dk_kv": dk_kv, "dv_kv": dv_kv}
 
 
-def attention_decode(q, k_cache, v_cache, seqlens, window=0):
+def attention_decode(q, k_cache, v_cache, seqlens, window=0, causal=True):
     """1.5-entmax attention for the newest queries of each sequence against a
     key/value cache (decode time for the causal decoders of "ADASPLASH --
     ROBERTA Benchmark Result", section 3, with the splash window of section
@@ -319,14 +319,18 @@ def attention_decode(q, k_cache, v_cache, seqlens, window=0):
     them the queries' own keys and values, so query i sits at position
     n_b - Lq + i (the queries are the last Lq positions of the sequence).
     Causality allows keys j <= that position; window W > 0 allows keys
-    j > position - W only (W keys including the query's own).  Scores
-    q . k_j / sqrt(d), 1.5-entmax over the allowed keys, O = A V.
+    j > position - W only (W keys including the query's own).  With
+    causal=False every one of the n_b cached keys is allowed to every query
+    (query length below key length without a causal mask; window must be
+    0).  Scores q . k_j / sqrt(d), 1.5-entmax over the allowed keys, O = A V.
 
     Returns (out, tau) shaped like q without / with its last axis; a query
     with no allowed key (its position below 0) gets O = 0 and tau = +inf.
     """
     q, k, v = _as64(q), _as64(k_cache), _as64(v_cache)
     single = q.ndim == 3
+    if window > 0 and not causal:
+        raise ValueError("the splash window is only defined for causal attention")
     if single:
         q = q[:, :, None, :]
     B, H, Lq, d = q.shape
@@ -338,7 +342,7 @@ def attention_decode(q, k_cache, v_cache, seqlens, window=0):
     for b in range(B):
         n = int(min(max(int(sl[b]), 0), S))
         for i in range(Lq):
-            pos = n - Lq + i
+            pos = n - Lq + i if causal else n - 1
             if pos < 0:
                 continue
             lo = max(0, pos - window + 1) if window > 0 else 0

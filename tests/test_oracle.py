@@ -531,3 +531,27 @@ def test_decode_several_queries_are_the_last_rows_of_causal_forward(window, hkv)
         np.testing.assert_allclose(out[b, :, Lq - m:], ref["out"], atol=1e-12)
         np.testing.assert_allclose(tau[b, :, Lq - m:], ref["tau"], atol=1e-12)
         assert np.all(out[b, :, :Lq - m] == 0) and np.all(np.isinf(tau[b, :, :Lq - m]))
+
+
+def test_decode_without_causal_mask_is_full_attention_over_the_cache():
+    # causal=False: every cached key for every query, i.e. the bidirectional
+    # forward of the queries against the n cached keys (rows of a longer
+    # sequence whose keys past n are padding)
+    from oracle import attention_decode, attention_forward
+    rng = np.random.default_rng(9)
+    B, H, S, d, Lq = 2, 2, 30, 8, 4
+    q = rng.normal(size=(B, H, Lq, d))
+    kc = rng.normal(size=(B, H, S, d))
+    vc = rng.normal(size=(B, H, S, d))
+    seqlens = np.array([S, 11])
+    out, tau = attention_decode(q, kc, vc, seqlens, 0, causal=False)
+    for b in range(B):
+        n = seqlens[b]
+        qf = np.zeros((1, H, S, d))
+        qf[0, :, :Lq] = q[b]
+        km = (np.arange(S) < n).astype(np.uint8)[None, :]
+        ref = attention_forward(qf, kc[b:b + 1], vc[b:b + 1], key_mask=km, rows=np.arange(Lq))
+        np.testing.assert_allclose(out[b], ref["out"], atol=1e-12)
+        np.testing.assert_allclose(tau[b], ref["tau"], atol=1e-12)
+    with pytest.raises(ValueError):
+        attention_decode(q, kc, vc, seqlens, 4, causal=False)
