@@ -81,7 +81,7 @@ def load_library(path=LIB_PATH):
     sz = ctypes.c_size_t
     lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.entmax_attn_decode_workspace_size.restype = sz
-    lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_decode.restype = i32
     lib.entmax_attn_status_string.argtypes = [i32]
     lib.entmax_attn_status_string.restype = ctypes.c_char_p
@@ -204,7 +204,7 @@ def decode_workspace_bytes(B, H, H_kv, S, d, window=0, Lq=1):
 
 
 def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=None, workspace=None,
-                       want_tau=True):
+                       want_tau=True, causal=True):
     """Decode-time 1.5-entmax attention: the newest queries of each sequence
     against a key/value cache.
 
@@ -212,7 +212,7 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
     [B, H_kv, S, d] (same dtype, float32 or bfloat16); seqlens [B] int32 on
     the GPU (valid cache positions per sequence, the new tokens' included:
     query i sits at seqlens[b] - Lq + i); window 0 (every earlier key) or
-    W > 0.  workspace: a uint8 GPU tensor of at least
+    W > 0.  causal=False: every query attends all seqlens[b] keys (window 0).  workspace: a uint8 GPU tensor of at least
     ``decode_workspace_bytes`` bytes, or None to allocate one.  Returns
     (out float32 shaped like q, tau float32 shaped like q without d, or None).
     """
@@ -236,7 +236,8 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if tau is None and want_tau:
         tau = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    rc = lib.entmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens.contiguous()), int(window),
+    rc = lib.entmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens.contiguous()),
+                                int(bool(causal)), int(window),
                                 _ptr(out), _ptr(tau), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 B, H, hkv, Lq, S, d, _dtype_code(q), _stream(q))
     _check(lib, rc)

@@ -5,7 +5,8 @@
 //
 // Sequence b holds n_b cached positions, the queries' own included: query i
 // sits at position n_b - Lq + i and may attend keys j <= that position (and
-// j > position - W with a window W > 0).  The rows of a workgroup are the
+// j > position - W with a window W > 0); without the causal mask every one
+// of the n_b keys.  The rows of a workgroup are the
 // (query head, query) pairs that share one key/value head, 16 at a time.
 // The keys any of them may attend, [lo_b, n_b), are split into chunks of 256
 // so that a long cache spreads over many workgroups (a decode step has few
@@ -50,6 +51,7 @@ struct DecArgs {
     float* tau;           // [rows]
     int* row_len;         // [rows] span length of the row's sequence
     int B, H, Hkv, Lq, S, window;
+    int causal;           // 0: every one of the n_b keys for every query (window 0)
     int nch, P;           // chunks of the longest possible span; row pitch of sbuf
     float scale;
 };
@@ -60,7 +62,7 @@ __device__ __forceinline__ void dec_span(const DecArgs& a, int b, int* lo, int* 
     len = len < 0 ? 0 : (len > a.S ? a.S : len);
     *n = len;
     const int first = len - a.Lq;   // position of query 0
-    *lo = (a.window > 0 && first - a.window + 1 > 0) ? first - a.window + 1 : 0;
+    *lo = (a.causal && a.window > 0 && first - a.window + 1 > 0) ? first - a.window + 1 : 0;
 }
 
 // Group z of the rows served by one key/value head: local rows [j0, j1) of
@@ -72,8 +74,10 @@ __device__ __forceinline__ void dec_rows(const DecArgs& a, int z, int* j0, int* 
     *j1 = *j0 + 16 < GL ? *j0 + 16 : GL;
 }
 
-// Key k may be attended by local row j (query j % Lq) of a sequence of n.
+// Key k (< n) may be attended by local row j (query j % Lq) of a sequence
+// of n: causal, query i at n - Lq + i; otherwise every key.
 __device__ __forceinline__ bool dec_allowed(const DecArgs& a, int n, int j, int k) {
+    if (!a.causal) return true;
     const int pos = n - a.Lq + j % a.Lq;
     return k <= pos && (a.window <= 0 || k > pos - a.window);
 }

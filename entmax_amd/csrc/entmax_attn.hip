@@ -219,11 +219,12 @@ DecLayout dec_layout(int B, int H, int Lq, int S, int d, int window) {  // any H
     return l;
 }
 
-int check_decode(int B, int H, int Hkv, int Lq, int S, int d, int dtype, int window) {
+int check_decode(int B, int H, int Hkv, int Lq, int S, int d, int dtype, int causal, int window) {
     if (B <= 0 || H <= 0 || S <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, S must be positive (got %d, %d, %d)", B, H, S);
     if (Lq <= 0 || Lq > S) return fail(ENTMAX_ERR_INVALID_ARG, "Lq = %d outside [1, S = %d]", Lq, S);
     if (Hkv <= 0 || H % Hkv != 0) return fail(ENTMAX_ERR_INVALID_ARG, "H_kv = %d must divide H = %d", Hkv, H);
     if (window < 0) return fail(ENTMAX_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal) return fail(ENTMAX_ERR_INVALID_ARG, "window > 0 requires causal attention");
     if (d != 64 && d != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", d);
     if (dtype != ENTMAX_F32 && dtype != ENTMAX_BF16) return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
     if (S > (1 << 24)) return fail(ENTMAX_ERR_UNSUPPORTED, "S = %d exceeds 2^24", S);
@@ -378,12 +379,12 @@ size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int S, 
     return dec_layout(B, H, Lq, S, d, window).total;
 }
 
-int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, int window,
-                       float* out, float* tau_out, void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
-                       int Lq, int S, int d, int dtype, void* stream) {
+int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, int causal,
+                       int window, float* out, float* tau_out, void* workspace, size_t workspace_bytes, int B, int H,
+                       int Hkv, int Lq, int S, int d, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens, out and workspace must not be NULL");
-    int rc = check_decode(B, H, Hkv, Lq, S, d, dtype, window);
+    int rc = check_decode(B, H, Hkv, Lq, S, d, dtype, causal, window);
     if (rc) return rc;
     const DecLayout l = dec_layout(B, H, Lq, S, d, window);
     if (workspace_bytes < l.total)
@@ -397,7 +398,8 @@ int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, 
     a.part = reinterpret_cast<float*>(ws + l.part);
     a.tau = reinterpret_cast<float*>(ws + l.tau);
     a.row_len = reinterpret_cast<int*>(ws + l.rlen);
-    a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.S = S; a.window = window; a.nch = l.nch; a.P = l.P;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.S = S; a.window = window; a.causal = causal != 0;
+    a.nch = l.nch; a.P = l.P;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) {

@@ -166,9 +166,11 @@ int entmax_bisect_rows_bwd(const float *p, const float *dp, float *ds, int R, in
  *    h reads key/value head h / (H / H_kv)).
  *  - seqlens: [B] int32, DEVICE memory: sequence b holds n_b = seqlens[b]
  *    valid cache positions, the new tokens' own keys and values included
- *    (values outside [0, S] are clamped to it).  Query i sits at position
- *    n_b - Lq + i: it may attend keys j <= n_b - Lq + i, and with window
- *    W > 0 only keys j > n_b - Lq + i - W (W keys including its own).
+ *    (values outside [0, S] are clamped to it).  causal != 0: query i sits
+ *    at position n_b - Lq + i and may attend keys j <= n_b - Lq + i, and
+ *    with window W > 0 only keys j > n_b - Lq + i - W (W keys including its
+ *    own).  causal == 0: every query may attend all n_b keys (window must
+ *    be 0).
  *  - out: [B, H, Lq, d] float32; tau_out: [B, H, Lq] float32 (score units) or
  *    NULL.  A query with no key to attend (n_b - Lq + i < 0) gets O = 0 and
  *    tau = +inf.
@@ -179,14 +181,15 @@ int entmax_bisect_rows_bwd(const float *p, const float *dp, float *ds, int R, in
  *    flight must not share a workspace.
  *  - Supported: d in {64, 128}; dtype ENTMAX_F32 or ENTMAX_BF16;
  *    1 <= Lq <= S <= 2^24; B * H_kv <= 65535.  A too small or misaligned
- *    workspace returns ENTMAX_ERR_INVALID_ARG.
+ *    workspace, or a window without causal, returns ENTMAX_ERR_INVALID_ARG.
  * entmax_attn_decode_workspace_size returns 0 for non-positive sizes or an
  * H_kv that does not divide H.
  */
 size_t entmax_attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int S, int d, int window);
 int entmax_attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
-                       int window, float *out, float *tau_out, void *workspace, size_t workspace_bytes,
-                       int B, int H, int H_kv, int Lq, int S, int d, int dtype, void *stream);
+                       int causal, int window, float *out, float *tau_out, void *workspace,
+                       size_t workspace_bytes, int B, int H, int H_kv, int Lq, int S, int d, int dtype,
+                       void *stream);
 
 const char *entmax_attn_status_string(int status);
 

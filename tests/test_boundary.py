@@ -132,19 +132,23 @@ def test_decode_rejects_bad_arguments(lib):
     assert lib.entmax_attn_decode_workspace_size(2, 4, 3, 1, 64, 64, 0) == 0
     assert lib.entmax_attn_decode_workspace_size(2, 4, 4, 0, 64, 64, 0) == 0
     W = ctypes.c_void_p(256)
-    ok = [P, P, P, P, 0, P, None, W, ws, 2, 4, 4, 1, 64, 64, 1, None]
-    for i in (0, 1, 2, 3, 5, 7):
+    # q, k, v, seqlens, causal, window, out, tau, ws, ws_bytes, B, H, Hkv, Lq, S, d, dtype, stream
+    ok = [P, P, P, P, 1, 0, P, None, W, ws, 2, 4, 4, 1, 64, 64, 1, None]
+    for i in (0, 1, 2, 3, 6, 8):
         a = list(ok)
         a[i] = None
         assert lib.entmax_attn_decode(*a) == 1
-    bad = {8: ws - 1, 11: 3, 4: -1, 12: 0, 14: 96, 15: 7}
+    bad = {9: ws - 1, 12: 3, 5: -1, 13: 0, 15: 96, 16: 7}
     for i, val in bad.items():
         a = list(ok)
         a[i] = val
-        assert lib.entmax_attn_decode(*a) == (2 if i in (14, 15) else 1), i
+        assert lib.entmax_attn_decode(*a) == (2 if i in (15, 16) else 1), i
     a = list(ok)
-    a[12] = 65           # Lq above S
+    a[13] = 65           # Lq above S
     assert lib.entmax_attn_decode(*a) == 1
     a = list(ok)
-    a[7] = ctypes.c_void_p(272)      # not 256-byte aligned
+    a[4], a[5] = 0, 8    # a window without causal
+    assert lib.entmax_attn_decode(*a) == 1
+    a = list(ok)
+    a[8] = ctypes.c_void_p(272)      # not 256-byte aligned
     assert lib.entmax_attn_decode(*a) == 1

@@ -28,8 +28,8 @@ def _inputs(B, H, Hkv, S, d, dtype, gain, seed, seqlens):
     return q, k, v, torch.tensor(seqlens, dtype=torch.int32)
 
 
-def _check(q, k, v, sl, window, dtype, out, tau):
-    ref_o, ref_t = attention_decode(q, k, v, sl.numpy(), window)
+def _check(q, k, v, sl, window, dtype, out, tau, causal=True):
+    ref_o, ref_t = attention_decode(q, k, v, sl.numpy(), window, causal=causal)
     o, t = out.cpu().numpy(), tau.cpu().numpy()
     assert np.array_equal(np.isinf(t), np.isinf(ref_t))
     fin = np.isfinite(ref_t)
@@ -165,3 +165,21 @@ def test_decode_bench_workloads(name):
                                   w["window"])
     torch.cuda.synchronize()
     _check(inp["q"], inp["k"], inp["v"], inp["seqlens"], w["window"], w["dtype"], out, tau)
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv,Lq,S", [("f32", 64, 4, 2, 1, 200), ("bf16", 128, 8, 2, 5, 700),
+                                              ("bf16", 64, 4, 4, 9, 3000)])
+def test_decode_without_causal_mask(dtype, d, H, Hkv, Lq, S):
+    # every cached key for every query (query length below key length, no mask)
+    from entmax_amd import entmax_attn_decode
+    seqlens = [S, 3, S // 2]
+    gen = torch.Generator().manual_seed(S + 7 * Lq)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn((3, H, Lq, d), generator=gen).to(dt)
+    k = torch.randn((3, Hkv, S, d), generator=gen).to(dt)
+    v = torch.randn((3, Hkv, S, d), generator=gen).to(dt)
+    sl = torch.tensor(seqlens, dtype=torch.int32)
+    log(f"[decode] no causal mask {dtype} d{d} H{H} Hkv{Hkv} Lq{Lq} S{S}")
+    out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, causal=False)
+    torch.cuda.synchronize()
+    _check(q, k, v, sl, 0, dtype, out, tau, causal=False)
