@@ -183,3 +183,18 @@ def test_decode_without_causal_mask(dtype, d, H, Hkv, Lq, S):
     out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0, causal=False)
     torch.cuda.synchronize()
     _check(q, k, v, sl, 0, dtype, out, tau, causal=False)
+
+
+def test_decode_and_rows_are_deterministic():
+    # no atomics and fixed summation orders: repeated calls give the same bits
+    from entmax_amd import entmax15_rows, entmax_attn_decode
+    q, k, v, sl = _inputs(2, 32, 8, 8192, 128, "bf16", 2.0, seed=11, seqlens=[8192, 4000])
+    q, k, v, sl = q.cuda(), k.cuda(), v.cuda(), sl.cuda()
+    o1, t1 = entmax_attn_decode(q, k, v, sl, 0)
+    o2, t2 = entmax_attn_decode(q, k, v, sl, 0)
+    s = torch.randn((40, 5000), generator=torch.Generator().manual_seed(3)).cuda()
+    p1, u1 = entmax15_rows(s)
+    p2, u2 = entmax15_rows(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(t1, t2)
+    assert torch.equal(p1, p2) and torch.equal(u1, u2)
