@@ -152,3 +152,20 @@ def test_decode_rejects_bad_arguments(lib):
     a = list(ok)
     a[8] = ctypes.c_void_p(272)      # not 256-byte aligned
     assert lib.entmax_attn_decode(*a) == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback of any kind: without the built library every call raises
+    import subprocess
+    import sys
+    code = (
+        "import entmax_amd._binding as b\n"
+        "b._lib = None\n"
+        "b.LIB_PATH = '" + str(tmp_path / "absent.so") + "'\n"
+        "try:\n"
+        "    b.load_library(b.LIB_PATH)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised', e)\n"
+    )
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "raised" in out.stdout and "not built" in out.stdout
