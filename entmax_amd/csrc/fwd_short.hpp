@@ -258,17 +258,28 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
     const int klo_i = a.window > 0 ? qrow - a.window : -1;
     auto tiles = [&](auto causal_tag) {
         constexpr bool CAUSAL = decltype(causal_tag)::value;
+        unsigned cm = kbits;
+        if constexpr (CAUSAL) {
+            // this lane's keys increase with the slot 4t + i, so the keys in
+            // (klo_i, khi_i] are one run of slots: [slots with key <= klo_i,
+            // slots with key <= khi_i)
+            auto cnt_le = [&](int bound) {
+                const int r = bound - kbase - 4 * g;
+                const int c = r < 0 ? 0 : 4 * (r >> 4) + min((r & 15) + 1, 4);
+                return c < 32 ? c : 32;
+            };
+            const int chi = cnt_le(khi_i), clo = a.window > 0 ? cnt_le(klo_i) : 0;
+            const unsigned mhi = chi >= 32 ? 0xFFFFFFFFu : (1u << chi) - 1u;
+            const unsigned mlo = clo >= 32 ? 0xFFFFFFFFu : (1u << clo) - 1u;
+            cm = kbits & mhi & ~mlo;
+            nl = static_cast<float>(__popc(cm));   // every allowed slot lies in [t0, t1)
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if (t < t0 || t >= t1) continue;    // uniform: outside the wave's keys (-inf)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (CAUSAL) {
-                    const int key = kbase + 16 * t + 4 * g + i;
-                    const bool ok = (((kbits >> (4 * t + i)) & 1u) != 0u) & (key <= khi_i) & (key > klo_i);
-                    nl += ok ? 1.f : 0.f;
-                    sv[t][i] = ok ? sv[t][i] : -kInf;
-                }
+                if constexpr (CAUSAL) sv[t][i] = ((cm >> (4 * t + i)) & 1u) != 0u ? sv[t][i] : -kInf;
                 mraw = fmaxf(mraw, sv[t][i]);
             }
         }
