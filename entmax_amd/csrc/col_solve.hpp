@@ -291,7 +291,15 @@ __device__ __forceinline__ float col_solve(const f32x4 (&sv)[NT], int t0, int t1
 template <int KMAX>
 __device__ __forceinline__ float col_finish(float* col, int len, ColState& s) {
     if (s.it >= kIters) return 0.5f * (s.lo + s.hi);
-    if (KMAX > 16 && __any(len > 16)) col_stage<(KMAX > 16 ? 32 : 16), 3>(col, len, s);
+    if (KMAX > 16 && __any(len > 16)) {
+        col_stage<(KMAX > 16 ? 32 : 16), 3>(col, len, s);
+        // a dense row can keep more than 16 band entries in a lane after
+        // three steps; the exact finish below holds 16, so step on
+        while (__any(len > 16)) {
+            if (s.it >= kIters) return 0.5f * (s.lo + s.hi);
+            col_stage<(KMAX > 16 ? 32 : 16), 3>(col, len, s);
+        }
+    }
     else if (__any(len > 8)) col_stage<16, 3>(col, len, s);
     else if (__any(len > 4)) col_stage<8, 3>(col, len, s);
     else if (__any(len > 2)) col_stage<4, 2>(col, len, s);

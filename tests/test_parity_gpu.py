@@ -205,3 +205,15 @@ def test_grouped_query_backward(dtype):
     # dk, dv of a shared head collect the atomics of all its query heads
     inp = _grouped(random_inputs(2, 4, 90, 64, dtype, seed=33, qk_gain=1.5, key_lengths=[90, 61]), 2)
     check_backward(inp, label="gqa")
+
+
+@pytest.mark.parametrize("L,causal", [(128, False), (128, True), (199, True), (600, False)])
+def test_dense_rows_with_one_high_key(L, causal):
+    # nearly every key in the support and one key well above the rest: after
+    # the first bisection stage a lane can still hold more than 16 band
+    # entries, which the exact finish must not truncate
+    inp = random_inputs(1, 2, L, 64, "f32", seed=L + int(causal), qk_gain=0.3)
+    qm = inp["q"][0, 0].mean(0)
+    inp["k"][0, :, L // 2] += 4.0 * qm / (qm.norm() ** 2)
+    inp["causal"] = causal
+    check_forward(inp, label=f"dense + one high key L{L} causal={causal}")
