@@ -162,3 +162,28 @@ def test_random_rows(case):
     err = float(np.abs(dsr[keep] - ref[keep]).max()) / max(1.0, float(np.abs(ref[keep]).max())) if keep.any() else 0.0
     log(f"[rows]   scaled bwd err {err:.3g} over {int(keep.sum())} rows")
     assert err <= TOL["f32"]
+
+
+def _bwd_cases(n=10, seed=555):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        causal = bool(rng.random() < 0.5)
+        out.append(dict(B=1, H=int(rng.integers(1, 3)), L=int(rng.integers(301, 2600)), d=int(rng.choice([64, 128])),
+                        dtype=dtype, causal=causal, window=int(rng.choice([0, 32])) if causal else 0,
+                        gain=float(rng.choice([0.3, 1.0] if dtype == "f32" else [0.3, 1.0, 2.0])), seed=seed + i))
+    return out
+
+
+BWD_CASES = _bwd_cases()
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"b{i}" for i in range(len(BWD_CASES))])
+def test_random_backward_long(case):
+    # the backward on spans the short cases above do not reach (dense and
+    # sparse supports, candidate lists that overflow)
+    c = case
+    inp = random_inputs(c["B"], c["H"], c["L"], c["d"], c["dtype"], seed=c["seed"], qk_gain=c["gain"])
+    inp["causal"], inp["window"] = c["causal"], c["window"]
+    check_backward(inp, heads=[(0, c["H"] - 1)], label=f"random bwd {c}")
