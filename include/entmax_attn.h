@@ -11,7 +11,8 @@
  * AdaSplash Attention" model card, Mathematical Formulation 2), n_i being
  * the number of keys row i may attend.
  *
- * Conventions shared by every entry point:
+ * Conventions shared by every entry point (the row-wise and decode-time
+ * calls further down state their own shapes, masks and options):
  *  - All tensor pointers are DEVICE memory, allocated and owned by the
  *    caller, contiguous, row-major.  q, k, v, dout: [B, H, L, d] of `dtype`;
  *    out, dq, dk, dv: [B, H, L, d] float32; tau: [B, H, L] float32;
@@ -28,8 +29,9 @@
  *    Disallowed keys are removed from the simplex (p = 0 exactly).
  *  - A query row with no allowed key gets O = 0 and tau = +inf.  Padded
  *    query rows are computed like any other row.
- *  - Inputs must be finite (not checked).  Scale is fixed to 1/sqrt(d),
- *    alpha to 1.5 and the bisection to 25 steps.
+ *  - Inputs must be finite (not checked).  Scale is fixed to 1/sqrt(d) and
+ *    the bisection to 25 steps; alpha is 1.5 except in the row-wise
+ *    entmax_bisect_rows_* calls, which take it.
  *  - Supported: d in {64, 128}; dtype ENTMAX_F32 or ENTMAX_BF16;
  *    1 <= L <= 65536.  Other values return ENTMAX_ERR_UNSUPPORTED.
  *  - Errors: integer status codes; nothing is launched when the arguments
