@@ -20,8 +20,9 @@
 //      dQ_i = scale (X - c_i Y) without another pass; then every entry adds
 //      scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.
 // A row whose support outgrows its list is finished by two more passes over
-// the keys (all waves take part, only those rows do work): one for dp, the
-// sums, X and Y, one for the atomics once c_i is known.
+// the keys (all waves take part, only those rows do work): one for dp and the
+// sums, one for the atomics and dQ_i = scale sum_j dS_ij K_j once c_i is
+// known (for a long support the difference X - c_i Y would cost digits).
 #pragma once
 
 #include "chunk_stream.hpp"
@@ -383,23 +384,20 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
                         if (pass == 0) {
                             sw += w[j];
                             swdp = fmaf(w[j], dp[j], swdp);
-                            const float wdp = w[j] * dp[j];
-#pragma unroll
-                            for (int d = 0; d < DPL; ++d) {
-                                X[d] = fmaf(wdp, kr[j][d], X[d]);
-                                Y[d] = fmaf(w[j], kr[j][d], Y[d]);
-                            }
                         } else if (e0 + j < n) {
                             scatter(key[j], w[j], dp[j], cc);
+                            // dQ directly from dS: a long support would lose
+                            // digits in the difference X - c Y
+                            const float ds = w[j] * (dp[j] - cc);
+#pragma unroll
+                            for (int d = 0; d < DPL; ++d) X[d] = fmaf(ds, kr[j][d], X[d]);
                         }
                     }
                 }
                 wave_sync();
             });
-            if (pass == 0) {
-                cc = sw > 0.f ? swdp / sw : 0.f;
-                if (ovf[i]) store_dq(i, cc, X, Y);
-            }
+            if (pass == 0) cc = sw > 0.f ? swdp / sw : 0.f;
+            else if (ovf[i]) store_dq(i, 0.f, X, Y);   // Y stays zero: dQ = scale X
         }
     }
 }

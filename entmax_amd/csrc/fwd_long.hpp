@@ -202,8 +202,8 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     //     S2_j + 2 (e_j - e_k) S1_j + (e_j - e_k)^2 N_j,
     // and the three steps walk the tree of these midpoints.  Entries at or
     // below max(lo, lb) go to a dump cell (9).  The fixed-point rounding
-    // (2^-23 of a cell width, or absolute for cell 8) is of the order of the
-    // float rounding of the sums themselves.
+    // (to nearest, 2^-23 of a cell width, or absolute for cell 8) is of the
+    // order of the float rounding of the sums themselves.
     constexpr int kCells = 10;
     unsigned* hist = reinterpret_cast<unsigned*>(lists) + wv * (kCells * 3 * kWave) + lane;   // [cell][N, S1, S2] at stride kWave
     static_assert(4 * kCells * 3 * kWave * 4 <= C::vl_bytes, "histograms fit the list region");
@@ -250,11 +250,15 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                     // = (u - 8) w in [0, 1] in cell 8; the dump cell's lies
                     // in [0, 1) and is never read
                     const float r = ci == 8 ? (u - 8.f) * w : __builtin_amdgcn_fractf(u);
+                    // rounded to nearest: truncation would bias every term
+                    // the same way, and over hundreds of entries per cell the
+                    // bias would move g at the edges by more than the float
+                    // rounding of the sums
                     const float rk = r * kFix;
                     unsigned* h = hist + ci * (3 * kWave);
                     lds_add(h, 1u);
-                    lds_add(h + kWave, static_cast<unsigned>(rk));
-                    lds_add(h + 2 * kWave, static_cast<unsigned>(r * rk));
+                    lds_add(h + kWave, static_cast<unsigned>(rk + 0.5f));
+                    lds_add(h + 2 * kWave, static_cast<unsigned>(fmaf(r, rk, 0.5f)));
                 }
             }
         });
