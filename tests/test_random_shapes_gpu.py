@@ -151,17 +151,25 @@ def test_random_rows(case):
     assert float(np.abs(p.cpu().numpy()[rows] - p_ref).max()) <= tol
     fin = np.isfinite(t_ref)
     assert float(np.abs(tau.cpu().numpy()[rows][fin] - t_ref[fin]).max()) <= tol
-    ref = entmax_alpha_backward(s64, dp[rows].double().numpy(), c["alpha"], ok)
-    # at alpha = 2 the weight p^(2 - alpha) jumps from 0 to 1 at the support
-    # boundary, so a row with an entry within rounding of tau has two valid
-    # gradients; such rows are left out of the comparison
-    keep = np.ones(len(rows), dtype=bool)
-    if c["alpha"] == 2.0:
-        keep = ~(np.abs(s64 - np.where(fin, t_ref, 0.0)[:, None]) <= 1e-6).any(axis=1)
-    dsr = ds.cpu().numpy()[rows]
-    err = float(np.abs(dsr[keep] - ref[keep]).max()) / max(1.0, float(np.abs(ref[keep]).max())) if keep.any() else 0.0
-    log(f"[rows]   scaled bwd err {err:.3g} over {int(keep.sum())} rows")
+    dp64 = dp[rows].double().numpy()
+    ref = entmax_alpha_backward(s64, dp64, c["alpha"], ok)
+    # the backward entry point on the oracle's p (rounded to float32): its
+    # own parity, for every alpha
+    ds_o = entmax_bisect_rows_bwd(torch.from_numpy(p_ref).float().cuda(), dp[rows].contiguous().cuda(), c["alpha"])
+    err = float(np.abs(ds_o.cpu().numpy() - ref).max()) / max(1.0, float(np.abs(ref).max()))
+    log(f"[rows]   scaled bwd err on the oracle's p {err:.3g}")
     assert err <= TOL["f32"]
+    # the chain forward -> backward where the weight p^(2 - alpha) =
+    # [(alpha - 1)(s - tau)]^((2 - alpha)/(alpha - 1)) is Lipschitz in tau
+    # (exponent >= 1, alpha <= 1.5).  Above 1.5 its slope is unbounded at
+    # the support boundary: a float32-sized error in tau moves the weight of
+    # an entry just above tau by far more than the tolerance (and at alpha = 2
+    # the weight jumps from 0 to 1), so the chain is ill-conditioned there
+    if c["alpha"] <= 1.5:
+        dsr = ds.cpu().numpy()[rows]
+        err = float(np.abs(dsr - ref).max()) / max(1.0, float(np.abs(ref).max()))
+        log(f"[rows]   scaled bwd err after the kernel's forward {err:.3g}")
+        assert err <= TOL["f32"]
 
 
 def _bwd_cases(n=10, seed=555):
