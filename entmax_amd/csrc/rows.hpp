@@ -92,6 +92,66 @@ __device__ __forceinline__ float bracket_hi(float n, float am1) {
     return GEN ? -__builtin_amdgcn_exp2f(-am1 * __builtin_amdgcn_logf(n)) : -__builtin_amdgcn_rsqf(n);
 }
 
+// Exact root t* of g(t) = sum [x - t]_+^2 = 1 (alpha = 1.5) from the
+// candidates cs of this thread (every entry of the row above lo, where
+// g(lo) >= 1 and t* lies in (lo, hi]).  Newton steps from the left (g is
+// convex and decreasing there, so the iterates stay at or below t*) and, at
+// each iterate t, the closed form of "ADASPLASH -- ROBERTA Benchmark
+// Result", section 2.2 Theorem 1, on the entries above t: the smaller root
+// tc of sum (x - t - e)^2 = 1, accepted when no entry lies in (t, tc] (then
+// every entry above tc is in the support and tc = t*).  Returns whether
+// every row of the wave was accepted within the round cap (uniform).
+template <int K, class RSum>
+__device__ __forceinline__ bool exact_root(const float (&cs)[K], float lo, float hi, RSum rsum, float& ts) {
+    float t = lo, res = lo;
+    bool done = false;
+    for (int r = 0; r < 8; ++r) {
+        float s1 = 0.f, s2 = 0.f, c = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float y = relu1(cs[k] - t);
+            s1 += y;
+            s2 = fmaf(y, y, s2);
+            c += cs[k] > t ? 1.f : 0.f;
+        }
+        s1 = rsum(s1);
+        s2 = rsum(s2);
+        c = rsum(c);
+        // e = (s1 - sqrt(D)) / c = (s2 - 1) / (s1 + sqrt(D)), D = s1^2 - c (s2 - 1);
+        // s1 > 0: the row maximum (x = 0) lies above every t <= hi < 0
+        const float q = s2 - 1.f;
+        const float disc = fmaf(s1, s1, -c * q);
+        const float tc = fmaf(q, __builtin_amdgcn_rcpf(s1 + __builtin_amdgcn_sqrtf(fmaxf(disc, 0.f))), t);
+        float inb = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) inb += (cs[k] > t && cs[k] <= tc) ? 1.f : 0.f;
+        inb = rsum(inb);
+        const bool ok = disc >= 0.f && inb == 0.f && tc <= hi;
+        res = (!done && ok) ? tc : res;
+        done = done || ok;
+        if (!__any(!done)) break;
+        // Newton step from the left: g(t) = s2, g'(t) = -2 s1
+        const float tn = fmaf(0.5f * q, __builtin_amdgcn_rcpf(s1), t);
+        t = fmaxf(t, fminf(tn, hi));
+    }
+    ts = res;
+    return !__any(!done);
+}
+
+// The midpoint that the remaining kIters - it bisection steps on [lo, hi]
+// end at when the root is ts: the centre of the dyadic cell (lo + j w,
+// lo + (j + 1) w] holding ts (g(mid) = 1 moves the upper end).  An error of
+// one cell (2^-25 of the bracket) is below the rounding of g itself.
+__device__ __forceinline__ float dyadic_mid(float lo, float hi, int it, float ts) {
+    const int r = kIters - it;
+    if (r <= 0 || !(hi > lo)) return 0.5f * (lo + hi);
+    const float cells = ldexpf(1.f, r);
+    const float w = (hi - lo) * ldexpf(1.f, -r);   // exact: power-of-two scaling
+    float j = ceilf((ts - lo) * (cells / (hi - lo))) - 1.f;
+    j = fminf(fmaxf(j, 0.f), cells - 1.f);
+    return fmaf(j + 0.5f, w, lo);
+}
+
 // 25 bisection steps on t for a row held in registers, NV quads per thread:
 // x = (alpha - 1)(s - max), -inf where not allowed, n >= 1 allowed entries.
 // g(mid) = sum [x - mid]_+^(1/(alpha-1)) (each term at most 1: x <= 0 and
@@ -99,7 +159,11 @@ __device__ __forceinline__ float bracket_hi(float n, float am1) {
 // Entries at or below the lower end never count again (every later midpoint
 // lies above it): after the first kFirst steps, when no thread holds more
 // than kCand entries above the lower end, the remaining steps run over those
-// slots.  pw: y -> y^(1/(alpha-1)); rsum: sum over the row's TPR threads,
+// slots (with a wave or less per row, two more steps and a second
+// compaction when no thread holds more than 2 kCand).  At alpha = 1.5 with
+// a wave or less per row the remaining steps are not taken one by one:
+// their end point follows from the exact root (exact_root, dyadic_mid), with
+// the steps as the fallback.  pw: y -> y^(1/(alpha-1)); rsum: sum over the row's TPR threads,
 // bitwise identical in all of them.  TPR <= 64: the threads of a wave take
 // the same path (several rows per wave with TPR < 64).
 template <int NV, bool GEN, int TPR, class PW, class RSum>
@@ -123,21 +187,54 @@ __device__ __forceinline__ float bisect_regs(const f32x4 (&xs)[NV], float n, flo
     for (; it < kFirst; ++it) step(full);
     float cs[kCand];
     int nc = 0;
+    auto compact = [&]() {
+        nc = 0;
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) cs[k] = -kInf;
+        for (int k = 0; k < kCand; ++k) cs[k] = -kInf;
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
+        for (int q = 0; q < NV; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = xs[q][i];
-            const bool cand = x > lo;
+            for (int i = 0; i < 4; ++i) {
+                const float x = xs[q][i];
+                const bool cand = x > lo;
 #pragma unroll
-            for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
-            nc += cand ? 1 : 0;
-        }
+                for (int k = 0; k < kCand; ++k) cs[k] = (cand & (nc == k)) ? x : cs[k];
+                nc += cand ? 1 : 0;
+            }
+    };
+    compact();
     bool few;
-    if constexpr (TPR <= kWave) few = !__any(nc > kCand);   // over the wave (all its rows)
-    else few = !__syncthreads_or(nc > kCand);
+    if constexpr (TPR <= kWave) {
+        few = !__any(nc > kCand);   // over the wave (all its rows)
+        // a thread with a few more candidates: two more steps over every
+        // entry (about a quarter of the band is left), then compact again
+        if (!few && !__any(nc > 2 * kCand)) {
+            step(full);
+            step(full);
+            it += 2;
+            compact();
+            few = !__any(nc > kCand);
+        }
+        if constexpr (!GEN) {
+            // alpha = 1.5: the remaining steps follow from the exact root,
+            // found over the candidates or, for a dense row, over every entry
+            float ts;
+            bool ok;
+            if (few) {
+                ok = exact_root(cs, lo, hi, rsum, ts);
+            } else {
+                float xa[4 * NV];
+#pragma unroll
+                for (int q = 0; q < NV; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xa[4 * q + i] = xs[q][i];
+                ok = exact_root(xa, lo, hi, rsum, ts);
+            }
+            if (ok) return dyadic_mid(lo, hi, it, ts);
+        }
+    } else {
+        few = !__syncthreads_or(nc > kCand);
+    }
     if constexpr (TPR == kThreads) {
         // a workgroup per row: when the whole row holds at most 64
         // candidates, wave 0 takes the remaining steps alone, without a
