@@ -389,13 +389,16 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
         }
     }
 
+    // O is written once and never read back here: non-temporal stores stream
+    // it out instead of leaving dirty lines in L2 for the end of the kernel
+    // (the encoder workload, one generation of workgroups: 14.4 -> 12.3 us)
     float* outh = a.out + head_off;
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = q0 + 16 * wv + 4 * g + i;
-            if (row < L) outh[static_cast<size_t>(row) * D + 16 * ct + c] = o[ct][i];
+            if (row < L) __builtin_nontemporal_store(o[ct][i], &outh[static_cast<size_t>(row) * D + 16 * ct + c]);
         }
 }
 
