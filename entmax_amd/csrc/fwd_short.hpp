@@ -391,15 +391,33 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
 
     // O is written once and never read back here: non-temporal stores stream
     // it out instead of leaving dirty lines in L2 for the end of the kernel
-    // (the encoder workload, one generation of workgroups: 14.4 -> 12.3 us)
+    // (the encoder workload, one generation of workgroups: 14.4 -> 12.3 us).
+    // Without L2 to merge them, stores of 64-byte row pieces (a lane group's
+    // 16 columns) would reach HBM as partial lines, so each 64-column half
+    // of the wave's 16 rows is restaged through LDS (row pitch 68 floats:
+    // the two lane groups of a half-wave write disjoint banks) and every
+    // store covers four whole 256-byte row pieces.
+    __syncthreads();   // every wave is done with V and the scratch: LDS is free
+    constexpr int OP = 68;
+    static_assert(C::lds_bytes >= sizeof(float) * 4 * 16 * OP, "O staging fits");
+    float* os = lds + wv * (16 * OP);
     float* outh = a.out + head_off;
 #pragma unroll
-    for (int ct = 0; ct < D / 16; ++ct)
+    for (int h = 0; h < D / 64; ++h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = q0 + 16 * wv + 4 * g + i;
-            if (row < L) __builtin_nontemporal_store(o[ct][i], &outh[static_cast<size_t>(row) * D + 16 * ct + c]);
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) os[(4 * g + i) * OP + 16 * cc + c] = o[4 * h + cc][i];
+        wave_sync();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int rl = 4 * k + lane / 16, col = 4 * (lane % 16);   // row of the wave, first column
+            const f32x4 v = *reinterpret_cast<const f32x4*>(os + rl * OP + col);
+            const int row = q0 + 16 * wv + rl;
+            if (row < L) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(outh + static_cast<size_t>(row) * D + 64 * h + col));
         }
+        wave_sync();   // reads done before the next half overwrites the rows
+    }
 }
 
 }  // namespace ea
