@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 
@@ -260,11 +261,22 @@ int check_rows(int R, int L) {
     return ENTMAX_OK;
 }
 
+// True when a non-null pointer of the list is not a multiple of `al` bytes:
+// the kernels read and write rows with 16-byte vector accesses, and floats
+// (tau, probs) and int32 lengths with 4-byte ones.
+static bool misaligned(std::initializer_list<const void*> ps, uintptr_t al) {
+    for (const void* p : ps)
+        if (p != nullptr && reinterpret_cast<uintptr_t>(p) % al != 0) return true;
+    return false;
+}
+
 extern "C" {
 
 int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
                         float* out, float* tau_out, int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !v || !out) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+    if (misaligned({q, k, v, out}, 16) || misaligned({tau_out}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned, tau_out 4-byte aligned");
     int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::FwdArgs a;
@@ -283,6 +295,8 @@ int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8
 int entmax_attn_probs_gqa(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
                           const float* tau, float* probs, int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !tau || !probs) return fail(ENTMAX_ERR_INVALID_ARG, "q, k, tau and probs must not be NULL");
+    if (misaligned({q, k}, 16) || misaligned({tau, probs}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "q and k must be 16-byte aligned, tau and probs 4-byte aligned");
     int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::ProbsArgs a;
@@ -310,6 +324,8 @@ int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8
                         int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
     if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv)
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk and dv must not be NULL");
+    if (misaligned({q, k, v, dout, dq, dk, dv}, 16) || misaligned({tau}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned, tau 4-byte aligned");
     int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
     ea::BwdArgs a;
@@ -342,6 +358,8 @@ int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int
 int entmax_bisect_rows_fwd(const void* scores, const uint8_t* mask, float* p, float* tau, int R, int L, float alpha,
                            int dtype, void* stream) {
     if (!scores || !p) return fail(ENTMAX_ERR_INVALID_ARG, "scores and p must not be NULL");
+    if (misaligned({scores, mask, p}, 16) || misaligned({tau}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "scores, mask and p must be 16-byte aligned, tau 4-byte aligned");
     if (!(alpha > 1.f && alpha <= 2.f)) return fail(ENTMAX_ERR_INVALID_ARG, "alpha = %g outside (1, 2]", alpha);
     int rc = check_rows(R, L);
     if (rc) return rc;
@@ -356,6 +374,7 @@ int entmax_bisect_rows_fwd(const void* scores, const uint8_t* mask, float* p, fl
 
 int entmax_bisect_rows_bwd(const float* p, const float* dp, float* ds, int R, int L, float alpha, void* stream) {
     if (!p || !dp || !ds) return fail(ENTMAX_ERR_INVALID_ARG, "p, dp and ds must not be NULL");
+    if (misaligned({p, dp, ds}, 16)) return fail(ENTMAX_ERR_INVALID_ARG, "p, dp and ds must be 16-byte aligned");
     if (!(alpha > 1.f && alpha <= 2.f)) return fail(ENTMAX_ERR_INVALID_ARG, "alpha = %g outside (1, 2]", alpha);
     int rc = check_rows(R, L);
     if (rc) return rc;
@@ -384,6 +403,8 @@ int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, 
                        int Hkv, int Lq, int S, int d, int dtype, void* stream) {
     if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens, out and workspace must not be NULL");
+    if (misaligned({q, k_cache, v_cache, out}, 16) || misaligned({seqlens, tau_out}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned, seqlens and tau_out 4-byte aligned");
     int rc = check_decode(B, H, Hkv, Lq, S, d, dtype, causal, window);
     if (rc) return rc;
     const DecLayout l = dec_layout(B, H, Lq, S, d, window);

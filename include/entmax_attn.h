@@ -17,7 +17,9 @@
  *    caller, contiguous, row-major.  q, k, v, dout: [B, H, L, d] of `dtype`;
  *    out, dq, dk, dv: [B, H, L, d] float32; tau: [B, H, L] float32;
  *    key_mask: [B, L] uint8 (nonzero = the key may be attended), or NULL for
- *    "all keys valid".  Pointers to [.., d] rows must be 16-byte aligned.
+ *    "all keys valid".  Pointers to [.., d] rows must be 16-byte aligned,
+ *    tau, probs and seqlens 4-byte aligned; a misaligned pointer returns
+ *    ENTMAX_ERR_INVALID_ARG before anything is launched.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is only enqueued; nothing synchronises.  The library allocates and
  *    frees no memory and keeps no state between calls; calls on different

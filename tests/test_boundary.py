@@ -154,6 +154,32 @@ def test_decode_rejects_bad_arguments(lib):
     assert lib.entmax_attn_decode(*a) == 1
 
 
+def test_entry_points_reject_misaligned_pointers(lib):
+    # rows are read and written with 16-byte vector accesses; tau and probs
+    # with 4-byte ones: a misaligned pointer is refused before any launch
+    M16, M4 = ctypes.c_void_p(24), ctypes.c_void_p(18)
+    for kw in ({"q": M16}, {"k": M16}, {"v": M16}, {"out": M16}, {"tau": M4}):
+        assert _fwd(lib, **kw) == 1, kw
+    assert b"aligned" in lib.entmax_attn_last_error()
+    args = [P, P, P, None, 0, 0, P, P, P, P, P, 1, 1, 8, 64, 1, None]
+    for i, bad in ((0, M16), (1, M16), (2, M16), (6, M4), (7, M16), (8, M16), (9, M16), (10, M16)):
+        a = list(args)
+        a[i] = bad
+        assert lib.entmax_attn_bwd(*a) == 1, i
+    assert lib.entmax_attn_probs(M16, P, None, 0, 0, P, P, 1, 1, 8, 64, 1, None) == 1
+    assert lib.entmax_attn_probs(P, P, None, 0, 0, P, M4, 1, 1, 8, 64, 1, None) == 1
+    assert lib.entmax_bisect_rows_fwd(M16, None, P, None, 4, 8, 1.5, 0, None) == 1
+    assert lib.entmax_bisect_rows_fwd(P, M16, P, None, 4, 8, 1.5, 0, None) == 1
+    assert lib.entmax_bisect_rows_fwd(P, None, P, M4, 4, 8, 1.5, 0, None) == 1
+    assert lib.entmax_bisect_rows_bwd(P, P, M16, 4, 8, 1.5, None) == 1
+    ws = lib.entmax_attn_decode_workspace_size(2, 4, 4, 1, 64, 64, 0)
+    ok = [P, P, P, P, 1, 0, P, None, ctypes.c_void_p(256), ws, 2, 4, 4, 1, 64, 64, 1, None]
+    for i, bad in ((0, M16), (1, M16), (2, M16), (3, M4), (6, M16), (7, M4)):
+        a = list(ok)
+        a[i] = bad
+        assert lib.entmax_attn_decode(*a) == 1, i
+
+
 def test_missing_library_fails_loudly(tmp_path):
     # no fallback of any kind: without the built library every call raises
     import subprocess
