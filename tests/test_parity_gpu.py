@@ -126,6 +126,19 @@ def test_stream_path_masked_f32():
     check_forward(inp, label="stream f32", check_probs=False)
 
 
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, False), ("f32", 128, True)])
+def test_maximum_length(dtype, d, causal):
+    # L = 65536, the largest length the entry points accept (the candidate
+    # lists hold key indices as 16-bit integers): rows at both ends and in
+    # the middle; the last causal row attends every key, 65535 included
+    # float32 keeps scores of order one (the 1e-5 bar is its limit there);
+    # its rows then overflow the candidate lists and take the fallback
+    inp = random_inputs(1, 1, 65536, d, dtype, seed=65536 + d, qk_gain=1.5 if dtype == "bf16" else 1.0)
+    inp["causal"] = causal
+    rows = np.array([0, 1, 2047, 32768, 65534, 65535])
+    check_forward(inp, rows=rows, label=f"max length {dtype} d{d}", check_probs=False)
+
+
 def test_stream_overflow_fallback():
     # near-uniform rows: every key is a candidate, far more than a list holds
     inp = random_inputs(1, 2, 1300, 64, "bf16", seed=9, qk_gain=0.2)
