@@ -139,6 +139,40 @@ def test_maximum_length(dtype, d, causal):
     check_forward(inp, rows=rows, label=f"max length {dtype} d{d}", check_probs=False)
 
 
+def test_backward_maximum_length():
+    # L = 65536 backward.  The full oracle gradient needs every (query, key)
+    # pair; what any size allows instead:
+    #  * dQ_i depends on row i alone: the oracle's row backward (alpha = 1.5)
+    #    on the scores of sampled rows, dp_i = V dO_i, dQ_i = d^-1/2 dS_i K;
+    #  * sum_j dK_j = 0 (every row of dS sums to zero: sum w (dp - c) = 0);
+    #  * sum_j dV_j = sum_i dO_i (every row of p sums to one).
+    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd
+    from oracle import entmax_alpha_backward
+    from tests.parity_util import scores64, to_gpu
+    L, d = 65536, 64
+    inp = random_inputs(1, 1, L, d, "bf16", seed=77, qk_gain=1.5)
+    g = to_gpu(inp)
+    log("[parity] bwd max length bf16 d64 L65536")
+    _, tau = entmax_attn_fwd(g["q"], g["k"], g["v"])
+    dq, dk, dv = entmax_attn_bwd(g["q"], g["k"], g["v"], tau, g["dout"])
+    torch.cuda.synchronize()
+    k64 = inp["k"][0, 0].double().numpy()
+    v64 = inp["v"][0, 0].double().numpy()
+    do64 = inp["dout"][0, 0].double().numpy()
+    rows = np.array([0, 1, 32768, 65535])
+    s = scores64(inp["q"], inp["k"], 0, 0, rows)
+    ds = entmax_alpha_backward(s, do64[rows] @ v64.T, 1.5)
+    dq_ref = (ds @ k64) / np.sqrt(d)
+    err = float(np.abs(dq.cpu().numpy()[0, 0][rows] - dq_ref).max()) / max(1.0, float(np.abs(dq_ref).max()))
+    dk_c, dv_c = dk[0, 0].double().cpu().numpy(), dv[0, 0].double().cpu().numpy()
+    # sums over 65536 keys of float32 atomics: relative to the sum of magnitudes
+    sum_dk = float(np.abs(dk_c.sum(axis=0)).max()) / float(np.abs(dk_c).sum(axis=0).max())
+    sum_dv = float(np.abs(dv_c.sum(axis=0) - do64.sum(axis=0)).max()) / float(np.abs(do64).sum(axis=0).max())
+    log(f"[parity]   dq scaled err {err:.3g}; |sum dK| {sum_dk:.3g}, |sum dV - sum dO| {sum_dv:.3g} (relative)")
+    assert err <= 2e-3
+    assert sum_dk <= 1e-6 and sum_dv <= 1e-6
+
+
 def test_stream_overflow_fallback():
     # near-uniform rows: every key is a candidate, far more than a list holds
     inp = random_inputs(1, 2, 1300, 64, "bf16", seed=9, qk_gain=0.2)
