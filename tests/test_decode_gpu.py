@@ -77,6 +77,18 @@ def test_decode_long_cache():
     _check(q, k, v, sl, 0, "bf16", out, tau)
 
 
+def test_decode_very_long_cache():
+    # 2^20 cached keys: 4096 chunks per row, and a row solve of more entries
+    # than the registers of a workgroup hold (streamed at every step)
+    from entmax_amd import entmax_attn_decode
+    S = 1 << 20
+    q, k, v, sl = _inputs(1, 2, 1, S, 64, "bf16", 1.0, seed=20, seqlens=[S])
+    log("[decode] bf16 d64 H2 Hkv1 S2^20 W0")
+    out, tau = entmax_attn_decode(q.cuda(), k.cuda(), v.cuda(), sl.cuda(), 0)
+    torch.cuda.synchronize()
+    _check(q, k, v, sl, 0, "bf16", out, tau)
+
+
 def test_decode_reuses_workspace():
     # a second, smaller call on the same workspace sees nothing of the first
     from entmax_amd import decode_workspace_bytes, entmax_attn_decode

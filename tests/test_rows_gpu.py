@@ -30,7 +30,10 @@ def _scores(R, L, dtype, gain, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("L,gain", [(4, 1.0), (100, 2.0), (256, 0.5), (1000, 4.0), (4096, 1.0), (4100, 3.0), (6000, 0.3)])
+# L = 40000 with fewer than 1024 rows: a workgroup per row, streamed from
+# memory at every step (rows beyond the 16384 entries its registers hold)
+@pytest.mark.parametrize("L,gain", [(4, 1.0), (100, 2.0), (256, 0.5), (1000, 4.0), (4096, 1.0), (4100, 3.0), (6000, 0.3),
+                                    (40000, 1.0)])
 def test_rows_forward(dtype, L, gain):
     from entmax_amd import entmax15_rows
     R = 37
@@ -84,7 +87,7 @@ def test_rows_rejects_bad_shapes():
 # the zero pattern is compared where the exact p is zero or above 1e-30.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("alpha", [1.1, 1.25, 1.75, 2.0])
-@pytest.mark.parametrize("L,gain", [(100, 2.0), (1000, 1.0), (4100, 3.0)])
+@pytest.mark.parametrize("L,gain", [(100, 2.0), (1000, 1.0), (4100, 3.0), (40000, 1.0)])
 def test_bisect_rows_forward(dtype, alpha, L, gain):
     from entmax_amd import entmax_bisect_rows
     from oracle import entmax_alpha_exact
