@@ -202,12 +202,14 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 1)) void fwd_stream_
                 const float thr = m[i] - 2.f;
                 // this chunk's candidates of the row (a ballot per 16-key tile)
                 unsigned long long bal[4];
+#pragma unroll
+                for (int c16 = 0; c16 < 4; ++c16) bal[c16] = __ballot(!ovf[i] && s[c16][i] > thr_s[i]);
+                // no candidate for these four rows in this chunk (uniform): the
+                // lists stay as they are
+                if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0ull) continue;
                 int add = 0;
 #pragma unroll
-                for (int c16 = 0; c16 < 4; ++c16) {
-                    bal[c16] = __ballot(!ovf[i] && s[c16][i] > thr_s[i]);
-                    add += __popc(static_cast<unsigned>((bal[c16] >> (16 * g)) & 0xFFFFull));
-                }
+                for (int c16 = 0; c16 < 4; ++c16) add += __popc(static_cast<unsigned>((bal[c16] >> (16 * g)) & 0xFFFFull));
                 // make room: drop entries that fell below the current threshold
                 const bool need = !ovf[i] && cnt[i] + add > CAP;
                 if (__any(need)) {
