@@ -85,15 +85,16 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the workload's forward kernel, from the
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/traffic.json,
-    or None when none were taken for the current kernel sources."""
+def measured_traffic(workload, kernel="fwd"):
+    """HBM bytes per launch of the workload's forward (or backward) kernel,
+    from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/traffic.json, or None when none were taken for the current
+    kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        rec = json.load(fh).get(workload)
+        rec = json.load(fh).get(workload if kernel == "fwd" else f"{workload}_{kernel}")
     if not rec or rec.get("source_sha") != kernel_source_sha():
         return None
     return rec["traffic_bytes"]
@@ -439,7 +440,7 @@ def main():
             flop = 2.0 * w.d * pairs + 2.0 * w.d * nnz
         achieved = flop / (kms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": measured_traffic(w.name) if kname == "fwd" else None,
+                "frac": achieved / peak, "traffic": measured_traffic(w.name, kname),
                 "flop_per_launch": flop, "launch_ms": kms}
 
     res = {
