@@ -60,9 +60,13 @@ struct ShortCfg {
     static constexpr int ksv_bytes = ks_bytes > v_bytes ? ks_bytes : v_bytes;
     static constexpr size_t lds_bytes = kAlias ? static_cast<size_t>(ksv_bytes) : static_cast<size_t>(ks_bytes) + v_bytes;
     static_assert(NCH >= 1 && SPAN <= 2 * kWave, "whole chunks per thread; mask bits in two ballots");
-    // waves per SIMD to aim for (bf16, d = 64): four workgroups per CU when
-    // their LDS fits (128 registers), else three (168 registers)
-    static constexpr int kOcc = (DT == DT_BF16 && D == 64) ? (lds_bytes * 4 <= 160 * 1024 ? 4 : 3) : 1;
+    // waves per SIMD to aim for (bf16, d = 64): five workgroups per CU with
+    // the reduced scratch (KC = 16, 96 registers; the causal 32-key window:
+    // 35.5 -> 34.3 us on the decoder workload), else four when their LDS
+    // fits (128 registers), else three (168 registers)
+    static constexpr int kOcc = (DT == DT_BF16 && D == 64)
+                                    ? (KC == 16 && lds_bytes * 5 <= 160 * 1024 ? 5 : lds_bytes * 4 <= 160 * 1024 ? 4 : 3)
+                                    : 1;
     static_assert(KC <= NT * 4 && KC >= 16, "scratch slots");
 };
 
