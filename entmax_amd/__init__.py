@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     EntmaxError,
+    bwd_workspace_bytes,
     decode_workspace_bytes,
     entmax_attn_bwd,
     entmax_attn_decode,

@@ -1,7 +1,9 @@
 """ctypes binding of libentmax_attn.so: argument marshalling only.
 
-Every function here checks shapes, dtypes and devices, allocates outputs
-with torch when the caller gives none, and calls the C ABI declared in
+Every function here checks the shape, dtype, device and contiguity of every
+tensor it passes on (inputs, and outputs or workspaces the caller provides,
+which are checked before anything is launched), allocates outputs with torch
+when the caller gives none, and calls the C ABI declared in
 ``include/entmax_attn.h`` with raw device pointers and torch's current HIP
 stream.  No step of the computation runs in Python, and there is no CPU
 fallback: without the built library every call raises.
@@ -23,6 +25,7 @@ EXPORTS = (
     "entmax15_rows_fwd",
     "entmax_attn_bwd",
     "entmax_attn_bwd_gqa",
+    "entmax_attn_bwd_workspace_bytes",
     "entmax_attn_decode",
     "entmax_attn_decode_workspace_size",
     "entmax_attn_fwd",
@@ -58,14 +61,18 @@ def load_library(path=LIB_PATH):
     vp, i32, u8p, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
     lib.entmax_attn_fwd.argtypes = [vp, vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_fwd.restype = i32
-    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, vp]
+    sz = ctypes.c_size_t
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.entmax_attn_bwd.restype = i32
+    lib.entmax_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.entmax_attn_bwd_workspace_bytes.restype = sz
     lib.entmax_attn_probs.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_probs.restype = i32
     # grouped-query variants: H_kv after H
     lib.entmax_attn_fwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_fwd_gqa.restype = i32
-    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, i32,
+                                        vp, sz, vp]
     lib.entmax_attn_bwd_gqa.restype = i32
     lib.entmax_attn_probs_gqa.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_probs_gqa.restype = i32
@@ -78,7 +85,6 @@ def load_library(path=LIB_PATH):
     lib.entmax_bisect_rows_fwd.restype = i32
     lib.entmax_bisect_rows_bwd.argtypes = [fp, fp, fp, i32, i32, f32, vp]
     lib.entmax_bisect_rows_bwd.restype = i32
-    sz = ctypes.c_size_t
     lib.entmax_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.entmax_attn_decode_workspace_size.restype = sz
     lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, i32, vp]
@@ -144,6 +150,28 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _out(t, shape, like, name, dtype=torch.float32):
+    """A caller-provided output (or auxiliary input) tensor: exactly ``shape``
+    and ``dtype``, contiguous, on ``like``'s device; or None.  Raises
+    ValueError before anything is launched."""
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {tuple(shape)} {dtype} tensor on {like.device} "
+                         f"(got {tuple(t.shape)} {t.dtype} on {t.device})")
+    return t
+
+
+def _workspace(ws, need, like, name="workspace"):
+    """A caller-provided workspace: a contiguous uint8 tensor of at least
+    ``need`` bytes on ``like``'s device, or None to allocate one."""
+    if ws is None:
+        return torch.empty((max(need, 1),), dtype=torch.uint8, device=like.device)
+    if ws.dtype != torch.uint8 or ws.device != like.device or not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError(f"{name} must be a contiguous uint8 tensor of at least {need} bytes on {like.device}")
+    return ws
+
+
 def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, tau_out=None, want_tau=True):
     """O = entmax_1.5(Q K^T / sqrt(d)) V and the row thresholds tau.
 
@@ -153,6 +181,8 @@ def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, ta
     hkv = _check_qkv(q, k, v)
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
+    out = _out(out, (B, H, L, d), q, "out")
+    tau_out = _out(tau_out, (B, H, L), q, "tau_out")
     if out is None:
         out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
     if tau_out is None and want_tau:
@@ -163,8 +193,17 @@ def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, ta
     return out, tau_out
 
 
-def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, dq=None, dk=None, dv=None):
-    """Gradients float32: dq [B, H, L, d], dk and dv [B, H_kv, L, d], from the forward's tau."""
+def bwd_workspace_bytes(B, H, L, d):
+    """Bytes of device workspace ``entmax_attn_bwd`` needs (c_i per query row)."""
+    return int(load_library().entmax_attn_bwd_workspace_bytes(B, H, L, d))
+
+
+def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """Gradients float32: dq [B, H, L, d], dk and dv [B, H_kv, L, d], from the forward's tau.
+
+    workspace: a uint8 GPU tensor of at least ``bwd_workspace_bytes`` bytes,
+    or None to allocate one.  Deterministic (no atomics)."""
     lib = load_library()
     hkv = _check_qkv(q, k, v)
     _check_qkv(q, dout)
@@ -172,14 +211,21 @@ def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, d
         raise ValueError("dout must match q")
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
-    if tau.shape != (B, H, L) or tau.dtype != torch.float32 or not tau.is_contiguous():
-        raise ValueError("tau must be a contiguous [B, H, L] float32 tensor")
+    if tau is None:
+        raise ValueError("tau is required")
+    _out(tau, (B, H, L), q, "tau")
+    dq = _out(dq, (B, H, L, d), q, "dq")
+    dk = _out(dk, (B, hkv, L, d), q, "dk")
+    dv = _out(dv, (B, hkv, L, d), q, "dv")
+    need = bwd_workspace_bytes(B, H, L, d)
+    workspace = _workspace(workspace, need, q)
     mk = lambda h: torch.empty((B, h, L, d), dtype=torch.float32, device=q.device)  # noqa: E731
     dq = mk(H) if dq is None else dq
     dk = mk(hkv) if dk is None else dk
     dv = mk(hkv) if dv is None else dv
     rc = lib.entmax_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
-                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, L, d, _dtype_code(q), _stream(q))
+                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, L, d, _dtype_code(q),
+                                 _ptr(workspace), workspace.numel(), _stream(q))
     _check(lib, rc)
     return dq, dk, dv
 
@@ -190,6 +236,10 @@ def entmax_attn_probs(q, k, tau, key_mask=None, causal=False, window=0, probs=No
     hkv = _check_qkv(q, k)
     km = _check_mask(key_mask, q)
     B, H, L, d = q.shape
+    if tau is None:
+        raise ValueError("tau is required")
+    _out(tau, (B, H, L), q, "tau")
+    probs = _out(probs, (B, H, L, L), q, "probs")
     if probs is None:
         probs = torch.empty((B, H, L, L), dtype=torch.float32, device=q.device)
     rc = lib.entmax_attn_probs_gqa(_ptr(q), _ptr(k), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
@@ -230,15 +280,16 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
         raise ValueError("seqlens must be a [B] int32 tensor on q's device")
     hkv, S = k_cache.shape[1], k_cache.shape[2]
     need = decode_workspace_bytes(B, H, hkv, S, d, window, Lq)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q)
+    out = _out(out, tuple(q.shape), q, "out")
+    tau = _out(tau, tuple(q.shape[:-1]), q, "tau")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if tau is None and want_tau:
         tau = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     rc = lib.entmax_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens.contiguous()),
                                 int(bool(causal)), int(window),
-                                _ptr(out), _ptr(tau), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(out), _ptr(tau), _ptr(workspace), workspace.numel(),
                                 B, H, hkv, Lq, S, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return out, tau
@@ -260,6 +311,8 @@ def entmax_bisect_rows(scores, alpha=1.5, mask=None, p=None, tau=None, want_tau=
         if mask.shape != (R, L) or mask.dtype != torch.uint8 or mask.device != scores.device:
             raise ValueError("mask must be a [R, L] uint8 tensor on the scores' device")
         mask = mask.contiguous()
+    p = _out(p, (R, L), scores, "p")
+    tau = _out(tau, (R,), scores, "tau")
     if p is None:
         p = torch.empty((R, L), dtype=torch.float32, device=scores.device)
     if tau is None and want_tau:
@@ -277,9 +330,10 @@ def entmax_bisect_rows_bwd(p, dp, alpha=1.5, ds=None):
     for name, t in (("p", p), ("dp", dp)):
         if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [R, L] float32 GPU tensor")
-    if dp.shape != p.shape:
-        raise ValueError("dp must match p")
+    if dp.shape != p.shape or dp.device != p.device:
+        raise ValueError("dp must match p (shape and device)")
     R, L = p.shape
+    ds = _out(ds, (R, L), p, "ds")
     if ds is None:
         ds = torch.empty((R, L), dtype=torch.float32, device=p.device)
     rc = lib.entmax_bisect_rows_bwd(_ptr(p), _ptr(dp), _ptr(ds), R, L, float(alpha), _stream(p))
@@ -301,6 +355,8 @@ def entmax15_rows(scores, mask=None, p=None, tau=None, want_tau=True):
         if mask.shape != (R, L) or mask.dtype != torch.uint8 or mask.device != scores.device:
             raise ValueError("mask must be a [R, L] uint8 tensor on the scores' device")
         mask = mask.contiguous()
+    p = _out(p, (R, L), scores, "p")
+    tau = _out(tau, (R,), scores, "tau")
     if p is None:
         p = torch.empty((R, L), dtype=torch.float32, device=scores.device)
     if tau is None and want_tau:
@@ -317,9 +373,10 @@ def entmax15_rows_bwd(p, dp, ds=None):
     for name, t in (("p", p), ("dp", dp)):
         if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [R, L] float32 GPU tensor")
-    if dp.shape != p.shape:
-        raise ValueError("dp must match p")
+    if dp.shape != p.shape or dp.device != p.device:
+        raise ValueError("dp must match p (shape and device)")
     R, L = p.shape
+    ds = _out(ds, (R, L), p, "ds")
     if ds is None:
         ds = torch.empty((R, L), dtype=torch.float32, device=p.device)
     rc = lib.entmax15_rows_bwd(_ptr(p), _ptr(dp), _ptr(ds), R, L, _stream(p))

@@ -1,4 +1,5 @@
-// Backward pass of 1.5-entmax attention, driven by the forward's tau.
+// Backward pass of 1.5-entmax attention, driven by the forward's tau: the
+// query side (dQ and the per-row constant c_i).
 //
 // Jacobian ("ADASPLASH -- ROBERTA Benchmark Result", section 2.4; "RoBERTa
 // Base with AdaSplash Attention" model card, Mathematical Formulation 2): with
@@ -7,28 +8,33 @@
 //   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
 //   dV_j = sum_i p_ij dO_i.
 // Everything off the support is exactly zero, so only the scores need a
-// dense pass.  One workgroup = 4 waves of 16 query rows of one (batch, head);
-// lane (g, c) of a wave holds rows 4g .. 4g + 3 of each 16 x 16 score tile
-// (key c) and the d-slice [c D/16, (c + 1) D/16) of those rows' Q and dO.
+// dense pass.  This kernel owns query rows: it writes dQ_i and c_i (to the
+// caller's workspace); dK and dV are formed by key-owning workgroups in
+// bwd_wide.hpp from the same c_i, so no two workgroups ever add into one
+// gradient row and the result does not depend on timing.
+// One workgroup = 4 waves of 16 query rows of one (batch, head); lane (g, c)
+// of a wave holds rows 4g .. 4g + 3 of each 16 x 16 score tile (key c) and
+// the d-slice [c D/16, (c + 1) D/16) of those rows' dO.
 //   1. S is recomputed on MFMA from K chunks staged in LDS (chunk_stream.hpp,
 //      one buffer, loads one chunk ahead) and every support entry (key, w)
 //      goes to its row's list in LDS.
 //   2. Per row, the entries are processed in batches of NB = 2 (V and K row
-//      gathers of a batch are issued before any is used; small batches keep
-//      the registers within three workgroups per CU): dp by a 16-lane dot
-//      product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j, and
-//      dQ_i = scale (X - c_i Y) without another pass; then every entry adds
-//      scale dS_ij Q_i to dK_j and p_ij dO_i to dV_j with fp32 atomics.
+//      gathers of a batch are issued before any is used): dp by a 16-lane
+//      dot product, then sum w, sum w dp, X = sum w dp K_j, Y = sum w K_j,
+//      and dQ_i = scale (X - c_i Y) without another pass.
 // A row whose support outgrows its list is finished by two more passes over
 // the keys (all waves take part, only those rows do work): one for dp and the
-// sums, one for the atomics and dQ_i = scale sum_j dS_ij K_j once c_i is
-// known (for a long support the difference X - c_i Y would cost digits).
+// sums, one for dQ_i = scale sum_j dS_ij K_j once c_i is known (for a long
+// support the difference X - c_i Y would cost digits).
+// In fix-up mode (args.fixup) a workgroup only runs when one of its rows
+// carries the overflow marker (kCMarker in c_i) left by the wide query-side kernel,
+// and then recomputes dQ and c for its whole tile.
 #pragma once
 
 #include "chunk_stream.hpp"
 #include "common.hpp"
 #include "fwd_short.hpp"
-#include "tau_solver.hpp"
+#include "dpp.hpp"
 
 namespace ea {
 
@@ -42,11 +48,13 @@ struct BwdArgs {
     float* dq;
     float* dk;
     float* dv;
+    float* cbuf;   // [B, H, L] c_i (workspace)
     int B, H, L;
     int Hkv;   // key/value heads (H % Hkv == 0)
     int causal, window;
     float scale;
     int nqt;
+    int fixup;     // run only for tiles holding an overflow marker in c_i
 };
 
 template <int DT, int D>
@@ -57,7 +65,7 @@ struct BwdCfg : ChunkCfg<DT, D> {
     // a bf16 d = 128 workgroup takes under a third of the LDS
     static constexpr int CAP = 48;
     static constexpr int NB = 2;     // entries per gather batch
-    static constexpr size_t list_bytes = static_cast<size_t>(BM) * CAP * (2 * sizeof(float) + sizeof(uint16_t));
+    static constexpr size_t list_bytes = static_cast<size_t>(BM) * CAP * (sizeof(float) + sizeof(uint16_t));
     static constexpr size_t lds_bytes = S::k_bytes + list_bytes + 64;
 };
 
@@ -98,16 +106,38 @@ __device__ __forceinline__ void group_rank16(unsigned long long mask, int g, int
     *total = __popc(gm);
 }
 
+// Overflow marker left in c_i by the wide query-side kernel for rows it
+// could not finish (a quiet-NaN bit pattern, compared as an integer: the
+// library is built without NaN semantics, and no computed c_i has these bits).
+constexpr unsigned kCMarker = 0x7FC0DEADu;
+
+// True (in every thread) when one of rows [q0, q0 + n) of head bh carries
+// the overflow marker.  Called by the whole workgroup.
+__device__ __forceinline__ bool tile_marked(const float* cbuf, size_t bh, int L, int q0, int n, int* flag) {
+    const int t = threadIdx.x;
+    if (t == 0) *flag = 0;
+    __syncthreads();
+    if (t < n && q0 + t < L) {
+        if (reinterpret_cast<const unsigned*>(cbuf)[bh * L + q0 + t] == kCMarker) atomicOr(flag, 1);
+    }
+    __syncthreads();
+    const bool r = *flag != 0;
+    __syncthreads();
+    return r;
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(BwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef BwdCfg<DT, D> C;
     constexpr int DPL = D / 16, BM = C::BM, CAP = C::CAP, NB = C::NB, CK = C::S::CK;
+    // the overflow passes stage one chunk's entries of four rows (one per
+    // lane group) in the four lists of that lane group's rows
+    static_assert(4 * CAP >= CK, "a chunk's entries of one row fit the staging window");
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
     float* lw = reinterpret_cast<float*>(Kb + C::S::k_bytes);        // [BM][CAP] w
-    float* ldp = lw + BM * CAP;                                       // [BM][CAP] dp
-    uint16_t* lk = reinterpret_cast<uint16_t*>(ldp + BM * CAP);       // [BM][CAP] key
+    uint16_t* lk = reinterpret_cast<uint16_t*>(lw + BM * CAP);        // [BM][CAP] key
     int* flag = reinterpret_cast<int*>(lk + BM * CAP);                // workgroup vote
 
     const int total = a.B * a.H * a.nqt;
@@ -117,17 +147,15 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
     const int b = bh / a.H;
     const int q0 = qt * BM;
     const int L = a.L;
+    if (a.fixup && !tile_marked(a.cbuf, static_cast<size_t>(bh), L, q0, BM, flag)) return;   // uniform
     const size_t head_off = static_cast<size_t>(bh) * L * D;
     const T* qh = static_cast<const T*>(a.q) + head_off;
-    // the key/value head; its dK and dV collect the atomics of every query
-    // head of its group
     const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
     const T* kh = static_cast<const T*>(a.k) + kv_off;
     const T* vh = static_cast<const T*>(a.v) + kv_off;
     const T* doh = static_cast<const T*>(a.dout) + head_off;
     float* dqh = a.dq + head_off;
-    float* dkh = a.dk + kv_off;
-    float* dvh = a.dv + kv_off;
+    float* ch = a.cbuf + static_cast<size_t>(bh) * L;
     const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
     const bool hasm = km != nullptr;
 
@@ -167,12 +195,11 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
         cnt[i] = 0;
         ovf[i] = false;
     }
-    // this lane's d-slice of dO and Q for row 4g + i (loaded when the row is processed)
-    float dor[DPL], qr[DPL];
+    // this lane's d-slice of dO for row 4g + i (loaded when the row is processed)
+    float dor[DPL];
     auto load_row = [&](int i) {
         const int row = clamp_row(q0 + r0 + 4 * g + i, L);
         load_row_slice<DT, DPL>(doh + static_cast<size_t>(row) * D + DPL * c, dor);
-        load_row_slice<DT, DPL>(qh + static_cast<size_t>(row) * D + DPL * c, qr);
     };
 
     // Support entries of one chunk for this wave: calls put(i, e, key, w)
@@ -236,15 +263,16 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
     });
     wave_sync();
 
-    // dp of a batch of entries of row i: V and K row slices are all gathered first
-    auto batch = [&](int rl, int e0, int n, int (&key)[NB], float (&w)[NB], float (&dp)[NB], float (&kr)[NB][DPL]) {
+    // dp of a batch of entries at list offset base (entries e0 .. e0 + NB - 1
+    // of n): V and K row slices are all gathered first
+    auto batch = [&](int base, int e0, int n, int (&key)[NB], float (&w)[NB], float (&dp)[NB], float (&kr)[NB][DPL]) {
         float vr[NB][DPL];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int e = e0 + j;
             const bool in = e < n;
-            key[j] = in ? static_cast<int>(lk[rl * CAP + (in ? e : 0)]) : 0;
-            w[j] = in ? lw[rl * CAP + (in ? e : 0)] : 0.f;
+            key[j] = in ? static_cast<int>(lk[base + (in ? e : 0)]) : 0;
+            w[j] = in ? lw[base + (in ? e : 0)] : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -259,47 +287,8 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
             dp[j] = row_sum<16>(part);
         }
     };
-    auto scatter = [&](int key, float w, float dp, float cc) {
-        const float ds = a.scale * w * (dp - cc);
-        const float p = w * w;
-        float* dkr = dkh + static_cast<size_t>(key) * D + DPL * c;
-        float* dvr = dvh + static_cast<size_t>(key) * D + DPL * c;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) {
-            unsafeAtomicAdd(dkr + d, ds * qr[d]);
-            unsafeAtomicAdd(dvr + d, p * dor[d]);
-        }
-    };
-    // The same through LDS (the K buffers, idle after the first pass): the
-    // 16 lanes of a group first write their d-slices of one entry's dK and
-    // dV rows, then each atomic instruction covers 16 consecutive floats of
-    // a row (lane c: floats c, c + 16, ...), which the L2 processes far
-    // faster than 16 scattered ones.  Called by the whole wave.
-    float* stg = reinterpret_cast<float*>(Kb) + wv * (8 * D) + g * (2 * D);
-    auto scatter_staged = [&](bool act, int rl, int e, float cc) {
-        const int ee = act ? e : 0;
-        const int key = lk[rl * CAP + ee];
-        const float w = lw[rl * CAP + ee], dp = ldp[rl * CAP + ee];
-        const float ds = act ? a.scale * w * (dp - cc) : 0.f;
-        const float p = act ? w * w : 0.f;
-#pragma unroll
-        for (int d = 0; d < DPL; d += 4) {
-            *reinterpret_cast<f32x4*>(stg + DPL * c + d) = f32x4{ds * qr[d], ds * qr[d + 1], ds * qr[d + 2], ds * qr[d + 3]};
-            *reinterpret_cast<f32x4*>(stg + D + DPL * c + d) = f32x4{p * dor[d], p * dor[d + 1], p * dor[d + 2], p * dor[d + 3]};
-        }
-        wave_sync();
-        if (act) {
-            float* dkr = dkh + static_cast<size_t>(key) * D + c;
-            float* dvr = dvh + static_cast<size_t>(key) * D + c;
-#pragma unroll
-            for (int j = 0; j < DPL; ++j) {
-                unsafeAtomicAdd(dkr + 16 * j, stg[c + 16 * j]);
-                unsafeAtomicAdd(dvr + 16 * j, stg[D + c + 16 * j]);
-            }
-        }
-        wave_sync();
-    };
-    auto store_dq = [&](int i, float cc, const float (&X)[DPL], const float (&Y)[DPL]) {
+    // dQ_i = scale (X - cc Y) and the row's c_i = crow
+    auto store_dq = [&](int i, float cc, const float (&X)[DPL], const float (&Y)[DPL], float crow) {
         const int row = q0 + r0 + 4 * g + i;
         if (row < L) {
             float* dst = dqh + static_cast<size_t>(row) * D + DPL * c;
@@ -308,6 +297,7 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
                 *reinterpret_cast<f32x4*>(dst + d) =
                     f32x4{a.scale * fmaf(-cc, Y[d], X[d]), a.scale * fmaf(-cc, Y[d + 1], X[d + 1]),
                           a.scale * fmaf(-cc, Y[d + 2], X[d + 2]), a.scale * fmaf(-cc, Y[d + 3], X[d + 3])};
+            if (c == 0) ch[row] = crow;
         }
     };
 
@@ -316,7 +306,7 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
     for (int i = 0; i < 4; ++i) {
         const int rl = r0 + 4 * g + i;
         const int n = ovf[i] ? 0 : cnt[i];   // uniform in the 16-lane group
-        // (rows without entries still store dQ = 0; the gathers are skipped)
+        // (rows without entries still store dQ = 0 and c = 0; the gathers are skipped)
         if (__any(n > 0)) load_row(i);
         float X[DPL], Y[DPL], sw = 0.f, swdp = 0.f;
 #pragma unroll
@@ -324,10 +314,9 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
         for (int e0 = 0; __any(e0 < n); e0 += NB) {
             int key[NB];
             float w[NB], dp[NB], kr[NB][DPL];
-            batch(rl, e0, n, key, w, dp, kr);
+            batch(rl * CAP, e0, n, key, w, dp, kr);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                if (c == 0 && e0 + j < n) ldp[rl * CAP + e0 + j] = dp[j];
                 sw += w[j];
                 swdp = fmaf(w[j], dp[j], swdp);
                 const float wdp = w[j] * dp[j];
@@ -339,27 +328,25 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
             }
         }
         const float cc = sw > 0.f ? swdp / sw : 0.f;
-        if (!ovf[i]) store_dq(i, cc, X, Y);
-        wave_sync();   // the dp of this row are in LDS
-        for (int e = 0; __any(e < n); ++e) {
-            scatter_staged(e < n, rl, e, cc);
-        }
+        if (!ovf[i]) store_dq(i, cc, X, Y, cc);
     }
 
     // ---- 3. rows with more support than their list --------------------------------------
     // workgroup-wide vote (the passes below stream keys for every wave)
+    wave_sync();
     if (tid == 0) *flag = 0;
     __syncthreads();
     if (__any(ovf[0] || ovf[1] || ovf[2] || ovf[3]) && lane == 0) atomicOr(flag, 1);
     __syncthreads();
     if (*flag == 0) return;   // uniform
 
-    // One row index i at a time (two passes each: sums, then atomics); per
-    // chunk, the overflowed rows' entries of that chunk use the list as a
-    // staging window (at most CK per row).
+    // One row index i at a time (two passes each: sums, then dQ); per chunk,
+    // the overflowed rows' entries of that chunk are staged in the lists of
+    // the lane group's four rows (at most CK <= 4 CAP entries per chunk), all
+    // free once section 2 is done.
+    const int stage_base = (r0 + 4 * g) * CAP;
     for (int i = 0; i < 4; ++i) {
         load_row(i);
-        const int rl = r0 + 4 * g + i;
         float X[DPL], Y[DPL], sw = 0.f, swdp = 0.f, cc = 0.f;
 #pragma unroll
         for (int d = 0; d < DPL; ++d) { X[d] = 0.f; Y[d] = 0.f; }
@@ -369,8 +356,8 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
                 chunk_entries(ch, kb, M, [&](int ii, bool pred, int rank, int tot, int key, float w) {
                     if (ii != i) return;
                     if (pred && ovf[i]) {
-                        lk[rl * CAP + n + rank] = static_cast<uint16_t>(key);
-                        lw[rl * CAP + n + rank] = w;
+                        lk[stage_base + n + rank] = static_cast<uint16_t>(key);
+                        lw[stage_base + n + rank] = w;
                     }
                     n += ovf[i] ? tot : 0;
                 });
@@ -378,14 +365,13 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
                 for (int e0 = 0; __any(e0 < n); e0 += NB) {
                     int key[NB];
                     float w[NB], dp[NB], kr[NB][DPL];
-                    batch(rl, e0, n, key, w, dp, kr);
+                    batch(stage_base, e0, n, key, w, dp, kr);
 #pragma unroll
                     for (int j = 0; j < NB; ++j) {
                         if (pass == 0) {
                             sw += w[j];
                             swdp = fmaf(w[j], dp[j], swdp);
                         } else if (e0 + j < n) {
-                            scatter(key[j], w[j], dp[j], cc);
                             // dQ directly from dS: a long support would lose
                             // digits in the difference X - c Y
                             const float ds = w[j] * (dp[j] - cc);
@@ -396,8 +382,11 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 3 : 2)) void bwd_kernel(
                 }
                 wave_sync();
             });
-            if (pass == 0) cc = sw > 0.f ? swdp / sw : 0.f;
-            else if (ovf[i]) store_dq(i, 0.f, X, Y);   // Y stays zero: dQ = scale X
+            if (pass == 0) {
+                cc = sw > 0.f ? swdp / sw : 0.f;
+            } else if (ovf[i]) {
+                store_dq(i, 0.f, X, Y, cc);   // Y stays zero: dQ = scale X
+            }
         }
     }
 }

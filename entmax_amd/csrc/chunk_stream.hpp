@@ -35,9 +35,9 @@ struct ChunkCfg {
 
 // NBUF: LDS buffers per stream.  Two let a chunk be staged while the
 // previous one is in use (one barrier per chunk); one halves the LDS at the
-// cost of a second barrier per chunk.  NPRE (with one buffer): chunks in
-// flight in registers, 2 (loads issued two chunks ahead) or 1 (one chunk
-// ahead, half the registers).
+// cost of a second barrier per chunk.  NPRE: chunks in flight in registers,
+// 2 (loads issued two chunks ahead) or 1 (one chunk ahead, half the
+// registers).
 template <int DT, int D, int NBUF = 2, int NPRE = 2>
 struct ChunkStream {
     typedef typename InT<DT>::type T;
@@ -49,11 +49,16 @@ struct ChunkStream {
     const uint8_t* kmp;    // key mask of the batch (or any readable byte when !hasm)
     bool hasm;
     int L, tid, lane;
+    // optional per-row float staged with each chunk (side[row], +inf past L)
+    // into sideb[64 b .. 64 b + 63] for the chunk's buffer b; null: none
+    const float* side = nullptr;
+    float* sideb = nullptr;
 
     struct Pre {
         u32x4 k[C::NPC];
         u32x4 v[C::NPC];
         uint8_t mb;
+        float sv;
     };
 
     // 32-bit byte offsets from the head's base (a head holds at most
@@ -62,6 +67,10 @@ struct ChunkStream {
     __device__ __forceinline__ void prefetch(int ch, bool withv, Pre& p) const {
         const int cb = ch * C::CK;
         p.mb = kmp[hasm ? clamp_row(cb + lane, L) : 0];   // no branch around the load
+        if (side != nullptr) {
+            const float sv = side[clamp_row(cb + lane, L)];
+            p.sv = cb + lane < L ? sv : kInf;
+        }
         const char* kc = reinterpret_cast<const char*>(kh);
         const char* vc = reinterpret_cast<const char*>(vh);
 #pragma unroll
@@ -73,6 +82,7 @@ struct ChunkStream {
         }
     }
     __device__ __forceinline__ void stage(int buf, bool withv, const Pre& p) const {
+        if (sideb != nullptr && tid < C::CK) sideb[buf * C::CK + tid] = p.sv;
         char* kb = Kb + buf * C::k_bytes;
 #pragma unroll
         for (int j = 0; j < C::NPC; ++j) {
@@ -99,7 +109,9 @@ struct ChunkStream {
         return __ballot((ch * C::CK + lane < L) & (!hasm | (p.mb != 0)));
     }
     // fn(ch, kbuf, vbuf, M) for every chunk of [ch0, ch1), in order.  Every
-    // thread of the workgroup must call this with the same arguments.
+    // thread of the workgroup must call this with the same arguments.  With a
+    // side array the staged values of a chunk sit at sideb + (kbuf - Kb) /
+    // k_bytes * 64 (the buffer index times 64).
     template <typename F>
     __device__ __forceinline__ void run(int ch0, int ch1, bool withv, F&& fn) const {
         if (ch0 >= ch1) return;
@@ -134,6 +146,28 @@ struct ChunkStream {
                 __syncthreads();
                 if (ch + 3 < ch1) prefetch(ch + 3, withv, pb);
                 fn(ch + 1, Kb, Vb, Mb);
+                __syncthreads();
+            }
+            return;
+        }
+        if constexpr (NPRE == 1) {
+            // two buffers, loads one chunk ahead: chunk ch is in buffer
+            // (ch - ch0) & 1 while chunk ch + 1 arrives in registers and is
+            // staged into the other buffer, which nobody reads since the
+            // previous barrier
+            Pre pa;
+            prefetch(ch0, withv, pa);
+            stage(0, withv, pa);
+            unsigned long long Mc = valid_bits(ch0, pa);
+            __syncthreads();
+            for (int ch = ch0; ch < ch1; ++ch) {
+                const int buf = (ch - ch0) & 1;
+                if (ch + 1 < ch1) prefetch(ch + 1, withv, pa);
+                fn(ch, Kb + buf * C::k_bytes, Vb + buf * C::v_bytes, Mc);
+                if (ch + 1 < ch1) {
+                    stage(buf ^ 1, withv, pa);
+                    Mc = valid_bits(ch + 1, pa);
+                }
                 __syncthreads();
             }
             return;

@@ -18,6 +18,7 @@ namespace ea {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kWave = 64;
@@ -165,6 +166,7 @@ struct FwdArgs {
     int causal, window;
     float scale;
     int nqt;   // query tiles per head
+    int fixup; // long-span kernel: only tiles with a row marked by the wide kernel
 };
 
 // Key/value head serving query head bh = b H + h when Hkv heads serve the H

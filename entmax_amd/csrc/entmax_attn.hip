@@ -11,10 +11,11 @@
 #include "entmax_attn.h"
 #include "fwd_long.hpp"
 #include "fwd_short.hpp"
-#include "fwd_stream.hpp"
+#include "fwd_wide.hpp"
 #include "probs.hpp"
 #include "rows.hpp"
 #include "bwd.hpp"
+#include "bwd_wide.hpp"
 #include "decode.hpp"
 
 namespace {
@@ -82,19 +83,25 @@ int launch_short(const ea::FwdArgs& a, hipStream_t st) {
     return check_launch("fwd_short");
 }
 
+// Spans beyond 2048 keys: the wide kernel (one pass over K, candidate
+// lists, a gather over the support), then the long-span kernel in fix-up
+// mode for the 64-row tiles holding a row whose candidates outgrew its list.
 template <int DT, int D>
-int launch_stream(const ea::FwdArgs& a, hipStream_t st) {
-    // rows whose running max lags hold up to ~50 scores within 2 of it at
-    // once: 80 keep list overflows (and their recompute fallback) rare
-    constexpr int CAP = 80;
-    typedef ea::StreamCfg<D, CAP> C;
-    auto kern = ea::fwd_stream_kernel<DT, D, CAP>;
-    const size_t lds = C::template total_bytes<DT>();
-    int rc = set_lds(kern, lds);
+int launch_wide(ea::FwdArgs a, hipStream_t st) {
+    typedef ea::WideCfg<DT, D> W;
+    typedef ea::LongCfg<DT, D> C;
+    auto kw = ea::fwd_wide_kernel<DT, D>;
+    auto kl = ea::fwd_long_kernel<DT, D>;
+    int rc = set_lds(kw, W::stream_lds_bytes);
+    if (!rc) rc = set_lds(kl, C::lds_bytes);
     if (rc) return rc;
-    const int grid = a.B * a.H * a.nqt;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(ea::kThreads), lds, st, a);
-    return check_launch("fwd_stream");
+    a.nqt = (a.L + W::BR - 1) / W::BR;
+    a.fixup = 0;
+    hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
+    a.nqt = (a.L + C::BM - 1) / C::BM;
+    a.fixup = 1;
+    hipLaunchKernelGGL(kl, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_wide");
 }
 
 template <int DT, int D>
@@ -125,27 +132,47 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
         return launch_short<DT, D, 2>(a, st);
     }
     // spans beyond 2048 keys: one pass over K with candidate lists and a
-    // gather over the support (the multi-pass streaming kernel re-reads K
+    // gather over the support (the multi-pass long-span kernel re-reads K
     // and V more than it saves there)
-    if (s64 > 2048) {
-        a.nqt = (L + 63) / 64;
-        return launch_stream<DT, D>(a, st);
-    }
+    if (s64 > 2048) return launch_wide<DT, D>(a, st);
     return launch_long<DT, D>(a, st);
 }
 
+// Backward: query side (dQ, c) then key side (dK, dV), all on one stream.
+// Spans beyond 2048 keys take the wide query-side kernel, whose rows with an
+// overflowing support are finished by the tile kernel in fix-up mode.
 template <int DT, int D>
-int launch_bwd(const ea::BwdArgs& a, hipStream_t st) {
-    auto kern = ea::bwd_kernel<DT, D>;
-    const size_t lds = ea::BwdCfg<DT, D>::lds_bytes;
-    int rc = set_lds(kern, lds);
+int launch_bwd(ea::BwdArgs a, hipStream_t st) {
+    typedef ea::WideCfg<DT, D> W;
+    auto kq = ea::bwd_kernel<DT, D>;
+    auto kw = ea::bwd_q_kernel<DT, D>;
+    auto kv = ea::bwd_kv_kernel<DT, D>;
+    constexpr size_t lds_q = ea::BwdCfg<DT, D>::lds_bytes;
+    int rc = set_lds(kq, lds_q);
+    if (!rc) rc = set_lds(kw, W::stream_lds_bytes);
+    if (!rc) rc = set_lds(kv, W::lds_bytes);
     if (rc) return rc;
-    const size_t n = static_cast<size_t>(a.B) * a.Hkv * a.L * D;   // dK, dV: [B, H_kv, L, d]
-    const unsigned fill_blocks = static_cast<unsigned>((n / 4 + 255) / 256 + 1);
-    hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dk, n);
-    hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, a.dv, n);
-    hipLaunchKernelGGL(kern, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), lds, st, a);
+    const int L = a.L;
+    const int nt64 = (L + 63) / 64;
+    if (max_span(L, 64, a.causal, a.window) > 2048) {
+        a.nqt = (L + W::BR - 1) / W::BR;
+        a.fixup = 0;
+        hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
+        a.fixup = 1;
+    } else {
+        a.fixup = 0;
+    }
+    a.nqt = nt64;
+    hipLaunchKernelGGL(kq, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), lds_q, st, a);
+    a.nqt = (L + W::BR - 1) / W::BR;   // key tiles per key/value head
+    hipLaunchKernelGGL(kv, dim3(a.B * a.Hkv * a.nqt), dim3(ea::kThreads), W::lds_bytes, st, a);
     return check_launch("bwd");
+}
+
+// Workspace of the backward: c_i per query row, 256-byte aligned size.
+size_t bwd_ws_bytes(int B, int H, int L) {
+    const size_t n = static_cast<size_t>(B) * H * L * sizeof(float);
+    return (n + 255) & ~static_cast<size_t>(255);
 }
 
 }  // namespace
@@ -286,6 +313,7 @@ int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8
     a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = 0;
+    a.fixup = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16)
         return d == 64 ? dispatch_fwd<ea::DT_BF16, 64>(a, st) : dispatch_fwd<ea::DT_BF16, 128>(a, st);
@@ -319,21 +347,32 @@ int entmax_attn_probs_gqa(const void* q, const void* k, const uint8_t* key_mask,
     return check_launch("probs");
 }
 
+size_t entmax_attn_bwd_workspace_bytes(int B, int H, int L, int d) {
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0) return 0;
+    return bwd_ws_bytes(B, H, L);
+}
+
 int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
                         const float* tau, const void* dout, float* dq, float* dk, float* dv,
-                        int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
-    if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv)
-        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk and dv must not be NULL");
+                        int B, int H, int Hkv, int L, int d, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv || !workspace)
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk, dv and workspace must not be NULL");
     if (misaligned({q, k, v, dout, dq, dk, dv}, 16) || misaligned({tau}, 4))
         return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned, tau 4-byte aligned");
     int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
     if (rc) return rc;
+    if (misaligned({workspace}, 256)) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    const size_t need = bwd_ws_bytes(B, H, L);
+    if (workspace_bytes < need)
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     ea::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
-    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.cbuf = static_cast<float*>(workspace);
     a.B = B; a.H = H; a.L = L; a.Hkv = Hkv; a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
-    a.nqt = (L + 63) / 64;
+    a.nqt = 0;
+    a.fixup = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) return d == 64 ? launch_bwd<ea::DT_BF16, 64>(a, st) : launch_bwd<ea::DT_BF16, 128>(a, st);
     return d == 64 ? launch_bwd<ea::DT_F32, 64>(a, st) : launch_bwd<ea::DT_F32, 128>(a, st);
@@ -346,8 +385,9 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* 
 
 int entmax_attn_bwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
                     const float* tau, const void* dout, float* dq, float* dk, float* dv,
-                    int B, int H, int L, int d, int dtype, void* stream) {
-    return entmax_attn_bwd_gqa(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, H, L, d, dtype, stream);
+                    int B, int H, int L, int d, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return entmax_attn_bwd_gqa(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, H, L, d, dtype,
+                               workspace, workspace_bytes, stream);
 }
 
 int entmax_attn_probs(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
@@ -445,6 +485,6 @@ const char* entmax_attn_status_string(int status) {
 
 const char* entmax_attn_last_error(void) { return g_err; }
 
-int entmax_attn_version(void) { return 1; }
+int entmax_attn_version(void) { return 2; }
 
 }  // extern "C"

@@ -26,7 +26,8 @@
 //      (bf16: row-major, read back with transpose loads), chunks where a
 //      wave has no nonzero P skipped for that wave.  O is written in fp32.
 // Every pass decision is uniform over the workgroup (the chunk loop and its
-// barriers are shared).
+// barriers are shared).  In fix-up mode (args.fixup) a workgroup runs only
+// when one of its rows carries the wide forward's overflow marker.
 #pragma once
 
 #include <type_traits>
@@ -35,6 +36,7 @@
 #include "col_solve.hpp"
 #include "common.hpp"
 #include "fwd_short.hpp"
+#include "fwd_wide.hpp"
 
 namespace ea {
 
@@ -72,6 +74,20 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     const int q0 = qt * BM;
     const int L = a.L;
     const size_t head_off = static_cast<size_t>(bh) * L * D;
+    if (a.fixup) {
+        // fix-up mode: run only for a tile holding a row the wide kernel
+        // could not finish (kOMarker in O[row][0]), and then for all its rows
+        const int t = threadIdx.x;
+        if (t == 0) *flag = 0;
+        __syncthreads();
+        if (t < BM && q0 + t < L &&
+            reinterpret_cast<const unsigned*>(a.out)[head_off + static_cast<size_t>(q0 + t) * D] == kOMarker)
+            atomicOr(flag, 1);
+        __syncthreads();
+        const bool marked = *flag != 0;
+        __syncthreads();
+        if (!marked) return;   // uniform
+    }
     const T* qh = static_cast<const T*>(a.q) + head_off;
     const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
     const T* kh = static_cast<const T*>(a.k) + kv_off;

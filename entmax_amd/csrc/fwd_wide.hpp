@@ -1,0 +1,316 @@
+// Forward kernel for query tiles whose key span exceeds 2048 keys.
+//
+// One workgroup = 4 waves of NF fragments of 16 query rows (64 rows per wave
+// in bf16) of one (batch, head); lane (g, c) holds query row 16 f + c of
+// each fragment f and keys 4g .. 4g + 3 of every 16-key tile of the S^T
+// products, so the four lanes c, c + 16, c + 32, c + 48 hold a row.  K
+// streams through LDS in chunks of 64 keys shared by the four waves
+// (wide.hpp); each LDS read of K feeds NF products.  The score row is never
+// stored whole; K is streamed twice:
+//   1. scores, the running maximum of each lane's share of the row and the
+//      allowed count;
+//   2. the row maximum m and a certified lower bound of tau: the larger of
+//      m - 2 ("DistilBERT SST-2 with AdaSplash Attention" model card,
+//      Mathematical Formulation 2: tau >= max - 2) and the root of
+//      sum_j ((s_j - t)/2)^2 = 1 over the four lanes' maxima ("ADASPLASH --
+//      ROBERTA Benchmark Result", section 2.2 Theorem 1: the root over a
+//      subset of a row is at most the row's).  The scores are recomputed and
+//      every score above that bound goes to the row's candidate list: the
+//      row's own O row in memory, still unwritten, holds D/2 entries of
+//      (score, key), D/8 per lane (lane-private, so an append is one store);
+//   3. tau is the 25-step bisection result on [m - 2, m - 2/sqrt(n)], found
+//      as in the short-span kernel (exact root by Newton steps from the left
+//      and the closed form of Theorem 1 on the list, then the centre of the
+//      dyadic cell that holds it; col_solve.hpp), and
+//      O_i = sum_j p_ij V_j over the list entries with s > tau, gathering V
+//      rows (sparse aggregation, "RoBERTa Base with AdaSplash Attention" model
+//      card, Architecture Overview).
+// Two passes over K instead of one: a single pass must bound tau from the
+// keys seen so far, and a prefix of a row can have a far larger support than
+// the whole row (a flat top that a later, larger score dwarfs), so its lists
+// would have to be much longer.  A row with more than D/8 scores above its
+// bound in one lane is marked (kOMarker in O[row][0]); the long-span kernel
+// (fwd_long.hpp) then recomputes the marked 64-row tiles in fix-up mode, with
+// S recomputed from the K tiles pass by pass.
+#pragma once
+
+#include <type_traits>
+
+#include "chunk_stream.hpp"
+#include "col_solve.hpp"
+#include "common.hpp"
+#include "fwd_short.hpp"
+#include "wide.hpp"
+
+namespace ea {
+
+// Marker left in O[row][0] for rows the wide forward could not finish (a
+// quiet-NaN bit pattern, compared as an integer; finite inputs never give a
+// NaN output).
+constexpr unsigned kOMarker = 0x7FC0BEEFu;
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_kernel(FwdArgs a) {
+    typedef typename InT<DT>::type T;
+    typedef WideCfg<DT, D> C;
+    constexpr int NF = C::NF, CK = C::CK, DQ = C::DQ, NB = C::NB;
+    constexpr int SUB = D / 8;     // list entries per lane (8 bytes each in the row's O)
+    extern __shared__ float lds[];
+    char* Kb = reinterpret_cast<char*>(lds);
+
+    const int total = a.B * a.H * a.nqt;
+    const int wi = xcd_swizzle(blockIdx.x, total);
+    const int bh = wi / a.nqt;
+    const int qt = wi - bh * a.nqt;
+    const int b = bh / a.H;
+    const int q0 = qt * C::BR;
+    const int L = a.L;
+    const size_t head_off = static_cast<size_t>(bh) * L * D;
+    const T* qh = static_cast<const T*>(a.q) + head_off;
+    const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
+    const T* kh = static_cast<const T*>(a.k) + kv_off;
+    const T* vh = static_cast<const T*>(a.v) + kv_off;
+    const uint8_t* km = a.key_mask ? a.key_mask + static_cast<size_t>(b) * L : nullptr;
+    const bool hasm = km != nullptr;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = lane / 16, c = lane % 16;
+    const int rbase = q0 + wv * NF * 16;   // the wave's first row
+
+    int klo, khi;
+    key_range(q0, C::BR, L, a.causal, a.window, &klo, &khi);
+    const int ch0 = klo / CK, ch1 = (khi + CK - 1) / CK;
+    int wlo, whi;   // keys the wave's rows may attend
+    key_range(rbase, NF * 16, L, a.causal, a.window, &wlo, &whi);
+
+    const float scale = a.scale;
+    QFrag<DT, D> qf[NF];
+    float LM[NF];      // running maximum of this lane's share of the row (raw accumulator units)
+    float thrr[NF];    // the row's candidate threshold (raw, pass 2)
+    float lbs[NF];     // its certified lower bound of tau (scaled units)
+    float m[NF];       // row maximum (raw)
+    int cnt[NF];       // entries in the row's list
+    bool ovf[NF];
+    float nl[NF];      // allowed keys seen by this lane (causal rows)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        qf[f].load(qh, rbase + 16 * f + c, L, g);
+        LM[f] = -kInf;
+        cnt[f] = 0;
+        ovf[f] = false;
+        nl[f] = 0.f;
+    }
+    float npop = 0.f;   // valid keys of the span (rows without a causal mask; uniform)
+    const bool allrows = rbase + NF * 16 <= L;
+    // this lane's list of row f: entries (score scaled, key bits) in the row's O
+    float* outh = a.out + head_off;
+    auto lst = [&](int f, int lane_g) {
+        return reinterpret_cast<f32x2*>(outh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g * SUB;
+    };
+
+    ChunkStream<DT, D, 2, 1> cs;
+    cs.Kb = Kb;
+    cs.Vb = nullptr;
+    cs.kh = kh;
+    cs.vh = vh;
+    cs.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+    cs.hasm = hasm;
+    cs.L = L;
+    cs.tid = tid;
+    cs.lane = lane;
+    constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
+    const int klane = c * C::KSTR + 16 * g;
+
+    // Score tiles of one chunk.  A chunk of valid keys that no causal /
+    // window bound crosses and whose rows are all query rows ("clean",
+    // uniform) takes plain products and no masking.
+    auto scores = [&](auto clean_tag, int cb, const char* kb, unsigned long long M, f32x4 (&s)[NF][4]) {
+        constexpr bool CLEAN = decltype(clean_tag)::value;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 o[NF];
+            if constexpr (CLEAN) {
+                tile_products<DT, D, NF>(kb + klane + 16 * t * C::KSTR, qf, o);
+            } else {
+                const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
+                const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
+                if (!ok) {
+#pragma unroll
+                    for (int f = 0; f < NF; ++f) s[f][t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+                    continue;
+                }
+                const unsigned bias = ((mb >> c) & 1u) ? 0u : kMaskedBits;
+                tile_products<DT, D, NF, true>(kb + klane + 16 * t * C::KSTR, qf, o, bias, g);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                    const int row = rbase + 16 * f + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = cb + 16 * t + 4 * g + i;
+                        const bool okk = row < L && (!a.causal || allowed_ij(row, key, 1, a.window));
+                        o[f][i] = okk ? o[f][i] : -kInf;
+                    }
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) s[f][t] = o[f];
+        }
+    };
+    auto clean_chunk = [&](int cb, unsigned long long M) {
+        const bool cross = a.causal && (cb + CK - 1 > rbase || (a.window > 0 && cb <= rbase + NF * 16 - 1 - a.window));
+        return M == ~0ull && !cross && allrows;
+    };
+
+    // ---- 1. row maxima and allowed counts ------------------------------------------------
+    cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
+        const int cb = chn * CK;
+        npop += static_cast<float>(__popcll(M));
+        if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
+        f32x4 s[NF][4];
+        if (clean_chunk(cb, M)) {
+            scores(std::true_type{}, cb, kb, M, s);
+            if (a.causal) {
+                const float pc = g == 0 ? static_cast<float>(kWave) : 0.f;   // every key of the chunk allowed
+#pragma unroll
+                for (int f = 0; f < NF; ++f) nl[f] += pc;
+            }
+        } else {
+            scores(std::false_type{}, cb, kb, M, s);
+            if (a.causal) {
+                // allowed count of causal rows: this lane's allowed, valid keys
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nl[f] += s[f][t][i] > -1e29f ? 1.f : 0.f;
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            float mx = LM[f];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mx = fmaxf(fmaxf(mx, s[f][t][0]), fmaxf(fmaxf(s[f][t][1], s[f][t][2]), s[f][t][3]));
+            LM[f] = mx;
+        }
+    });
+
+    // ---- 2. thresholds, then the candidate lists ------------------------------------------
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        m[f] = col4_max(LM[f]);
+        const bool none = !(m[f] > -kInf);   // a row without an allowed key
+        const float ms = none ? 0.f : m[f] * scale;
+        // the root over the four lanes' maxima, in the half-scaled shifted
+        // domain x = (s - m)/2 (at least -1: tau >= m - 2; lanes without a
+        // key hold -inf, below every root)
+        const float xl = LM[f] > -kInf ? fmaf(LM[f], 0.5f * scale, -0.5f * ms) : -2.f;
+        const float lbx = fmaxf(col_lower_bound(xl), -1.f);
+        lbs[f] = none ? -kInf : fmaf(2.f, lbx, ms);
+        const float tr = lbs[f] / scale;
+        thrr[f] = none ? kInf : tr - 1e-6f * fabsf(tr) - 1e-30f;   // a little low: rounding keeps more
+    }
+    cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
+        const int cb = chn * CK;
+        if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
+        f32x4 s[NF][4];
+        if (clean_chunk(cb, M)) scores(std::true_type{}, cb, kb, M, s);
+        else scores(std::false_type{}, cb, kb, M, s);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            float tm[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tm[t] = fmaxf(fmaxf(s[f][t][0], s[f][t][1]), fmaxf(s[f][t][2], s[f][t][3]));
+            if (!__any(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])) > thrr[f])) continue;   // uniform
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!__any(tm[t] > thrr[f])) continue;   // uniform: no candidate in this tile
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (s[f][t][i] > thrr[f]) {
+                        if (cnt[f] < SUB)
+                            lst(f, g)[cnt[f]] = f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
+                        else
+                            ovf[f] = true;
+                        ++cnt[f];
+                    }
+                }
+            }
+        }
+    });
+    // the lists written by the row's four lanes are visible to all of them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    // ---- tau, then O over the support, row by row ---------------------------------------
+#pragma unroll 1
+    for (int f = 0; f < NF; ++f) {
+        const int row = rbase + 16 * f + c;
+        const float n = row < L ? (a.causal ? col4_sum(nl[f]) : npop) : 0.f;
+        const bool empty = n == 0.f;
+        const float ms = empty ? 0.f : m[f] * scale;
+        const float hs = 0.5f * ms;
+        ColState st;
+        st.lo = -1.f;
+        st.hi = -__builtin_amdgcn_rsqf(empty ? 1.f : n);
+        st.lb = fmaxf(-1.f, fmaf(lbs[f], 0.5f, -hs));
+        st.it = 0;
+        st.hc = 0.f;
+        st.cnt = 0.f;
+        st.a1 = 0.f;
+        st.a2 = 0.f;
+        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // some lane's list overflowed
+        const int len = rovf ? 0 : min(cnt[f], SUB);
+        const f32x2* mine = lst(f, g);
+        float sl[SUB];
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) {
+            const float v = mine[k < len ? k : 0][0];
+            sl[k] = k < len ? fmaf(v, 0.5f, -hs) : -kInf;
+        }
+        const float ts = col_exact<SUB>(sl, st, SUB * 4 + 3);
+        const float t = col_dyadic(st, ts);
+        // O = sum p V over the list entries above tau (all four lanes' lists)
+        float o[DQ];
+#pragma unroll
+        for (int d = 0; d < DQ; ++d) o[d] = 0.f;
+#pragma unroll 1
+        for (int g2 = 0; g2 < 4; ++g2) {
+            const int n2 = __shfl(len, 16 * g2 + c, kWave);   // entries of lane (g2, c)
+            const int nmax = wave_max_int<kWave>(n2);
+            const f32x2* other = lst(f, g2);
+            for (int e0 = 0; e0 < nmax; e0 += NB) {
+                int key[NB];
+                float p[NB];
+                RowSlice<DT, DQ> vr[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const bool in = e0 + j < n2;
+                    const f32x2 en = other[in ? e0 + j : 0];
+                    const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
+                    p[j] = in && !empty ? y * y : 0.f;
+                    key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
+                }
+#pragma unroll
+                for (int j = 0; j < NB; ++j) vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int d = 0; d < DQ; ++d) o[d] = fmaf(p[j], vr[j].at(d), o[d]);
+            }
+        }
+        // every lane of the wave has read the row's lists before any is overwritten
+        __builtin_amdgcn_wave_barrier();
+        if (row < L) {
+            float* orow = outh + static_cast<size_t>(row) * D + g * DQ;
+#pragma unroll
+            for (int d = 0; d < DQ; d += 4) *reinterpret_cast<f32x4*>(orow + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]};
+            if (rovf && g == 0) reinterpret_cast<unsigned*>(orow)[0] = kOMarker;   // recomputed by the fix-up
+            if (a.tau != nullptr && g == 0) a.tau[static_cast<size_t>(bh) * L + row] = empty ? kInf : fmaf(2.f, t, ms);
+        }
+    }
+}
+
+}  // namespace ea

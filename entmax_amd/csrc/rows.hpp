@@ -21,7 +21,7 @@
 
 #include "col_solve.hpp"
 #include "common.hpp"
-#include "tau_solver.hpp"
+#include "dpp.hpp"
 
 namespace ea {
 

@@ -80,13 +80,23 @@ int entmax_attn_fwd(const void *q, const void *k, const void *v,
  * dp_ij = dout_i . v_j, c_i = sum_j w_ij dp_ij / sum_j w_ij and
  * dS_ij = w_ij (dp_ij - c_i):  dq = dS k / sqrt(d), dk = dS^T q / sqrt(d),
  * dv = p^T dout.  dq, dk, dv are overwritten (float32).
- * Required: q, k, v, tau, dout, dq, dk, dv.  Optional: key_mask.
+ * Required: q, k, v, tau, dout, dq, dk, dv, workspace.  Optional: key_mask.
+ *  - workspace: caller-owned DEVICE memory, 256-byte aligned, of at least
+ *    entmax_attn_bwd_workspace_bytes(B, H, L, d) bytes (c_i of every query
+ *    row); no initialisation needed, scratch after the call.  Two calls in
+ *    flight must not share a workspace.  A too small or misaligned
+ *    workspace returns ENTMAX_ERR_INVALID_ARG.
+ *  - Deterministic: query rows (dq, c) and key rows (dk, dv) are each
+ *    owned by one workgroup and summed in a fixed order (no atomics), so
+ *    repeated calls on the same inputs give identical bits.
  */
+size_t entmax_attn_bwd_workspace_bytes(int B, int H, int L, int d);
 int entmax_attn_bwd(const void *q, const void *k, const void *v,
                     const uint8_t *key_mask, int causal, int window,
                     const float *tau, const void *dout,
                     float *dq, float *dk, float *dv,
-                    int B, int H, int L, int d, int dtype, void *stream);
+                    int B, int H, int L, int d, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Dense attention weights for inspection and tests: probs[b,h,i,j] =
@@ -104,9 +114,10 @@ int entmax_attn_probs(const void *q, const void *k,
  * Step-by-Step Tensor Execution Trace: K and V have H_kv heads, each repeated
  * for H / H_kv consecutive query heads).  k, v: [B, H_kv, L, d]; query head
  * h uses key/value head h / (H / H_kv).  dk, dv: [B, H_kv, L, d], each the
- * sum over the query heads of its group.  H_kv must divide H (else
- * ENTMAX_ERR_INVALID_ARG).  With H_kv = H these are the calls above, which
- * are implemented through them.
+ * sum over the query heads of its group (in head order).  The backward's
+ * workspace is sized as for the call above (by the H query heads).  H_kv
+ * must divide H (else ENTMAX_ERR_INVALID_ARG).  With H_kv = H these are the
+ * calls above, which are implemented through them.
  */
 int entmax_attn_fwd_gqa(const void *q, const void *k, const void *v,
                         const uint8_t *key_mask, int causal, int window,
@@ -116,7 +127,8 @@ int entmax_attn_bwd_gqa(const void *q, const void *k, const void *v,
                         const uint8_t *key_mask, int causal, int window,
                         const float *tau, const void *dout,
                         float *dq, float *dk, float *dv,
-                        int B, int H, int H_kv, int L, int d, int dtype, void *stream);
+                        int B, int H, int H_kv, int L, int d, int dtype,
+                        void *workspace, size_t workspace_bytes, void *stream);
 int entmax_attn_probs_gqa(const void *q, const void *k,
                           const uint8_t *key_mask, int causal, int window,
                           const float *tau, float *probs,

@@ -50,7 +50,7 @@ def test_status_strings(lib):
     assert lib.entmax_attn_status_string(1) == b"invalid argument"
     assert lib.entmax_attn_status_string(2) == b"unsupported configuration"
     assert lib.entmax_attn_status_string(3) == b"HIP error"
-    assert lib.entmax_attn_version() == 1
+    assert lib.entmax_attn_version() == 2
 
 
 P = ctypes.c_void_p(16)   # never dereferenced: every call below is rejected first
@@ -71,13 +71,37 @@ def test_fwd_rejects_bad_arguments(lib, kw, code):
     assert lib.entmax_attn_last_error() != b""
 
 
+W256 = ctypes.c_void_p(256)   # a 256-byte aligned stand-in for a workspace
+
+
+def _bwd_args(lib, B=1, H=1, L=8, d=64):
+    # q, k, v, mask, causal, window, tau, dout, dq, dk, dv, B, H, L, d, dtype, ws, ws_bytes, stream
+    ws = lib.entmax_attn_bwd_workspace_bytes(B, H, L, d)
+    return [P, P, P, None, 0, 0, P, P, P, P, P, B, H, L, d, 1, W256, ws, None]
+
+
+def test_bwd_workspace_size(lib):
+    # c_i of every query row, rounded up to 256 bytes
+    assert lib.entmax_attn_bwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 4
+    assert lib.entmax_attn_bwd_workspace_bytes(2, 3, 7, 64) == 256
+    assert lib.entmax_attn_bwd_workspace_bytes(0, 3, 7, 64) == 0
+    assert lib.entmax_attn_bwd_workspace_bytes(1, 1, -1, 64) == 0
+
+
 def test_bwd_and_probs_reject_null(lib):
-    args = [P, P, P, None, 0, 0, P, P, P, P, P, 1, 1, 8, 64, 1, None]
-    for i in (0, 1, 2, 6, 7, 8, 9, 10):
+    args = _bwd_args(lib)
+    for i in (0, 1, 2, 6, 7, 8, 9, 10, 16):
         a = list(args)
         a[i] = None
-        assert lib.entmax_attn_bwd(*a) == 1
+        assert lib.entmax_attn_bwd(*a) == 1, i
     assert lib.entmax_attn_bwd(*args[:4], 0, 5, *args[6:]) == 1         # window without causal
+    a = list(args)
+    a[17] = args[17] - 1                                                 # workspace too small
+    assert lib.entmax_attn_bwd(*a) == 1
+    assert b"workspace" in lib.entmax_attn_last_error()
+    a = list(args)
+    a[16] = ctypes.c_void_p(272)                                         # workspace not 256-byte aligned
+    assert lib.entmax_attn_bwd(*a) == 1
     assert lib.entmax_attn_probs(P, P, None, 0, 0, None, P, 1, 1, 8, 64, 1, None) == 1
     assert lib.entmax_attn_probs(P, P, None, 0, 0, P, P, 1, 1, 8, 32, 1, None) == 2
 
@@ -93,11 +117,31 @@ def test_binding_validates_before_calling():
         _dtype_code(torch.zeros(1, dtype=torch.float16))
 
 
+def test_binding_validates_outputs_before_calling():
+    # caller-provided outputs and workspaces of the wrong shape, dtype,
+    # device or layout are refused by the binding, before any launch
+    import torch
+    from entmax_amd._binding import _out, _workspace
+    like = torch.zeros(2, 3, 8, 64)
+    good = torch.zeros(2, 3, 8, 64)
+    assert _out(good, (2, 3, 8, 64), like, "out") is good
+    assert _out(None, (2, 3, 8, 64), like, "out") is None
+    for bad in (torch.zeros(2, 3, 8, 32), torch.zeros(2, 3, 8, 64, dtype=torch.bfloat16),
+                torch.zeros(2, 3, 64, 8).transpose(2, 3)):
+        with pytest.raises(ValueError):
+            _out(bad, (2, 3, 8, 64), like, "out")
+    assert _workspace(torch.zeros(300, dtype=torch.uint8), 256, like).numel() == 300
+    for bad in (torch.zeros(100, dtype=torch.uint8), torch.zeros(300, dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            _workspace(bad, 256, like)
+
+
 def test_grouped_query_rejects_bad_kv_heads(lib):
     # H_kv must divide H
     for hkv in (0, -1, 3):
         assert lib.entmax_attn_fwd_gqa(P, P, P, None, 0, 0, P, None, 1, 4, hkv, 8, 64, 1, None) == 1
-        assert lib.entmax_attn_bwd_gqa(P, P, P, None, 0, 0, P, P, P, P, P, 1, 4, hkv, 8, 64, 1, None) == 1
+        assert lib.entmax_attn_bwd_gqa(P, P, P, None, 0, 0, P, P, P, P, P, 1, 4, hkv, 8, 64, 1, W256, 1 << 20,
+                                       None) == 1
         assert lib.entmax_attn_probs_gqa(P, P, None, 0, 0, P, P, 1, 4, hkv, 8, 64, 1, None) == 1
     assert b"H_kv" in lib.entmax_attn_last_error()
 
@@ -161,7 +205,7 @@ def test_entry_points_reject_misaligned_pointers(lib):
     for kw in ({"q": M16}, {"k": M16}, {"v": M16}, {"out": M16}, {"tau": M4}):
         assert _fwd(lib, **kw) == 1, kw
     assert b"aligned" in lib.entmax_attn_last_error()
-    args = [P, P, P, None, 0, 0, P, P, P, P, P, 1, 1, 8, 64, 1, None]
+    args = _bwd_args(lib)
     for i, bad in ((0, M16), (1, M16), (2, M16), (6, M4), (7, M16), (8, M16), (9, M16), (10, M16)):
         a = list(args)
         a[i] = bad

@@ -58,8 +58,9 @@ def test_decoder_sampled_rows_all_heads():
 
 
 def test_longctx_forward_two_heads():
+    # two whole heads: O, tau, A entry by entry and the exact-zero pattern
     inp = make_inputs("longctx")
-    check_forward(inp, heads=[(0, 0), (0, 31)], label="longctx", check_probs=False)
+    check_forward(inp, heads=[(0, 0), (0, 31)], label="longctx")
 
 
 def test_longctx_forward_sampled_rows():
@@ -114,17 +115,24 @@ def test_scattered_key_mask_causal():
     check_forward(inp, label="scattered mask")
 
 
-# ---- the streaming path (key span > 1024) and its overflow fallback -------------
+# ---- the streaming path (key span > 2048) and its overflow fallback -------------
 
 def test_stream_path_bidirectional():
-    inp = random_inputs(1, 2, 2000, 64, "bf16", seed=7)
-    check_forward(inp, label="stream", check_probs=False)
+    inp = random_inputs(1, 2, 2200, 64, "bf16", seed=7)
+    check_forward(inp, label="stream")
 
 
 def test_stream_path_masked_f32():
-    inp = random_inputs(2, 1, 1500, 128, "f32", seed=8, key_lengths=[1500, 1203])
-    check_forward(inp, label="stream f32", check_probs=False)
+    inp = random_inputs(2, 1, 2300, 128, "f32", seed=8, key_lengths=[2300, 2203])
+    check_forward(inp, label="stream f32")
 
+
+def test_stream_path_causal_window_and_grouped():
+    # causal rows of up to 4000 keys with a wide window, grouped K and V
+    inp = random_inputs(1, 4, 4000, 128, "bf16", seed=14, qk_gain=1.5)
+    inp["k"], inp["v"] = inp["k"][:, :2].contiguous(), inp["v"][:, :2].contiguous()
+    inp["causal"], inp["window"] = True, 2500
+    check_forward(inp, heads=[(0, 0), (0, 3)], label="stream causal window gqa")
 
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, False), ("f32", 128, True)])
 def test_maximum_length(dtype, d, causal):
@@ -174,9 +182,10 @@ def test_backward_maximum_length():
 
 
 def test_stream_overflow_fallback():
-    # near-uniform rows: every key is a candidate, far more than a list holds
-    inp = random_inputs(1, 2, 1300, 64, "bf16", seed=9, qk_gain=0.2)
-    check_forward(inp, label="stream overflow", check_probs=False)
+    # near-uniform rows of 2200 keys: every key is a candidate, far more than
+    # a list holds
+    inp = random_inputs(1, 2, 2200, 64, "bf16", seed=9, qk_gain=0.2)
+    check_forward(inp, label="stream overflow")
 
 
 # ---- determinism and streams ----------------------------------------------------
@@ -219,9 +228,71 @@ def test_backward_masked_causal_window():
 
 
 def test_backward_dense_support_overflow():
-    # supports of hundreds of keys: the per-row list overflows
+    # supports of hundreds of keys: the per-row list overflows; the key side
+    # flushes its lists many times per key
     inp = random_inputs(1, 2, 600, 64, "f32", seed=13, qk_gain=0.3)
     check_backward(inp, label="dense support")
+
+
+@pytest.mark.parametrize("L,gain,causal", [(2304, 2.0, False), (2400, 0.4, False), (3000, 1.0, True)])
+def test_backward_long_spans(L, gain, causal):
+    # spans beyond 2048 keys take the wide query-side kernel; gain 0.4 gives
+    # supports of hundreds of keys (overflow markers and the tile fix-up)
+    inp = random_inputs(1, 2, L, 128, "bf16", seed=L + 3, qk_gain=gain)
+    inp["causal"] = causal
+    check_backward(inp, label=f"long span gain{gain}")
+
+
+def test_backward_long_span_f32_masked_window():
+    inp = random_inputs(2, 1, 2600, 64, "f32", seed=15, key_lengths=[2600, 2311])
+    inp["causal"], inp["window"] = True, 2200
+    check_backward(inp, label="long span f32 masked window")
+
+
+@pytest.mark.parametrize("L,d,gain", [(300, 64, 1.5), (2304, 128, 2.0), (2200, 64, 0.3)])
+def test_backward_is_deterministic(L, d, gain):
+    # query rows and key rows each have one owner and a fixed summation
+    # order: two calls give identical bits
+    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd
+    from tests.parity_util import to_gpu
+    g = to_gpu(random_inputs(2, 2, L, d, "bf16", seed=L + d, qk_gain=gain))
+    _, tau = entmax_attn_fwd(g["q"], g["k"], g["v"])
+    a = entmax_attn_bwd(g["q"], g["k"], g["v"], tau, g["dout"])
+    b = entmax_attn_bwd(g["q"], g["k"], g["v"], tau, g["dout"])
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_plain_entry_points_through_ctypes():
+    # entmax_attn_fwd / entmax_attn_bwd (not the grouped variants) called
+    # with raw pointers, against the oracle
+    import ctypes
+    from entmax_amd import bwd_workspace_bytes, load_library
+    from oracle import attention_backward, attention_forward
+    from tests.parity_util import to_gpu
+    lib = load_library()
+    inp = random_inputs(2, 2, 150, 64, "bf16", seed=21, key_lengths=[150, 97])
+    g = to_gpu(inp)
+    B, H, L, d = g["q"].shape
+    out = torch.empty((B, H, L, d), device="cuda")
+    tau = torch.empty((B, H, L), device="cuda")
+    grads = [torch.empty((B, H, L, d), device="cuda") for _ in range(3)]
+    ws = torch.empty((bwd_workspace_bytes(B, H, L, d),), dtype=torch.uint8, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.entmax_attn_fwd(P(g["q"]), P(g["k"]), P(g["v"]), P(g["key_mask"]), 0, 0, P(out), P(tau),
+                               B, H, L, d, 1, st) == 0
+    assert lib.entmax_attn_bwd(P(g["q"]), P(g["k"]), P(g["v"]), P(g["key_mask"]), 0, 0, P(tau), P(g["dout"]),
+                               P(grads[0]), P(grads[1]), P(grads[2]), B, H, L, d, 1, P(ws), ws.numel(), st) == 0
+    torch.cuda.synchronize()
+    ref = attention_forward(inp["q"], inp["k"], inp["v"], inp["key_mask"])
+    refb = attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], inp["key_mask"])
+    assert float(np.abs(out.cpu().numpy().reshape(ref["out"].shape) - ref["out"]).max()) <= 2e-3
+    for name, gt in zip(("dq", "dk", "dv"), grads):
+        r = refb[name]
+        err = float(np.abs(gt.cpu().numpy().reshape(r.shape) - r).max()) / max(1.0, float(np.abs(r).max()))
+        assert err <= 2e-3, (name, err)
 
 
 # ---- grouped-query attention (key/value heads shared by groups of query heads) ----
@@ -264,3 +335,31 @@ def test_dense_rows_with_one_high_key(L, causal):
     inp["k"][0, :, L // 2] += 4.0 * qm / (qm.norm() ** 2)
     inp["causal"] = causal
     check_forward(inp, label=f"dense + one high key L{L} causal={causal}")
+
+
+def test_binding_refuses_bad_outputs_before_launch():
+    # outputs, tau and workspaces of the wrong shape, dtype, device or layout
+    # raise ValueError in the binding; nothing reaches the kernels
+    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd, entmax_attn_probs
+    from tests.parity_util import to_gpu
+    g = to_gpu(random_inputs(1, 2, 64, 64, "bf16", seed=3))
+    q, k, v, do = g["q"], g["k"], g["v"], g["dout"]
+    out, tau = entmax_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    bad_out = [torch.empty((1, 2, 64, 32), device="cuda"), torch.empty((1, 2, 64, 64), device="cuda",
+                                                                       dtype=torch.bfloat16),
+               torch.empty((1, 2, 64, 64)), torch.empty((1, 2, 64, 64), device="cuda").transpose(2, 3)]
+    for o in bad_out:
+        with pytest.raises(ValueError):
+            entmax_attn_fwd(q, k, v, out=o)
+    with pytest.raises(ValueError):
+        entmax_attn_fwd(q, k, v, tau_out=torch.empty((1, 2, 63), device="cuda"))
+    with pytest.raises(ValueError):
+        entmax_attn_bwd(q, k, v, tau.cpu(), do)                                  # tau on the CPU
+    with pytest.raises(ValueError):
+        entmax_attn_bwd(q, k, v, tau, do, dk=torch.empty((1, 2, 64, 64), device="cuda", dtype=torch.float16))
+    with pytest.raises(ValueError):
+        entmax_attn_bwd(q, k, v, tau, do, workspace=torch.empty((4,), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        entmax_attn_probs(q, k, tau, probs=torch.empty((1, 2, 64, 32), device="cuda"))
+    torch.cuda.synchronize()

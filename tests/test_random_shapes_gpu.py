@@ -66,7 +66,7 @@ def test_random_shape(case):
     label = (f"random B{c['B']} H{H}/{hkv} L{c['L']} d{c['d']} {c['dtype']} causal={c['causal']} "
              f"W{c['window']} pad={c['pad']} gain={c['gain']}")
     head = [(c["B"] - 1, H - 1)]
-    check_forward(inp, heads=head, check_probs=c["L"] <= 1024, label=label)
+    check_forward(inp, heads=head, label=label)
     if c["L"] <= 300:
         # grouped K, V: their gradients sum over every query head of the group
         check_backward(inp, heads=head if hkv == H else None, label=label)
