@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     bwd_workspace_bytes,
     decode_workspace_bytes,
     entmax_attn_bwd,
+    entmax_attn_bwd_noalloc,
     entmax_attn_decode,
     entmax_attn_fwd,
     entmax_attn_probs,

@@ -25,6 +25,7 @@ EXPORTS = (
     "entmax15_rows_fwd",
     "entmax_attn_bwd",
     "entmax_attn_bwd_gqa",
+    "entmax_attn_bwd_noalloc",
     "entmax_attn_bwd_workspace_bytes",
     "entmax_attn_decode",
     "entmax_attn_decode_workspace_size",
@@ -74,6 +75,9 @@ def load_library(path=LIB_PATH):
     lib.entmax_attn_bwd_gqa.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32, i32,
                                         vp, sz, vp]
     lib.entmax_attn_bwd_gqa.restype = i32
+    lib.entmax_attn_bwd_noalloc.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, fp, fp, fp, i32, i32, i32, i32, i32,
+                                            i32, vp]
+    lib.entmax_attn_bwd_noalloc.restype = i32
     lib.entmax_attn_probs_gqa.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_probs_gqa.restype = i32
     lib.entmax15_rows_fwd.argtypes = [vp, u8p, fp, fp, i32, i32, i32, vp]
@@ -226,6 +230,30 @@ def entmax_attn_bwd(q, k, v, tau, dout, key_mask=None, causal=False, window=0, d
     rc = lib.entmax_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, L, d, _dtype_code(q),
                                  _ptr(workspace), workspace.numel(), _stream(q))
+    _check(lib, rc)
+    return dq, dk, dv
+
+
+def entmax_attn_bwd_noalloc(q, k, v, tau, dout, dq, dk, dv, key_mask=None, causal=False, window=0):
+    """``entmax_attn_bwd`` into caller-provided dq, dk, dv with no allocation:
+    c_i lives in the library's built-in scratch (at most 1048576 query rows
+    B H L; calls in flight at once on one GPU race).  Returns (dq, dk, dv)."""
+    lib = load_library()
+    hkv = _check_qkv(q, k, v)
+    _check_qkv(q, dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    if tau is None or dq is None or dk is None or dv is None:
+        raise ValueError("tau, dq, dk and dv are required (this call allocates nothing)")
+    _out(tau, (B, H, L), q, "tau")
+    _out(dq, (B, H, L, d), q, "dq")
+    _out(dk, (B, hkv, L, d), q, "dk")
+    _out(dv, (B, hkv, L, d), q, "dv")
+    rc = lib.entmax_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, L, d, _dtype_code(q),
+                                     _stream(q))
     _check(lib, rc)
     return dq, dk, dv
 

@@ -7,6 +7,7 @@
 #include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "entmax_attn.h"
 #include "fwd_long.hpp"
@@ -173,6 +174,37 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
 size_t bwd_ws_bytes(int B, int H, int L) {
     const size_t n = static_cast<size_t>(B) * H * L * sizeof(float);
     return (n + 255) & ~static_cast<size_t>(255);
+}
+
+// Scratch of the allocation-free backward (entmax_attn_bwd_noalloc): c_i of
+// up to kScratchRows query rows (B H L), 4 MiB.  Every GPU the library runs
+// on holds one copy until the process ends.  In host code the name stands
+// for a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, once per device (scratch_addr).
+constexpr size_t kScratchRows = static_cast<size_t>(1) << 20;
+static __device__ __align__(256) float scratch[kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device.
+int scratch_addr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ENTMAX_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ENTMAX_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(ENTMAX_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ENTMAX_OK;
 }
 
 }  // namespace
@@ -352,23 +384,17 @@ size_t entmax_attn_bwd_workspace_bytes(int B, int H, int L, int d) {
     return bwd_ws_bytes(B, H, L);
 }
 
-int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
-                        const float* tau, const void* dout, float* dq, float* dk, float* dv,
-                        int B, int H, int Hkv, int L, int d, int dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-    if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv || !workspace)
-        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk, dv and workspace must not be NULL");
-    if (misaligned({q, k, v, dout, dq, dk, dv}, 16) || misaligned({tau}, 4))
-        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned, tau 4-byte aligned");
-    int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
-    if (rc) return rc;
-    if (misaligned({workspace}, 256)) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-    const size_t need = bwd_ws_bytes(B, H, L);
-    if (workspace_bytes < need)
-        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+}  // extern "C"
+
+namespace {
+
+// Backward after the workspace checks: cbuf holds c_i of the B H L query rows.
+int bwd_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+            const float* tau, const void* dout, float* dq, float* dk, float* dv,
+            int B, int H, int Hkv, int L, int d, int dtype, float* cbuf, void* stream) {
     ea::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.cbuf = static_cast<float*>(workspace);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.cbuf = cbuf;
     a.B = B; a.H = H; a.L = L; a.Hkv = Hkv; a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = 0;
@@ -376,6 +402,52 @@ int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == ENTMAX_BF16) return d == 64 ? launch_bwd<ea::DT_BF16, 64>(a, st) : launch_bwd<ea::DT_BF16, 128>(a, st);
     return d == 64 ? launch_bwd<ea::DT_F32, 64>(a, st) : launch_bwd<ea::DT_F32, 128>(a, st);
+}
+
+int bwd_check(const void* q, const void* k, const void* v, const void* tau, const void* dout,
+              const void* dq, const void* dk, const void* dv, int causal, int window,
+              int B, int H, int Hkv, int L, int d, int dtype) {
+    if (!q || !k || !v || !tau || !dout || !dq || !dk || !dv)
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, tau, dout, dq, dk and dv must not be NULL");
+    if (misaligned({q, k, v, dout, dq, dk, dv}, 16) || misaligned({tau}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned, tau 4-byte aligned");
+    return check_common(B, H, Hkv, L, d, dtype, causal, window);
+}
+
+}  // namespace
+
+extern "C" {
+
+int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
+                        const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                        int B, int H, int Hkv, int L, int d, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    int rc = bwd_check(q, k, v, tau, dout, dq, dk, dv, causal, window, B, H, Hkv, L, d, dtype);
+    if (rc) return rc;
+    if (!workspace) return fail(ENTMAX_ERR_INVALID_ARG, "workspace must not be NULL");
+    if (misaligned({workspace}, 256)) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    const size_t need = bwd_ws_bytes(B, H, L);
+    if (workspace_bytes < need)
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype,
+                   static_cast<float*>(workspace), stream);
+}
+
+int entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal,
+                            int window, const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                            int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
+    int rc = bwd_check(q, k, v, tau, dout, dq, dk, dv, causal, window, B, H, Hkv, L, d, dtype);
+    if (rc) return rc;
+    const size_t rows = static_cast<size_t>(B) * H * L;
+    if (rows > kScratchRows)
+        return fail(ENTMAX_ERR_INVALID_ARG, "B*H*L = %zu query rows exceeds the %zu of the built-in scratch",
+                    rows, kScratchRows);
+    void* ws = nullptr;
+    rc = scratch_addr(&ws);
+    if (rc) return rc;
+    // every query row's c_i is written before it is read: nothing to clear
+    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype,
+                   static_cast<float*>(ws), stream);
 }
 
 int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,

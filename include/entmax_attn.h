@@ -134,6 +134,26 @@ int entmax_attn_probs_gqa(const void *q, const void *k,
                           const float *tau, float *probs,
                           int B, int H, int H_kv, int L, int d, int dtype, void *stream);
 
+/* entmax_attn_bwd_noalloc: entmax_attn_bwd_gqa for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * determinism, without the workspace: c_i lives in a scratch array built
+ * into the library (4 MiB per GPU, held from the library's first use on
+ * that GPU until the process ends; its address is looked up once per
+ * device, on the first call there).
+ *  - B * H * L above 1048576 query rows returns ENTMAX_ERR_INVALID_ARG.
+ *  - Calls no hipMalloc, hipFree or allocating library routine.
+ *  - All calls on one GPU share its scratch: two calls in flight at once on
+ *    one GPU (other streams, other host threads) race and give undefined
+ *    results.  Calls on one stream are ordered and safe.
+ */
+int entmax_attn_bwd_noalloc(const void *q, const void *k, const void *v,
+                            const uint8_t *key_mask, int causal, int window,
+                            const float *tau, const void *dout,
+                            float *dq, float *dk, float *dv,
+                            int B, int H, int H_kv, int L, int d, int dtype,
+                            void *stream);
+
 /*
  * Row-wise 1.5-entmax as an op of its own (the pages' entmax15_bisect
  * export, "ADASPLASH -- ROBERTA Benchmark Result", section 4), with the same
