@@ -49,6 +49,11 @@ struct BwdArgs {
     float* dk;
     float* dv;
     float* cbuf;   // [B, H, L] c_i (workspace)
+    // support buckets of the key side (long spans; null otherwise):
+    // kcnt [B, H_kv, L] entries appended per key (zero before the query
+    // side), kflag: set when some query row could not append its entries
+    int* kcnt;
+    int* kflag;
     int B, H, L;
     int Hkv;   // key/value heads (H % Hkv == 0)
     int causal, window;

@@ -23,6 +23,16 @@
 //    dQ_i = scale (sum w dp K - c_i sum w K).  A row whose support outgrows
 //    its lists gets the overflow marker in c_i, and the tile-wise kernel of
 //    bwd.hpp finishes it in fix-up mode.
+//    With support buckets (kcnt non-null), every entry (i, j) with w > 0
+//    also goes to key j's bucket: (query, w, w dp), 16 bytes, at a slot
+//    taken with an integer atomic on kcnt_j, stored in j's dK and dV rows
+//    (still unwritten: KCAP = D/2 slots).
+//  * bwd_kv_gather_kernel: per key, the bucket is put in query order and
+//    summed: dK_j = scale sum (w dp - w c_i) Q_i, dV_j = sum w^2 dO_i.  The
+//    order is fixed by the entries themselves, not by the atomics, so
+//    repeated calls give identical bits.  A key whose bucket overflowed is
+//    left to bwd_kv_kernel in fix-up mode (all keys when some query row
+//    overflowed its list and emitted nothing).
 //  * bwd_kv_kernel (keys stationary, query rows streamed): the same scores
 //    transposed; the support entries of each key (query index, w) go to the
 //    key's list.  A list that cannot take a tile's entries is flushed (the
@@ -104,6 +114,12 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
         ovf[f] = false;
     }
     const bool allrows = rbase + NF * 16 <= L;
+    // support buckets of the key side: query head within its group, and the
+    // key/value head's dK, dV rows and counters
+    const unsigned hq16 = static_cast<unsigned>((bh - b * a.H) % (a.H / a.Hkv)) << 16;
+    int* kch = a.kcnt != nullptr ? a.kcnt + static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L : nullptr;
+    float* dkb = a.dk + kv_off;
+    float* dvb = a.dv + kv_off;
     // this lane's list of row f: entries (w, key bits) in the row's dQ
     auto lst = [&](int f, int lane_g) {
         return reinterpret_cast<f32x2*>(dqh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g * SUB;
@@ -244,6 +260,15 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
                         X[d] = fmaf(wdp, kr[j].at(d), X[d]);
                         Y[d] = fmaf(w[j], kr[j].at(d), Y[d]);
                     }
+                    // the list's own lane hands the entry to key j's bucket
+                    if (kch != nullptr && g == g2 && e0 + j < n2 && w[j] > 0.f) {
+                        const int slot = atomicAdd(kch + key[j], 1);
+                        if (slot < D / 2) {
+                            float* dst = (slot < D / 4 ? dkb : dvb) + static_cast<size_t>(key[j]) * D + 4 * (slot % (D / 4));
+                            *reinterpret_cast<u32x4*>(dst) =
+                                u32x4{hq16 | static_cast<unsigned>(row), __float_as_uint(w[j]), __float_as_uint(wdp), 0u};
+                        }
+                    }
                 }
             }
         }
@@ -251,7 +276,10 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
         __builtin_amdgcn_wave_barrier();
         if (row < L) {
             if (rovf) {
-                if (g == 0) reinterpret_cast<unsigned*>(ch)[row] = kCMarker;   // finished by the fix-up pass
+                if (g == 0) {
+                    reinterpret_cast<unsigned*>(ch)[row] = kCMarker;   // finished by the fix-up pass
+                    if (a.kflag != nullptr) *a.kflag = 1;             // its entries are in no bucket
+                }
             } else {
                 const float cc = sw > 0.f ? swdp / sw : 0.f;
                 float* dst = dqh + static_cast<size_t>(row) * D + g * DQ;
@@ -262,6 +290,115 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
                               a.scale * fmaf(-cc, Y[d + 2], X[d + 2]), a.scale * fmaf(-cc, Y[d + 3], X[d + 3])};
                 if (g == 0) ch[row] = cc;
             }
+        }
+    }
+}
+
+// ============================================================================
+// Key side from the support buckets
+// ============================================================================
+// D/8 lanes per key (8 features each), 256/(D/8) keys per workgroup.  grid:
+// B H_kv ceil(L / keys per workgroup).
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void bwd_kv_gather_kernel(BwdArgs a) {
+    typedef typename InT<DT>::type T;
+    constexpr int KCAP = D / 2;      // bucket slots per key
+    constexpr int LPK = D / 8;       // lanes per key
+    constexpr int FPL = 8;           // features per lane
+    constexpr int EPL = KCAP / LPK;  // bucket slots per lane while ordering
+    constexpr int KPB = kThreads / LPK;
+    constexpr int UB = 4;            // entries gathered per batch
+    __shared__ u32x4 srt[KPB][KCAP];
+    if (*a.kflag != 0) return;       // uniform: the recompute kernel does every key
+
+    const int L = a.L;
+    const int nkg = (L + KPB - 1) / KPB;
+    const int total = a.B * a.Hkv * nkg;
+    const int wi = xcd_swizzle(blockIdx.x, total);
+    const int bkv = wi / nkg;
+    const int b = bkv / a.Hkv;
+    const int hk = bkv - b * a.Hkv;
+    const int rep = a.H / a.Hkv;
+    const int tid = threadIdx.x;
+    const int ks = tid / LPK;        // key slot in the workgroup
+    const int l = tid % LPK;
+    const int key = (wi - bkv * nkg) * KPB + ks;
+    const bool kin = key < L;
+    const size_t kv_off = static_cast<size_t>(bkv) * L * D;
+    float* dkr = a.dk + kv_off + static_cast<size_t>(kin ? key : 0) * D;
+    float* dvr = a.dv + kv_off + static_cast<size_t>(kin ? key : 0) * D;
+    const int n = kin ? a.kcnt[static_cast<size_t>(bkv) * L + key] : 0;
+    const bool mine = kin && n <= KCAP;   // else the recompute kernel writes this key
+    const int ne = mine ? n : 0;
+
+    // bucket slots l, l + 16, ...; rank of each = entries with a smaller
+    // (query head, query) code, all codes of one bucket being distinct
+    u32x4 e[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int s = l + LPK * r;
+        const float* src = (s < D / 4 ? dkr : dvr) + 4 * (s % (D / 4));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        e[r] = s < ne ? v : u32x4{0xFFFFFFFFu, 0u, 0u, 0u};
+    }
+    int rank[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) rank[r] = 0;
+    const int nw = wave_max_int<kWave>(ne);
+    const int gb = (tid % kWave) & ~(LPK - 1);   // first lane of this key's group
+#pragma unroll
+    for (int r2 = 0; r2 < EPL; ++r2) {
+        if (LPK * r2 >= nw) break;   // uniform
+#pragma unroll 4
+        for (int l2 = 0; l2 < LPK; ++l2) {
+            const unsigned o = static_cast<unsigned>(__shfl(static_cast<int>(e[r2][0]), gb + l2, kWave));
+#pragma unroll
+            for (int r = 0; r < EPL; ++r) rank[r] += o < e[r][0] ? 1 : 0;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < EPL; ++r)
+        if (l + LPK * r < ne) srt[ks][rank[r]] = e[r];
+    wave_sync();   // a key's lanes share one wave
+
+    float dk[FPL], dv[FPL];
+#pragma unroll
+    for (int d = 0; d < FPL; ++d) { dk[d] = 0.f; dv[d] = 0.f; }
+    const size_t hstride = static_cast<size_t>(L) * D;
+    const T* q0 = static_cast<const T*>(a.q) + static_cast<size_t>(b * a.H + hk * rep) * hstride + l * FPL;
+    const T* o0 = static_cast<const T*>(a.dout) + static_cast<size_t>(b * a.H + hk * rep) * hstride + l * FPL;
+    const float* c0 = a.cbuf + static_cast<size_t>(b * a.H + hk * rep) * L;
+    for (int e0 = 0; e0 < nw; e0 += UB) {
+        float w[UB], wdp[UB], ci[UB];
+        RowSlice<DT, FPL> qr[UB], orr[UB];
+#pragma unroll
+        for (int j = 0; j < UB; ++j) {
+            const bool in = e0 + j < ne;
+            const u32x4 en = srt[ks][in ? e0 + j : 0];
+            const unsigned code = in ? en[0] : 0u;
+            const size_t qrow = static_cast<size_t>(code >> 16) * L + (code & 0xFFFFu);
+            w[j] = in ? __uint_as_float(en[1]) : 0.f;
+            wdp[j] = in ? __uint_as_float(en[2]) : 0.f;
+            qr[j].load(q0 + qrow * D);
+            orr[j].load(o0 + qrow * D);
+            ci[j] = c0[qrow];
+        }
+#pragma unroll
+        for (int j = 0; j < UB; ++j) {
+            const float ds = a.scale * fmaf(-w[j], ci[j], wdp[j]);
+            const float p = w[j] * w[j];
+#pragma unroll
+            for (int d = 0; d < FPL; ++d) {
+                dk[d] = fmaf(ds, qr[j].at(d), dk[d]);
+                dv[d] = fmaf(p, orr[j].at(d), dv[d]);
+            }
+        }
+    }
+    if (mine) {
+#pragma unroll
+        for (int d = 0; d < FPL; d += 4) {
+            *reinterpret_cast<f32x4*>(dkr + l * FPL + d) = f32x4{dk[d], dk[d + 1], dk[d + 2], dk[d + 3]};
+            *reinterpret_cast<f32x4*>(dvr + l * FPL + d) = f32x4{dv[d], dv[d + 1], dv[d + 2], dv[d + 3]};
         }
     }
 }
@@ -316,8 +453,19 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_kv_kerne
     }
     const int ch0 = qlo / CK, ch1 = qlo < qhi ? (qhi + CK - 1) / CK : ch0;
 
+    // fix-up mode (after the bucket gather): only keys whose bucket
+    // overflowed, or every key when some query row emitted no entries
+    const bool every = !a.fixup || *a.kflag != 0;   // uniform
+    const int* kcb = a.kcnt != nullptr ? a.kcnt + static_cast<size_t>(bkv) * L : nullptr;
+    if (!every) {
+        const int kt0 = k0 + tid;
+        const bool over = tid < C::BR && kt0 < L && kcb[kt0] > D / 2;
+        if (!__syncthreads_or(over)) return;
+    }
+
     QFrag<DT, D> kf[NF];   // stationary keys in the B-operand layout
     bool kok[NF];
+    bool kwr[NF];          // this call writes the key's rows
     int cnt[NF];           // entries in the key's list (the same in its four lanes)
     bool written[NF];
 #pragma unroll
@@ -326,6 +474,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_kv_kerne
         kf[f].load(kh, key, L, g);
         const uint8_t mb = km != nullptr ? km[clamp_row(key, L)] : uint8_t(1);
         kok[f] = key < L && mb != 0;
+        kwr[f] = key < L && (every || kcb[key] > D / 2);
         cnt[f] = 0;
         written[f] = false;
     }
@@ -393,7 +542,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_kv_kerne
                     }
                 }
             }
-            if (key < L && (n > 0 || (final_write && !written[f]))) {
+            if (kwr[f] && (n > 0 || (final_write && !written[f]))) {
                 float* dkr = dkh + static_cast<size_t>(key) * D + g * DQ;
                 float* dvr = dvh + static_cast<size_t>(key) * D + g * DQ;
 #pragma unroll

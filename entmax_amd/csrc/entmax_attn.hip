@@ -140,8 +140,11 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
 }
 
 // Backward: query side (dQ, c) then key side (dK, dV), all on one stream.
-// Spans beyond 2048 keys take the wide query-side kernel, whose rows with an
-// overflowing support are finished by the tile kernel in fix-up mode.
+// Spans beyond 2048 keys take the wide query-side kernel, which also fills
+// the support buckets of the key side; its rows with an overflowing support
+// are finished by the tile kernel in fix-up mode, and keys whose bucket
+// overflowed by the key-side recompute kernel in fix-up mode.  Shorter spans
+// take the tile kernel and the key-side recompute kernel.
 template <int DT, int D>
 int launch_bwd(ea::BwdArgs a, hipStream_t st) {
     typedef ea::WideCfg<DT, D> W;
@@ -155,34 +158,51 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
     if (rc) return rc;
     const int L = a.L;
     const int nt64 = (L + 63) / 64;
-    if (max_span(L, 64, a.causal, a.window) > 2048) {
+    const bool wide = max_span(L, 64, a.causal, a.window) > 2048;
+    if (wide) {
+        // bucket counters and the flag start at zero (a fill kernel, so that
+        // the sequence can be captured in a graph)
+        const size_t nz = static_cast<size_t>(reinterpret_cast<char*>(a.kflag) - reinterpret_cast<char*>(a.kcnt)) / 4 + 64;
+        hipLaunchKernelGGL(ea::zero_fill_kernel, dim3(static_cast<unsigned>((nz / 4 + ea::kThreads) / ea::kThreads)),
+                           dim3(ea::kThreads), 0, st, reinterpret_cast<float*>(a.kcnt), nz);
         a.nqt = (L + W::BR - 1) / W::BR;
         a.fixup = 0;
         hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
         a.fixup = 1;
     } else {
+        a.kcnt = nullptr;
+        a.kflag = nullptr;
         a.fixup = 0;
     }
     a.nqt = nt64;
     hipLaunchKernelGGL(kq, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), lds_q, st, a);
+    if (wide) {
+        constexpr int kpb = ea::kThreads / (D / 8);   // keys per gather workgroup
+        const unsigned ng = static_cast<unsigned>(a.B * a.Hkv * ((L + kpb - 1) / kpb));
+        hipLaunchKernelGGL((ea::bwd_kv_gather_kernel<DT, D>), dim3(ng), dim3(ea::kThreads), 0, st, a);
+    }
     a.nqt = (L + W::BR - 1) / W::BR;   // key tiles per key/value head
     hipLaunchKernelGGL(kv, dim3(a.B * a.Hkv * a.nqt), dim3(ea::kThreads), W::lds_bytes, st, a);
     return check_launch("bwd");
 }
 
-// Workspace of the backward: c_i per query row, 256-byte aligned size.
-size_t bwd_ws_bytes(int B, int H, int L) {
+// Workspace of the backward: c_i per query row, then a bucket counter per
+// key (sized by the query heads, which bound the key/value heads), then the
+// overflow flag; each part 256-byte aligned.
+size_t bwd_ws_part(int B, int H, int L) {
     const size_t n = static_cast<size_t>(B) * H * L * sizeof(float);
     return (n + 255) & ~static_cast<size_t>(255);
 }
+size_t bwd_ws_bytes(int B, int H, int L) { return 2 * bwd_ws_part(B, H, L) + 256; }
 
-// Scratch of the allocation-free backward (entmax_attn_bwd_noalloc): c_i of
-// up to kScratchRows query rows (B H L), 4 MiB.  Every GPU the library runs
-// on holds one copy until the process ends.  In host code the name stands
-// for a host-side stand-in: the device address comes from
+// Scratch of the allocation-free backward (entmax_attn_bwd_noalloc): the
+// backward's workspace for up to kScratchRows query rows (B H L): c_i and a
+// bucket counter per row, and a flag, 8 MiB + 256 bytes.  Every GPU the
+// library runs on holds one copy until the process ends.  In host code the
+// name stands for a host-side stand-in: the device address comes from
 // hipGetSymbolAddress, once per device (scratch_addr).
 constexpr size_t kScratchRows = static_cast<size_t>(1) << 20;
-static __device__ __align__(256) float scratch[kScratchRows];
+static __device__ __align__(256) float scratch[2 * kScratchRows + 64];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -388,13 +408,18 @@ size_t entmax_attn_bwd_workspace_bytes(int B, int H, int L, int d) {
 
 namespace {
 
-// Backward after the workspace checks: cbuf holds c_i of the B H L query rows.
+// Backward after the workspace checks: ws is a workspace of bwd_ws_bytes.
 int bwd_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
             const float* tau, const void* dout, float* dq, float* dk, float* dv,
-            int B, int H, int Hkv, int L, int d, int dtype, float* cbuf, void* stream) {
+            int B, int H, int Hkv, int L, int d, int dtype, void* ws, void* stream) {
     ea::BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.cbuf = cbuf;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    char* w = static_cast<char*>(ws);
+    const size_t part = bwd_ws_part(B, H, L);
+    a.cbuf = reinterpret_cast<float*>(w);
+    a.kcnt = reinterpret_cast<int*>(w + part);
+    a.kflag = reinterpret_cast<int*>(w + 2 * part);
     a.B = B; a.H = H; a.L = L; a.Hkv = Hkv; a.causal = causal ? 1 : 0; a.window = window;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = 0;
@@ -429,8 +454,8 @@ int entmax_attn_bwd_gqa(const void* q, const void* k, const void* v, const uint8
     const size_t need = bwd_ws_bytes(B, H, L);
     if (workspace_bytes < need)
         return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype,
-                   static_cast<float*>(workspace), stream);
+    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype, workspace,
+                   stream);
 }
 
 int entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal,
@@ -445,9 +470,9 @@ int entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const u
     void* ws = nullptr;
     rc = scratch_addr(&ws);
     if (rc) return rc;
-    // every query row's c_i is written before it is read: nothing to clear
-    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype,
-                   static_cast<float*>(ws), stream);
+    // c_i of every query row is written before it is read, and the bucket
+    // counters are cleared by the call itself (a fill kernel)
+    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype, ws, stream);
 }
 
 int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,

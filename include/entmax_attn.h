@@ -83,12 +83,16 @@ int entmax_attn_fwd(const void *q, const void *k, const void *v,
  * Required: q, k, v, tau, dout, dq, dk, dv, workspace.  Optional: key_mask.
  *  - workspace: caller-owned DEVICE memory, 256-byte aligned, of at least
  *    entmax_attn_bwd_workspace_bytes(B, H, L, d) bytes (c_i of every query
- *    row); no initialisation needed, scratch after the call.  Two calls in
+ *    row, a support counter per key, a flag: 8 B H L bytes plus at most
+ *    768); no initialisation needed, scratch after the call.  Two calls in
  *    flight must not share a workspace.  A too small or misaligned
  *    workspace returns ENTMAX_ERR_INVALID_ARG.
- *  - Deterministic: query rows (dq, c) and key rows (dk, dv) are each
- *    owned by one workgroup and summed in a fixed order (no atomics), so
- *    repeated calls on the same inputs give identical bits.
+ *  - dk and dv serve as scratch until the call completes (for key spans
+ *    above 2048, each key's support entries are collected in its own rows).
+ *  - Deterministic: every row of dq, dk and dv is summed by one thread
+ *    group in an order fixed by the data (query rows by key index, key rows
+ *    by query index), never by float atomics, so repeated calls on the same
+ *    inputs give identical bits.
  */
 size_t entmax_attn_bwd_workspace_bytes(int B, int H, int L, int d);
 int entmax_attn_bwd(const void *q, const void *k, const void *v,
@@ -138,9 +142,9 @@ int entmax_attn_probs_gqa(const void *q, const void *k,
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  Same arguments, results and
  * determinism, without the workspace: c_i lives in a scratch array built
- * into the library (4 MiB per GPU, held from the library's first use on
- * that GPU until the process ends; its address is looked up once per
- * device, on the first call there).
+ * into the library (8 MiB + 256 bytes per GPU, held from the library's
+ * first use on that GPU until the process ends; its address is looked up
+ * once per device, on the first call there).
  *  - B * H * L above 1048576 query rows returns ENTMAX_ERR_INVALID_ARG.
  *  - Calls no hipMalloc, hipFree or allocating library routine.
  *  - All calls on one GPU share its scratch: two calls in flight at once on

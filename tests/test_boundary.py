@@ -81,9 +81,10 @@ def _bwd_args(lib, B=1, H=1, L=8, d=64):
 
 
 def test_bwd_workspace_size(lib):
-    # c_i of every query row, rounded up to 256 bytes
-    assert lib.entmax_attn_bwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 4
-    assert lib.entmax_attn_bwd_workspace_bytes(2, 3, 7, 64) == 256
+    # c_i of every query row and a bucket counter per row, each rounded up
+    # to 256 bytes, then 256 bytes for the overflow flag
+    assert lib.entmax_attn_bwd_workspace_bytes(1, 32, 8192, 128) == 2 * 32 * 8192 * 4 + 256
+    assert lib.entmax_attn_bwd_workspace_bytes(2, 3, 7, 64) == 3 * 256
     assert lib.entmax_attn_bwd_workspace_bytes(0, 3, 7, 64) == 0
     assert lib.entmax_attn_bwd_workspace_bytes(1, 1, -1, 64) == 0
 
