@@ -11,6 +11,7 @@
 
 #include "entmax_attn.h"
 #include "fwd_long.hpp"
+#include "fwd_reg.hpp"
 #include "fwd_short.hpp"
 #include "fwd_wide.hpp"
 #include "probs.hpp"
@@ -118,6 +119,33 @@ int launch_long(ea::FwdArgs a, hipStream_t st) {
 }
 
 template <int DT, int D>
+int launch_reg(ea::FwdArgs a, hipStream_t st) {
+    typedef ea::RegCfg<DT, D> C;
+    auto kern = ea::fwd_reg_kernel<DT, D>;
+    int rc = set_lds(kern, C::lds_bytes);
+    if (rc) return rc;
+    a.nqt = (a.L + C::BM - 1) / C::BM;
+    const long long grid = static_cast<long long>(a.B) * a.H * a.nqt;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(ea::kThreads), C::lds_bytes, st, a);
+    return check_launch("fwd_reg");
+}
+
+// The register-held kernel takes a tile of 32 rows when the 128-key pairs
+// its rows may attend number at most 8.
+bool reg_fits(int L, int causal, int window) {
+    const int bm = 32, pk = 128;
+    if (!causal || window <= 0) return (L + pk - 1) / pk <= 8;
+    int worst = 0;
+    for (int q0 = 0; q0 < L; q0 += bm) {
+        int lo, hi;
+        ea::key_range(q0, bm, L, causal, window, &lo, &hi);
+        const int n = lo < hi ? (hi + pk - 1) / pk - lo / pk : 0;
+        worst = n > worst ? n : worst;
+    }
+    return worst <= 8;
+}
+
+template <int DT, int D>
 int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
     const int L = a.L;
     const int s64 = max_span(L, 64, a.causal, a.window);
@@ -136,6 +164,9 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
     // gather over the support (the multi-pass long-span kernel re-reads K
     // and V more than it saves there)
     if (s64 > 2048) return launch_wide<DT, D>(a, st);
+    // (float32 at d = 128 would not keep its scores in registers)
+    if constexpr (!(DT == ea::DT_F32 && D == 128))
+        if (reg_fits(L, a.causal, a.window)) return launch_reg<DT, D>(a, st);
     return launch_long<DT, D>(a, st);
 }
 
