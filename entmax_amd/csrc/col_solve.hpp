@@ -284,6 +284,58 @@ __device__ __forceinline__ float col_solve(const f32x4 (&sv)[NT], int t0, int t1
     return col_finish<KMAX>(col, len, s);
 }
 
+// Threshold of a row whose scores all sit in registers of its four lanes
+// (tiles [t0, t1) of sv; -inf where excluded), by Newton steps on
+// sqrt(g(t)) - 1 from the exact root over the four lane maxima (a lower
+// bound).  sqrt(g) is the Euclidean norm of [x - t]_+, convex and
+// decreasing in t, so every iterate stays at or below the root t*; a row
+// stops once its step is below 1e-5, the error then being of the order of
+// the step squared over the mean excess.  Returns the centre of the 25-step
+// bisection's dyadic cell of [-1, -1/sqrt(n)] that holds t* (half-scaled,
+// shifted domain; tau = 2 (mc2 + t)), equal in the four lanes of the row.
+// Must be called by every lane of the wave.
+template <int NT>
+__device__ __forceinline__ float col_newton(const f32x4 (&sv)[NT], int t0, int t1, float c2, float mc2, float n,
+                                           float xlmax) {
+    const bool empty = n == 0.f;
+    const float hi = -__builtin_amdgcn_rsqf(empty ? 1.f : n);
+    float t = fminf(fmaxf(col_lower_bound(xlmax), -1.f), hi);
+    bool done = empty || n <= 1.f;   // n = 1: the root is the lower end -1
+    for (int r = 0; r < 16 && __any(!done); ++r) {
+        const float bias = -(mc2 + t);
+        float s1 = 0.f, s2 = 0.f, u1 = 0.f, u2 = 0.f;   // two chains each
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            if (k < t0 || k >= t1) continue;   // uniform: -inf there
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y = relu1(fmaf(sv[k][i], c2, bias));
+                if (i & 1) {
+                    u1 += y;
+                    u2 = fmaf(y, y, u2);
+                } else {
+                    s1 += y;
+                    s2 = fmaf(y, y, s2);
+                }
+            }
+        }
+        s1 = col4_sum(s1 + u1);
+        s2 = col4_sum(s2 + u2);
+        if (!done) {
+            const float rg = __builtin_amdgcn_sqrtf(s2);
+            const float step = (rg - 1.f) * rg * __builtin_amdgcn_rcpf(s1);
+            t = fminf(t + fmaxf(step, 0.f), hi);
+            done = step < 1e-5f;
+        }
+    }
+    if (empty || n <= 1.f) return -1.f;
+    ColState st;
+    st.lo = -1.f;
+    st.hi = hi;
+    st.it = 0;
+    return col_dyadic(st, t);
+}
+
 // From a state whose band (entries in (lo, hi] above lb, at most KMAX per
 // lane) sits in the scratch column: one stage of bisection steps, then the
 // exact finish on what is left of the band.  Returns t (half-scaled,

@@ -31,6 +31,8 @@
 // wave's rows are skipped by that wave.
 #pragma once
 
+#include <type_traits>
+
 #include "col_solve.hpp"
 #include "common.hpp"
 #include "fwd_short.hpp"
@@ -174,34 +176,49 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             if (jp + 1 < j1) prefetch(jp + 1, kc, pr);
             const char* kb = buf + (jj & 1) * C::buf_bytes + (64 * hf + c) * C::KSTR + 16 * g;
             const int cb = jp * PK + 64 * hf;
+            // a clean chunk (every key valid, no causal / window bound
+            // crossing the wave's rows, every row a query row: uniform) takes
+            // plain products and no masking
+            const bool cross = a.causal && (cb + 63 > rbase || (a.window > 0 && cb <= rbase + 15 - a.window));
+            auto tiles = [&](auto clean_tag) {
+                constexpr bool CLEAN = decltype(clean_tag)::value;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
-                const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
-                f32x4 sv = {-kInf, -kInf, -kInf, -kInf};
-                if (ok) {
-                    KFrag<DT, D> kf;
-                    kf.load_lds_at(kb + 16 * t * C::KSTR);
-                    sv = mb == 0xFFFFu ? kf.st(qf) : kf.st_bias(qf, ((mb >> c) & 1u) ? 0u : kMaskedBits, g);
-                    if (a.causal) {
+                for (int t = 0; t < 4; ++t) {
+                    f32x4 sv = {-kInf, -kInf, -kInf, -kInf};
+                    if constexpr (CLEAN) {
+                        KFrag<DT, D> kf;
+                        kf.load_lds_at(kb + 16 * t * C::KSTR);
+                        sv = kf.st(qf);
+                        mlane = fmaxf(mlane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+                    } else {
+                        const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
+                        const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
+                        if (ok) {
+                            KFrag<DT, D> kf;
+                            kf.load_lds_at(kb + 16 * t * C::KSTR);
+                            sv = kf.st_bias(qf, ((mb >> c) & 1u) ? 0u : kMaskedBits, g);
+                            if (a.causal) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = cb + 16 * t + 4 * g + i;
-                            sv[i] = ((key <= khi_i) & (key > klo_i)) ? sv[i] : -kInf;
+                                for (int i = 0; i < 4; ++i) {
+                                    const int key = cb + 16 * t + 4 * g + i;
+                                    sv[i] = ((key <= khi_i) & (key > klo_i)) ? sv[i] : -kInf;
+                                }
+                            }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sv[i] = rowok ? sv[i] : -kInf;
+                            mlane = fmaxf(mlane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+                            if (a.causal) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) nl += sv[i] > -1e29f ? 1.f : 0.f;
+                            }
                         }
                     }
-                    if (!allrows) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sv[i] = rowok ? sv[i] : -kInf;
-                    }
-                    mlane = fmaxf(mlane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-                    if (a.causal) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) nl += sv[i] > -1e29f ? 1.f : 0.f;
-                    }
+                    S[4 * jj + t] = sv;
                 }
-                S[4 * jj + t] = sv;
-            }
+            };
+            if (M == ~0ull && !cross && allrows) tiles(std::true_type{});
+            else tiles(std::false_type{});
+            if (a.causal && M == ~0ull && !cross && allrows) nl += 16.f;   // four clean tiles: 16 keys of this lane
             if (!a.causal) nl += static_cast<float>(__popcll(M));
             if (jp + 1 < j1) {
                 stage_k((jj + 1) & 1, pr);
@@ -250,22 +267,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
 #pragma unroll 1
     for (int r = 0; r < C::kRounds && go; ++r) {
         const float bias = -(mc2 + t);
-        float s1 = 0.f, s2 = 0.f, u1 = 0.f, u2 = 0.f;   // two chains each
+        float s1 = 0.f, s2 = 0.f;
+        // a wave whose rows are all done skips the pass (its partner wave,
+        // with the same rows, skips it too)
+        if (__any(!done)) {
+            float u1 = 0.f, u2 = 0.f;   // two chains each
 #pragma unroll
-        for (int k = 0; k < NT; ++k)
+            for (int k = 0; k < NT; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y = relu1(fmaf(S[k][i], c2, bias));
-                if (i & 1) {
-                    u1 += y;
-                    u2 = fmaf(y, y, u2);
-                } else {
-                    s1 += y;
-                    s2 = fmaf(y, y, s2);
+                for (int i = 0; i < 4; ++i) {
+                    const float y = relu1(fmaf(S[k][i], c2, bias));
+                    if (i & 1) {
+                        u1 += y;
+                        u2 = fmaf(y, y, u2);
+                    } else {
+                        s1 += y;
+                        s2 = fmaf(y, y, s2);
+                    }
                 }
-            }
-        s1 = col4_sum(s1 + u1);
-        s2 = col4_sum(s2 + u2);
+            s1 = col4_sum(s1 + u1);
+            s2 = col4_sum(s2 + u2);
+        }
         const f32x4 pp = exchange(f32x4{s1, s2, 0.f, 0.f});
         if (!done) {
             // the same sums in both waves of the row group (addition commutes)

@@ -312,8 +312,7 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
     // ---- 2. tau ----------------------------------------------------------------------------
     const float c2 = 0.5f * a.scale;
     const float mc2 = empty ? 0.f : mraw * c2;
-    float* col = scratch + wv * (KC * kWave) + lane;
-    float tr = col_solve<NT, KC>(sv, t0, t1, c2, mc2, empty ? 1.f : n, fmaf(mlane, c2, -mc2), col);
+    float tr = col_newton<NT>(sv, t0, t1, c2, mc2, n, fmaf(mlane, c2, -mc2));
     if (a.tau != nullptr && g == 0 && rowok) a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tr);
     const float sh = empty ? 0.f : mc2 + tr;   // p = clamp(acc c2 - sh)^2; empty rows have acc = -inf
 
