@@ -39,6 +39,7 @@ from .entmax15 import (  # noqa: F401
 )
 from .entmax_alpha import (  # noqa: F401
     entmax_alpha_backward,
+    entmax_alpha_vjp,
     entmax_alpha_bisect,
     entmax_alpha_exact,
     tsallis_objective,

@@ -136,6 +136,26 @@ def entmax_alpha_backward(s, dp, alpha, allowed=None):
     return ds[0] if np.ndim(s) == 1 else ds
 
 
+def entmax_alpha_vjp(p, dp, alpha):
+    """The backward of entmax_alpha_backward taken at a given output p (each
+    row a point of the simplex): w = p^(2 - alpha) on the support p > 0 (zero
+    off it) and ds = w * dp - w * (w . dp) / sum(w) (section 2.4's Jacobian in
+    the general-alpha form of section 2.2's stationarity).  At the exact p it
+    is entmax_alpha_backward; at the p of another solve it is the gradient
+    that solve's output leads to, which separates the backward's own
+    arithmetic from the conditioning of w in tau (for alpha > 1.5 the slope
+    of w is unbounded at the support boundary, and at alpha = 2 w is the
+    support indicator).  Rows with no support get ds = 0.
+    """
+    _check_alpha(alpha)
+    p = np.atleast_2d(np.asarray(p, dtype=np.float64))
+    dp = np.atleast_2d(np.asarray(dp, dtype=np.float64))
+    w = np.where(p > 0, np.where(p > 0, p, 1.0) ** (2.0 - alpha), 0.0)
+    den = w.sum(axis=1, keepdims=True)
+    c = np.where(den > 0, (w * dp).sum(axis=1, keepdims=True) / np.where(den > 0, den, 1.0), 0.0)
+    return w * (dp - c)
+
+
 def tsallis_objective(p, s, alpha):
     """p.s + H_alpha(p), H_alpha(p) = sum (p - p^alpha) / (alpha (alpha - 1))
     ("ADASPLASH -- ROBERTA Benchmark Result", section 2.1); alpha-entmax is

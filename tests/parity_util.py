@@ -139,3 +139,33 @@ def check_backward(inp, heads=None, label="", tau=None):
     for name in ("dq", "dk", "dv"):
         assert errs[name] <= tol, errs
     return errs
+
+
+def chain_rows_ok(s64, tau_gpu, tau_ref, alpha, ok=None, slope_err=1e-6):
+    """Rows whose alpha-entmax backward is well conditioned in tau at the
+    forward's error: no allowed entry so close to the exact tau that the
+    weight w = p^(2 - alpha) = [(alpha - 1)(s - tau)]^k, k = (2 - alpha)/(alpha - 1),
+    moves by more than ``slope_err`` under that row's tau error.  For
+    alpha <= 1.5 (k >= 1) w is Lipschitz and every row qualifies; for
+    1.5 < alpha < 2 the band is where k (alpha - 1)^k delta^(k - 1) eps
+    exceeds slope_err; at alpha = 2 (w an indicator) it is twice the error;
+    never below 1e-6 max(1, |tau|), the float32 resolution of the scores."""
+    s64 = np.atleast_2d(s64)
+    eps = np.abs(np.asarray(tau_gpu, np.float64) - np.asarray(tau_ref, np.float64))
+    fin = np.isfinite(tau_ref)
+    eps = np.where(fin, eps, 0.0)
+    if alpha <= 1.5:
+        return np.ones(s64.shape[0], bool), np.zeros(s64.shape[0])
+    k = (2.0 - alpha) / (alpha - 1.0)
+    if k == 0.0:
+        band = 2.0 * eps
+    else:
+        with np.errstate(divide="ignore"):
+            band = np.where(eps > 0, (slope_err / (k * (alpha - 1.0) ** k * np.maximum(eps, 1e-300))) ** (1.0 / (k - 1.0)), 0.0)
+    # and at least the float32 resolution of the scores near tau, where the
+    # two sides may round an entry to opposite sides of it
+    band = np.maximum(np.maximum(band, 2.0 * eps), 1e-6 * np.maximum(1.0, np.abs(np.where(fin, tau_ref, 0.0))))
+    allowed = np.ones_like(s64, bool) if ok is None else np.atleast_2d(ok)
+    dist = np.abs(s64 - np.where(fin, tau_ref, 0.0)[:, None])
+    near = ((dist < band[:, None]) & allowed).any(axis=1)
+    return fin & ~near | ~fin, band

@@ -13,6 +13,7 @@ from oracle import (
     entmax15_backward,
     entmax15_exact,
     entmax_alpha_backward,
+    entmax_alpha_vjp,
     entmax_alpha_bisect,
     entmax_alpha_exact,
     tsallis_objective,
@@ -159,6 +160,25 @@ def test_backward_alpha15_matches():
     allowed = rng.random(s.shape) > 0.2
     np.testing.assert_allclose(entmax_alpha_backward(s, dp, 1.5, allowed),
                                entmax15_backward(s, dp, allowed), atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.75, 2.0])
+def test_vjp_at_exact_p_is_the_gradient(alpha):
+    # at the exact output: the finite-difference gradient of alpha-entmax
+    rng = np.random.default_rng(int(alpha * 100) + 7)
+    s = rng.normal(size=12)
+    dp = rng.normal(size=12)
+    p, _ = entmax_alpha_exact(s, alpha)
+    ds = entmax_alpha_vjp(p, dp, alpha)[0]
+    np.testing.assert_allclose(ds, _fd_jacobian(s, alpha).T @ dp, atol=1e-6)
+
+
+def test_vjp_sparsemax_closed_form():
+    # alpha = 2 (sparsemax): w is the support indicator, so ds = dp minus its
+    # mean over the support, and zero off it; a row without support gets 0
+    p = np.array([[0.75, 0.25, 0.0], [0.0, 0.0, 0.0]])
+    dp = np.array([[1.0, -2.0, 5.0], [1.0, 2.0, 3.0]])
+    np.testing.assert_allclose(entmax_alpha_vjp(p, dp, 2.0), [[1.5, -1.5, 0.0], [0.0, 0.0, 0.0]], atol=1e-15)
 
 
 def test_rejects_alpha_outside():
