@@ -35,6 +35,7 @@ from .entmax15 import (  # noqa: F401
     attention_forward,
     attention_backward,
     attention_decode,
+    attention_decode_backward,
     tsallis15_objective,
 )
 from .entmax_alpha import (  # noqa: F401

@@ -354,3 +354,52 @@ def attention_decode(q, k_cache, v_cache, seqlens, window=0, causal=True):
     if single:
         return out[:, :, 0], tau[:, :, 0]
     return out, tau
+
+
+def attention_decode_backward(q, k_cache, v_cache, dout, seqlens, window=0, causal=True):
+    """Gradients of ``attention_decode`` w.r.t. q, k_cache and v_cache.
+
+    The same Jacobian as ``attention_backward`` ("ADASPLASH -- ROBERTA
+    Benchmark Result", section 2.4): per query row with p = entmax15(s) over
+    its allowed keys, w = sqrt(p), dp_j = dO . v_j, c = sum w dp / sum w,
+    dS_j = w_j (dp_j - c); dq = dS K / sqrt(d), and every row adds
+    dS_j q / sqrt(d) to dk_j and p_j dO to dv_j of its key/value head.
+    Keys no query may attend (past n_b, or outside every window) get zero.
+
+    Arguments as ``attention_decode`` plus dout shaped like q.  Returns
+    (dq, dk, dv): dq like q, dk and dv like the caches, float64.
+    """
+    q, k, v, do = _as64(q), _as64(k_cache), _as64(v_cache), _as64(dout)
+    single = q.ndim == 3
+    if window > 0 and not causal:
+        raise ValueError("the splash window is only defined for causal attention")
+    if single:
+        q, do = q[:, :, None, :], do[:, :, None, :]
+    B, H, Lq, d = q.shape
+    S = k.shape[2]
+    rep = H // k.shape[1]
+    sl = np.asarray(seqlens.detach().cpu().numpy() if hasattr(seqlens, "detach") else seqlens)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    sc = 1.0 / np.sqrt(d)
+    for b in range(B):
+        n = int(min(max(int(sl[b]), 0), S))
+        for i in range(Lq):
+            pos = n - Lq + i if causal else n - 1
+            if pos < 0:
+                continue
+            lo = max(0, pos - window + 1) if window > 0 else 0
+            for h in range(H):
+                kh, vh = k[b, h // rep, lo:pos + 1], v[b, h // rep, lo:pos + 1]
+                p, _ = entmax15_exact((kh @ q[b, h, i]) * sc)
+                w = np.sqrt(p)
+                dp = vh @ do[b, h, i]
+                c = (w * dp).sum() / w.sum()
+                ds = w * (dp - c)
+                dq[b, h, i] = (ds @ kh) * sc
+                dk[b, h // rep, lo:pos + 1] += np.outer(ds, q[b, h, i]) * sc
+                dv[b, h // rep, lo:pos + 1] += np.outer(p, do[b, h, i])
+    if single:
+        return dq[:, :, 0], dk, dv
+    return dq, dk, dv

@@ -555,3 +555,55 @@ def test_decode_without_causal_mask_is_full_attention_over_the_cache():
         np.testing.assert_allclose(tau[b], ref["tau"], atol=1e-12)
     with pytest.raises(ValueError):
         attention_decode(q, kc, vc, seqlens, 4, causal=False)
+
+
+# ---------------------------------------------------------------------------
+# Backward at query length below key length (decode form)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 3), (False, 0)])
+def test_decode_backward_finite_differences(causal, window):
+    # central differences of attention_decode itself: grouped heads, two
+    # sequences of different valid lengths, two queries each
+    from oracle import attention_decode, attention_decode_backward
+    rng = np.random.default_rng(31 + window + 7 * causal)
+    B, H, Hkv, Lq, S, d = 2, 4, 2, 2, 6, 3
+    q = rng.normal(size=(B, H, Lq, d)) * 1.4
+    kc, vc = rng.normal(size=(B, Hkv, S, d)), rng.normal(size=(B, Hkv, S, d))
+    do = rng.normal(size=(B, H, Lq, d))
+    seqlens = np.array([S, 4])
+
+    def loss(q_, k_, v_):
+        return float((attention_decode(q_, k_, v_, seqlens, window, causal=causal)[0] * do).sum())
+
+    dq, dk, dv = attention_decode_backward(q, kc, vc, do, seqlens, window, causal=causal)
+    h = 1e-6
+    for x, ref, pos in ((q, dq, 0), (kc, dk, 1), (vc, dv, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args = [q, kc, vc]
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args[pos] = xp
+            fp = loss(*args)
+            args[pos] = xm
+            fm = loss(*args)
+            num[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(ref, num, atol=3e-7)
+    # keys past the valid length of sequence 1 get no gradient
+    assert np.all(dk[1, :, 4:] == 0) and np.all(dv[1, :, 4:] == 0)
+
+
+def test_decode_backward_is_the_square_backward_when_the_queries_fill_the_cache():
+    # Lq = n = S with the causal mask: the decode rows are the causal rows of
+    # a square sequence, so the gradients are attention_backward's
+    from oracle import attention_backward, attention_decode_backward
+    rng = np.random.default_rng(41)
+    B, H, L, d = 1, 2, 9, 4
+    q, k, v, do = (rng.normal(size=(B, H, L, d)) for _ in range(4))
+    for window in (0, 4):
+        dq, dk, dv = attention_decode_backward(q, k, v, do, np.array([L]), window, causal=True)
+        g = attention_backward(q, k, v, do, causal=True, window=window)
+        np.testing.assert_allclose(dq, g["dq"][None], atol=1e-12)
+        np.testing.assert_allclose(dk, g["dk"][None], atol=1e-12)
+        np.testing.assert_allclose(dv, g["dv"][None], atol=1e-12)
