@@ -22,7 +22,7 @@ struct ChunkCfg {
     static constexpr int EPC = 16 / ESZ;              // elements per 16-byte piece
     static constexpr int CPR = D / EPC;               // pieces per row
     static constexpr int NPC = CK * CPR / kThreads;   // pieces per thread per chunk
-    static constexpr int KSTR = D * ESZ + 16;         // K row stride in LDS (bytes)
+    static constexpr int KSTR = D * ESZ + 32;         // K row stride in LDS (bytes): +32 keeps the 16-byte row reads of a tile free of bank conflicts (+16 and +64 conflict)
     static constexpr int k_bytes = CK * KSTR;         // one K buffer
     static constexpr int VRS = D * 2 + 32;            // bf16: V row stride (bytes), row-major
     static constexpr int VSTR = CK + EPC;             // fp32: V^T row stride (elements)

@@ -49,7 +49,7 @@ struct RegCfg {
     static constexpr int EPC = 16 / ESZ;                 // elements per 16-byte piece
     static constexpr int CPR = D / EPC;                  // pieces per row
     static constexpr int NPC = PK * CPR / kThreads;      // pieces per thread per pair
-    static constexpr int KSTR = D * ESZ + 16;            // K row stride in LDS (bytes)
+    static constexpr int KSTR = D * ESZ + 32;            // K row stride in LDS (bytes): conflict-free tile reads
     static constexpr int k_bytes = PK * KSTR;
     static constexpr int VRS = D * 2 + 32;               // bf16: V row stride (bytes)
     static constexpr int VSTR = PK + EPC;                // fp32: V^T row stride (elements)

@@ -48,7 +48,7 @@ struct ShortCfg {
     static constexpr int VRS = D * 2 + 32;
     static constexpr int v_bytes = DT == DT_BF16 ? SPAN * VRS : D * VSTR * ESZ;
     static constexpr int scr_bytes = 4 * KC * kWave * 4;       // per wave: KC rows x 64 lanes
-    static constexpr int KSTR = D * ESZ + 16;                   // K row stride in LDS (bytes)
+    static constexpr int KSTR = D * ESZ + 32;                   // K row stride in LDS (bytes): conflict-free tile reads
     static constexpr int k_bytes = SPAN * KSTR;
     static constexpr int NKC = SPAN * CPR / kThreads;           // K chunks per thread
     // K staging (step 0-1) and the solve's scratch (step 2) share one region;
