@@ -11,10 +11,12 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     EntmaxError,
     bwd_workspace_bytes,
+    decode_bwd_workspace_bytes,
     decode_workspace_bytes,
     entmax_attn_bwd,
     entmax_attn_bwd_noalloc,
     entmax_attn_decode,
+    entmax_attn_decode_bwd,
     entmax_attn_fwd,
     entmax_attn_probs,
     entmax15_rows,

@@ -28,6 +28,8 @@ EXPORTS = (
     "entmax_attn_bwd_noalloc",
     "entmax_attn_bwd_workspace_bytes",
     "entmax_attn_decode",
+    "entmax_attn_decode_bwd",
+    "entmax_attn_decode_bwd_workspace_size",
     "entmax_attn_decode_workspace_size",
     "entmax_attn_fwd",
     "entmax_attn_fwd_gqa",
@@ -93,6 +95,11 @@ def load_library(path=LIB_PATH):
     lib.entmax_attn_decode_workspace_size.restype = sz
     lib.entmax_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_decode.restype = i32
+    lib.entmax_attn_decode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.entmax_attn_decode_bwd_workspace_size.restype = sz
+    lib.entmax_attn_decode_bwd.argtypes = [vp, vp, vp, vp, i32, i32, fp, vp, fp, fp, fp, vp, sz, i32, i32, i32, i32,
+                                           i32, i32, i32, vp]
+    lib.entmax_attn_decode_bwd.restype = i32
     lib.entmax_attn_status_string.argtypes = [i32]
     lib.entmax_attn_status_string.restype = ctypes.c_char_p
     lib.entmax_attn_last_error.argtypes = []
@@ -321,6 +328,55 @@ def entmax_attn_decode(q, k_cache, v_cache, seqlens, window=0, out=None, tau=Non
                                 B, H, hkv, Lq, S, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return out, tau
+
+
+def decode_bwd_workspace_bytes(B, H, H_kv, S, d, window=0, Lq=1):
+    """Bytes of device workspace ``entmax_attn_decode_bwd`` needs."""
+    return int(load_library().entmax_attn_decode_bwd_workspace_size(B, H, H_kv, Lq, S, d, int(window)))
+
+
+def entmax_attn_decode_bwd(q, k_cache, v_cache, seqlens, tau, dout, window=0, causal=True, dq=None, dk=None,
+                           dv=None, workspace=None):
+    """Gradients of ``entmax_attn_decode`` from its tau: (dq float32 shaped
+    like q, dk and dv float32 [B, H_kv, S, d]).  Arguments as for the
+    forward, plus tau (the forward's) and dout shaped like q.  workspace: a
+    uint8 GPU tensor of at least ``decode_bwd_workspace_bytes`` bytes, or
+    None to allocate one.  Deterministic (no atomics)."""
+    lib = load_library()
+    if q.dim() not in (3, 4) or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, H, d] or [B, H, Lq, d]; k_cache and v_cache [B, H_kv, S, d] of one shape")
+    B, H, d = q.shape[0], q.shape[1], q.shape[-1]
+    Lq = 1 if q.dim() == 3 else q.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or H % k_cache.shape[1] != 0:
+        raise ValueError("k_cache must be [B, H_kv, S, d] with H_kv dividing H")
+    for name, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("dout", dout)):
+        if not x.is_cuda or not x.is_contiguous() or x.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of q's dtype")
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    if seqlens.shape != (B,) or seqlens.dtype != torch.int32 or seqlens.device != q.device:
+        raise ValueError("seqlens must be a [B] int32 tensor on q's device")
+    if tau is None:
+        raise ValueError("tau is required")
+    _out(tau, tuple(q.shape[:-1]), q, "tau")
+    hkv, S = k_cache.shape[1], k_cache.shape[2]
+    dq = _out(dq, tuple(q.shape), q, "dq")
+    dk = _out(dk, (B, hkv, S, d), q, "dk")
+    dv = _out(dv, (B, hkv, S, d), q, "dv")
+    need = decode_bwd_workspace_bytes(B, H, hkv, S, d, window, Lq)
+    workspace = _workspace(workspace, need, q)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, hkv, S, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, hkv, S, d), dtype=torch.float32, device=q.device)
+    rc = lib.entmax_attn_decode_bwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens.contiguous()),
+                                    int(bool(causal)), int(window), _ptr(tau), _ptr(dout), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(workspace), workspace.numel(), B, H, hkv, Lq, S, d,
+                                    _dtype_code(q), _stream(q))
+    _check(lib, rc)
+    return dq, dk, dv
 
 
 def entmax_bisect_rows(scores, alpha=1.5, mask=None, p=None, tau=None, want_tau=True):

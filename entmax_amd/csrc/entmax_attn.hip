@@ -19,6 +19,7 @@
 #include "bwd.hpp"
 #include "bwd_wide.hpp"
 #include "decode.hpp"
+#include "decode_bwd.hpp"
 
 namespace {
 
@@ -330,6 +331,28 @@ DecLayout dec_layout(int B, int H, int Lq, int S, int d, int window) {  // any H
     return l;
 }
 
+// Workspace of the decode backward: the scores and dS of every row's span,
+// the chunk maxima and the span lengths (written by the scores kernel).
+struct DecBwdLayout {
+    int nch, P;
+    size_t sbuf, dsbuf, cmax, rlen, total;
+};
+
+DecBwdLayout dec_bwd_layout(int B, int H, int Lq, int S, int d, int window) {
+    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    const DecLayout f = dec_layout(B, H, Lq, S, d, window);
+    DecBwdLayout l;
+    l.nch = f.nch;
+    l.P = f.P;
+    const size_t rows = static_cast<size_t>(B) * H * Lq;
+    l.sbuf = 0;
+    l.dsbuf = l.sbuf + al(rows * l.P * sizeof(float));
+    l.cmax = l.dsbuf + al(rows * l.P * sizeof(float));
+    l.rlen = l.cmax + al(rows * l.nch * sizeof(float));
+    l.total = l.rlen + al(rows * sizeof(int));
+    return l;
+}
+
 int check_decode(int B, int H, int Hkv, int Lq, int S, int d, int dtype, int causal, int window) {
     if (B <= 0 || H <= 0 || S <= 0) return fail(ENTMAX_ERR_INVALID_ARG, "B, H, S must be positive (got %d, %d, %d)", B, H, S);
     if (Lq <= 0 || Lq > S) return fail(ENTMAX_ERR_INVALID_ARG, "Lq = %d outside [1, S = %d]", Lq, S);
@@ -343,6 +366,20 @@ int check_decode(int B, int H, int Hkv, int Lq, int S, int d, int dtype, int cau
     if (static_cast<long long>(B) * H * Lq * (S + 255) > (1LL << 36)) return fail(ENTMAX_ERR_UNSUPPORTED, "B * H * Lq * S too large");
     if ((static_cast<long long>(H / Hkv) * Lq + 15) / 16 > 65535) return fail(ENTMAX_ERR_UNSUPPORTED, "H / H_kv * Lq too large");
     return ENTMAX_OK;
+}
+
+// Decode backward: scores of every row's span, then dq and dS per row, then
+// dk and dv per key.
+template <int DT, int D>
+void launch_decode_bwd(const ea::DecBwdArgs& a, hipStream_t st) {
+    const ea::DecArgs& f = a.f;
+    const int nz = ((f.H / f.Hkv) * f.Lq + 15) / 16;
+    const dim3 block(ea::kThreads);
+    hipLaunchKernelGGL((ea::dec_scores_kernel<DT, D>), dim3(f.nch, f.B * f.Hkv, nz), block, 0, st, f);
+    const int rows = f.B * f.H * f.Lq;
+    const int wpb = ea::kThreads / ea::kWave;
+    hipLaunchKernelGGL((ea::dec_bwd_rows_kernel<DT, D>), dim3((rows + wpb - 1) / wpb), block, 0, st, a);
+    hipLaunchKernelGGL((ea::dec_bwd_keys_kernel<DT, D>), dim3((f.S + wpb - 1) / wpb, f.B * f.Hkv), block, 0, st, a);
 }
 
 template <int DT, int D>
@@ -599,6 +636,52 @@ int entmax_attn_decode(const void* q, const void* k_cache, const void* v_cache, 
         else launch_decode<ea::DT_F32, 128>(a, st);
     }
     return check_launch("decode");
+}
+
+size_t entmax_attn_decode_bwd_workspace_size(int B, int H, int H_kv, int Lq, int S, int d, int window) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || Lq <= 0 || S <= 0 || d <= 0 || window < 0) return 0;
+    return dec_bwd_layout(B, H, Lq, S, d, window).total;
+}
+
+int entmax_attn_decode_bwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, int causal,
+                           int window, const float* tau, const void* dout, float* dq, float* dk, float* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int Lq, int S, int d,
+                           int dtype, void* stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !tau || !dout || !dq || !dk || !dv || !workspace)
+        return fail(ENTMAX_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, seqlens, tau, dout, dq, dk, dv and workspace must not be NULL");
+    if (misaligned({q, k_cache, v_cache, dout, dq, dk, dv}, 16) || misaligned({seqlens, tau}, 4))
+        return fail(ENTMAX_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, dout, dq, dk and dv must be 16-byte aligned, seqlens and tau 4-byte aligned");
+    int rc = check_decode(B, H, Hkv, Lq, S, d, dtype, causal, window);
+    if (rc) return rc;
+    const DecBwdLayout l = dec_bwd_layout(B, H, Lq, S, d, window);
+    if (workspace_bytes < l.total)
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(ENTMAX_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    ea::DecBwdArgs a;
+    ea::DecArgs& f = a.f;
+    f.q = q; f.k = k_cache; f.v = v_cache; f.seqlens = seqlens; f.out = nullptr; f.tau_out = nullptr;
+    f.sbuf = reinterpret_cast<float*>(ws + l.sbuf);
+    f.cmax = reinterpret_cast<float*>(ws + l.cmax);
+    f.part = nullptr;
+    f.tau = nullptr;
+    f.row_len = reinterpret_cast<int*>(ws + l.rlen);
+    f.B = B; f.H = H; f.Hkv = Hkv; f.Lq = Lq; f.S = S; f.window = window; f.causal = causal != 0;
+    f.nch = l.nch; f.P = l.P;
+    f.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    a.tau = tau; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dsbuf = reinterpret_cast<float*>(ws + l.dsbuf);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16) {
+        if (d == 64) launch_decode_bwd<ea::DT_BF16, 64>(a, st);
+        else launch_decode_bwd<ea::DT_BF16, 128>(a, st);
+    } else {
+        if (d == 64) launch_decode_bwd<ea::DT_F32, 64>(a, st);
+        else launch_decode_bwd<ea::DT_F32, 128>(a, st);
+    }
+    return check_launch("decode_bwd");
 }
 
 const char* entmax_attn_status_string(int status) {

@@ -231,6 +231,33 @@ int entmax_attn_decode(const void *q, const void *k_cache, const void *v_cache, 
                        size_t workspace_bytes, int B, int H, int H_kv, int Lq, int S, int d, int dtype,
                        void *stream);
 
+/*
+ * Backward of the decode-time forward (query length below key length),
+ * from the forward's tau ("ADASPLASH -- ROBERTA Benchmark Result", section
+ * 2.4 Jacobian over the rows of section 3's decoders): per query row,
+ * w_j = sqrt(p_j), dp_j = dout . v_j, c = sum w dp / sum w,
+ * dS_j = w_j (dp_j - c); dq = dS k / sqrt(d), and every key j of the row's
+ * key/value head gets dS_j q / sqrt(d) in dk and p_j dout in dv.
+ *  - q, k_cache, v_cache, seqlens, causal, window, B, H, H_kv, Lq, S, d,
+ *    dtype: as for entmax_attn_decode (the same call's arguments).
+ *  - tau: [B, H, Lq] float32, the forward's tau_out.  dout: [B, H, Lq, d] of
+ *    `dtype`.  dq: [B, H, Lq, d], dk and dv: [B, H_kv, S, d], float32,
+ *    overwritten; keys that no query may attend (past n_b, or outside every
+ *    window) get zero; dk and dv of a shared key/value head sum its query
+ *    heads.
+ *  - workspace: caller-owned DEVICE memory, 256-byte aligned, of at least
+ *    entmax_attn_decode_bwd_workspace_size(B, H, H_kv, Lq, S, d, window)
+ *    bytes (scores and dS of every row's span); scratch after the call.
+ *  - Deterministic: every row of dq, dk and dv is summed by one wave in a
+ *    fixed order (no atomics).
+ *  - Errors as entmax_attn_decode.
+ */
+size_t entmax_attn_decode_bwd_workspace_size(int B, int H, int H_kv, int Lq, int S, int d, int window);
+int entmax_attn_decode_bwd(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens,
+                           int causal, int window, const float *tau, const void *dout,
+                           float *dq, float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                           int B, int H, int H_kv, int Lq, int S, int d, int dtype, void *stream);
+
 const char *entmax_attn_status_string(int status);
 
 /* Message describing the most recent failure on the calling thread

@@ -212,3 +212,57 @@ def test_decode_and_rows_are_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(t1, t2)
     assert torch.equal(p1, p2) and torch.equal(u1, u2)
+
+
+# ---- backward at query length below key length (entmax_attn_decode_bwd) ----
+
+DEC_BWD_CASES = [
+    # B, H, Hkv, Lq, S, d, dtype, causal, window, seqlens
+    (2, 4, 2, 1, 300, 64, "bf16", True, 0, [300, 177]),
+    (2, 4, 2, 1, 300, 64, "bf16", True, 32, [300, 177]),
+    (1, 2, 2, 5, 700, 128, "f32", True, 0, [650]),
+    (2, 2, 1, 7, 520, 64, "f32", False, 0, [520, 301]),
+    (1, 4, 1, 3, 3000, 128, "bf16", True, 0, [2990]),
+    (1, 2, 2, 64, 64, 64, "f32", True, 0, [64]),
+]
+
+
+@pytest.mark.parametrize("case", DEC_BWD_CASES, ids=[f"c{i}" for i in range(len(DEC_BWD_CASES))])
+def test_decode_backward(case):
+    # dq, dk and dv after the kernel's own forward, against the float64
+    # oracle's gradient; errors scaled by max(1, |reference|_inf)
+    from entmax_amd import entmax_attn_decode, entmax_attn_decode_bwd
+    from oracle import attention_decode_backward
+    B, H, Hkv, Lq, S, d, dtype, causal, window, seqlens = case
+    gen = torch.Generator().manual_seed(7000 + S + Lq)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = (torch.randn((B, H, Lq, d), generator=gen) * 1.5).to(dt)
+    k = torch.randn((B, Hkv, S, d), generator=gen).to(dt)
+    v = torch.randn((B, Hkv, S, d), generator=gen).to(dt)
+    do = torch.randn((B, H, Lq, d), generator=gen).to(dt)
+    sl = torch.tensor(seqlens, dtype=torch.int32)
+    log(f"[decode bwd] B{B} H{H}/{Hkv} Lq{Lq} S{S} d{d} {dtype} causal {causal} window {window} seqlens {seqlens}")
+    g = {n: x.cuda() for n, x in (("q", q), ("k", k), ("v", v), ("do", do), ("sl", sl))}
+    _, tau = entmax_attn_decode(g["q"], g["k"], g["v"], g["sl"], window, causal=causal)
+    dq, dk, dv = entmax_attn_decode_bwd(g["q"], g["k"], g["v"], g["sl"], tau, g["do"], window, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = attention_decode_backward(q, k, v, do, sl.numpy(), window, causal=causal)
+    for name, x, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = float(np.abs(x.cpu().numpy() - r).max()) / max(1.0, float(np.abs(r).max()))
+        log(f"[decode bwd]   scaled err {name} {err:.3g}")
+        assert err <= TOL[dtype], (name, err)
+    # deterministic: a second call gives the same bits
+    dq2, dk2, dv2 = entmax_attn_decode_bwd(g["q"], g["k"], g["v"], g["sl"], tau, g["do"], window, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_decode_backward_rejects_small_workspace():
+    from entmax_amd import decode_bwd_workspace_bytes, entmax_attn_decode, entmax_attn_decode_bwd
+    q = torch.randn((1, 2, 1, 64), device="cuda")
+    k = torch.randn((1, 2, 100, 64), device="cuda")
+    sl = torch.tensor([100], dtype=torch.int32, device="cuda")
+    _, tau = entmax_attn_decode(q, k, k, sl)
+    need = decode_bwd_workspace_bytes(1, 2, 2, 100, 64, 0, 1)
+    with pytest.raises(ValueError):
+        entmax_attn_decode_bwd(q, k, k, sl, tau, q, workspace=torch.empty((need - 1,), dtype=torch.uint8, device="cuda"))
