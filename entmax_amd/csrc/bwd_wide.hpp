@@ -18,7 +18,9 @@
 //  * bwd_q_kernel (query rows stationary, keys streamed): the support
 //    entries of each row (s_ij > tau_i) go to the row's list, kept in the
 //    row's own dQ row (still unwritten: D/2 entries of (w, key), D/8 per
-//    lane, lane-private so that an append is one store); afterwards each row
+//    lane, lane-private so that an append is one store, entry e of lane
+//    group g at slot 4 e + g so that a row's first entries share one
+//    32-byte sector); afterwards each row
 //    gathers V_j and K_j of its entries and forms c_i and
 //    dQ_i = scale (sum w dp K - c_i sum w K).  A row whose support outgrows
 //    its lists gets the overflow marker in c_i, and the tile-wise kernel of
@@ -120,9 +122,10 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
     int* kch = a.kcnt != nullptr ? a.kcnt + static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L : nullptr;
     float* dkb = a.dk + kv_off;
     float* dvb = a.dv + kv_off;
-    // this lane's list of row f: entries (w, key bits) in the row's dQ
+    // this lane's list of row f: entries (w, key bits) in the row's dQ,
+    // entry e at [4 e]
     auto lst = [&](int f, int lane_g) {
-        return reinterpret_cast<f32x2*>(dqh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g * SUB;
+        return reinterpret_cast<f32x2*>(dqh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g;
     };
 
     ChunkStream<DT, D, 2, 1> cs;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
                         // w = (s - tau)/2; an entry the low raw threshold let in
                         // by rounding gets w = 0 and contributes nothing
                         if (cnt[f] < SUB)
-                            lst(f, g)[cnt[f]] = f32x2{fmaxf(0.5f * fmaf(s[f][t][i], a.scale, -tau[f]), 0.f),
+                            lst(f, g)[4 * cnt[f]] = f32x2{fmaxf(0.5f * fmaf(s[f][t][i], a.scale, -tau[f]), 0.f),
                                                       __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
                         else
                             ovf[f] = true;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const bool in = e0 + j < n2;
-                    const f32x2 en = other[in ? e0 + j : 0];
+                    const f32x2 en = other[4 * (in ? e0 + j : 0)];
                     key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
                     w[j] = in ? en[0] : 0.f;
                 }

@@ -17,7 +17,9 @@
 //      subset of a row is at most the row's).  The scores are recomputed and
 //      every score above that bound goes to the row's candidate list: the
 //      row's own O row in memory, still unwritten, holds D/2 entries of
-//      (score, key), D/8 per lane (lane-private, so an append is one store);
+//      (score, key), D/8 per lane (lane-private, so an append is one store;
+//      entry e of lane group g at slot 4 e + g, so that the first entries of
+//      a row's four lanes share one 32-byte sector);
 //   3. tau is the 25-step bisection result on [m - 2, m - 2/sqrt(n)], found
 //      as in the short-span kernel (exact root by Newton steps from the left
 //      and the closed form of Theorem 1 on the list, then the centre of the
@@ -104,10 +106,11 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     }
     float npop = 0.f;   // valid keys of the span (rows without a causal mask; uniform)
     const bool allrows = rbase + NF * 16 <= L;
-    // this lane's list of row f: entries (score scaled, key bits) in the row's O
+    // this lane's list of row f: entries (score scaled, key bits) in the row's O,
+    // entry e at [4 e]
     float* outh = a.out + head_off;
     auto lst = [&](int f, int lane_g) {
-        return reinterpret_cast<f32x2*>(outh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g * SUB;
+        return reinterpret_cast<f32x2*>(outh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g;
     };
 
     ChunkStream<DT, D, 2, 1> cs;
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
                 for (int i = 0; i < 4; ++i) {
                     if (s[f][t][i] > thrr[f]) {
                         if (cnt[f] < SUB)
-                            lst(f, g)[cnt[f]] = f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
+                            lst(f, g)[4 * cnt[f]] = f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
                         else
                             ovf[f] = true;
                         ++cnt[f];
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         float sl[SUB];
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const float v = mine[k < len ? k : 0][0];
+            const float v = mine[4 * (k < len ? k : 0)][0];
             sl[k] = k < len ? fmaf(v, 0.5f, -hs) : -kInf;
         }
         const float ts = col_exact<SUB>(sl, st, SUB * 4 + 3);
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const bool in = e0 + j < n2;
-                    const f32x2 en = other[in ? e0 + j : 0];
+                    const f32x2 en = other[4 * (in ? e0 + j : 0)];
                     const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
                     p[j] = in && !empty ? y * y : 0.f;
                     key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
