@@ -51,6 +51,29 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// two floats rounded to nearest-even bf16, the first in the low half
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// p = y^2 of 8 entries as two bf16 operands: hi the nearest bf16 of p, lo
+// the nearest bf16 of the remainder p - hi (formed exactly by one fma), so
+// that hi + lo carries about 16 significant bits of p.
+__device__ __forceinline__ void split_sq_bf16(const float (&y)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float a = y[2 * m], b = y[2 * m + 1];
+        h[m] = pack_bf16(a * a, b * b);
+        const float ha = __uint_as_float(h[m] << 16), hb = __uint_as_float(h[m] & 0xffff0000u);
+        l[m] = pack_bf16(fmaf(a, a, -ha), fmaf(b, b, -hb));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Sums / maxima over groups of N consecutive lanes (N a power of two <= 64).
 // Butterfly order: every lane of the group ends with a bitwise-identical
 // value (floating-point addition is commutative).

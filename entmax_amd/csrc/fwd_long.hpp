@@ -389,14 +389,14 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
         f32x4 sv[NTC];
         bool ok[NTC];
         tiles(ch, kb, M, sv, ok);
-        f32x4 p[NTC];
+        f32x4 yv[NTC];   // p = y^2
         bool nz = false;
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float y = relu1(fmaf(sv[t][i], c2, -sh));
-                p[t][i] = y * y;
+                yv[t][i] = y;
                 nz |= y > 0.f;
             }
         }
@@ -404,14 +404,14 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
         if constexpr (DT == DT_BF16) {
 #pragma unroll
             for (int h = 0; h < NTC / 2; ++h) {
-                bf16x8 phi, plo;
+                float y8[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pv = i < 4 ? p[2 * h][i] : p[2 * h + 1][i - 4];
-                    const __bf16 hb = static_cast<__bf16>(pv);
-                    phi[i] = hb;
-                    plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
+                for (int i = 0; i < 4; ++i) {
+                    y8[i] = yv[2 * h][i];
+                    y8[4 + i] = yv[2 * h + 1][i];
                 }
+                bf16x8 phi, plo;
+                split_sq_bf16(y8, phi, plo);
 #pragma unroll
                 for (int ct = 0; ct < D / 16; ++ct) {
                     // B operand through transpose loads (see the short-span kernel)
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
                 for (int ct = 0; ct < D / 16; ++ct) {
                     const f32x4 bv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(vb) + (16 * ct + c) * C::VSTR + 16 * t + 4 * g);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o[ct] = mfma_f32(p[t][q], bv[q], o[ct]);
+                    for (int q = 0; q < 4; ++q) o[ct] = mfma_f32(yv[t][q] * yv[t][q], bv[q], o[ct]);
                 }
             }
         }

@@ -15,12 +15,15 @@
 // of the "DistilBERT SST-2 with AdaSplash Attention" model card,
 // Mathematical Formulation 2), in the half-scaled shifted domain
 // x = (s - max)/2, p = [x - t]_+^2:
-//   * t starts at the exact root over the row's eight lane maxima (a
-//     subset of the row, hence a lower bound of the root);
 //   * Newton steps on sqrt(g(t)) - 1, where sqrt(g) is the Euclidean norm
 //     of the vector [x - t]_+: a convex, decreasing function of t, so every
-//     iterate stays at or below the root t* (and unlike g itself it is
-//     nearly linear far from the root: one entry is solved in one step);
+//     iterate from the left stays at or below the root t* (and unlike g
+//     itself it is nearly linear far from the root: one entry is solved in
+//     one step);
+//   * the start is a lower bound from subsets of the row (the root of a
+//     subset is at most the row's): the exact root over a wave's four lane
+//     maxima, raised by two Newton steps over its 32 pair maxima (each lane's
+//     maximum of every 128-key pair); the larger of the two halves' bounds;
 //   * a row stops once its step is below 1e-5 (the error then is of the
 //     order of the step squared over the mean excess);
 //   * the 25-step bisection's final midpoint is the centre of the dyadic
@@ -28,7 +31,8 @@
 // The two halves of a row meet in LDS once per round; every round decision
 // is uniform over the workgroup.  O = P V on MFMA, bf16 P split into a high
 // and a low part so that P keeps about 16 bits; pairs whose P is zero for a
-// wave's rows are skipped by that wave.
+// wave's rows are skipped by that wave.  The first V pair is fetched before
+// the rounds.
 #pragma once
 
 #include <type_traits>
@@ -61,6 +65,7 @@ struct RegCfg {
     static constexpr int RB = D * ESZ;                   // bytes per K / V row in HBM
     static constexpr int RS = RB == 128 ? 7 : RB == 256 ? 8 : 9;
     static constexpr int kRounds = 16;                   // threshold rounds at most
+    static constexpr float kStop = 1e-5f;                // a step below this ends a row's rounds
     static_assert(NPC >= 1 && (1 << RS) == RB, "whole pieces per thread; row bytes a power of two");
     static_assert(BM * D * 4 <= 2 * buf_bytes, "the halves' partial O fit the staging buffers");
 };
@@ -159,6 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     const int klo_i = a.window > 0 ? qrow - a.window : -1;   // window: key > query - W
     f32x4 S[NT];
     float mlane = -kInf, nl = 0.f;
+    float mpair[NP];   // this lane's maximum of each pair
     {
         Pre pr;
         prefetch(j0, kc, pr);
@@ -171,6 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             if (jp >= j1) {   // uniform
 #pragma unroll
                 for (int t = 0; t < 4; ++t) S[4 * jj + t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+                mpair[jj] = -kInf;
                 continue;
             }
             if (jp + 1 < j1) prefetch(jp + 1, kc, pr);
@@ -180,6 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             // crossing the wave's rows, every row a query row: uniform) takes
             // plain products and no masking
             const bool cross = a.causal && (cb + 63 > rbase || (a.window > 0 && cb <= rbase + 15 - a.window));
+            float mpr = -kInf;   // this lane's maximum over the pair
             auto tiles = [&](auto clean_tag) {
                 constexpr bool CLEAN = decltype(clean_tag)::value;
 #pragma unroll
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
                         KFrag<DT, D> kf;
                         kf.load_lds_at(kb + 16 * t * C::KSTR);
                         sv = kf.st(qf);
-                        mlane = fmaxf(mlane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+                        mpr = fmaxf(mpr, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
                     } else {
                         const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
                         const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
                             }
 #pragma unroll
                             for (int i = 0; i < 4; ++i) sv[i] = rowok ? sv[i] : -kInf;
-                            mlane = fmaxf(mlane, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+                            mpr = fmaxf(mpr, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
                             if (a.causal) {
 #pragma unroll
                                 for (int i = 0; i < 4; ++i) nl += sv[i] > -1e29f ? 1.f : 0.f;
@@ -218,6 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             };
             if (M == ~0ull && !cross && allrows) tiles(std::true_type{});
             else tiles(std::false_type{});
+            mpair[jj] = mpr;
+            mlane = fmaxf(mlane, mpr);
             if (a.causal && M == ~0ull && !cross && allrows) nl += 16.f;   // four clean tiles: 16 keys of this lane
             if (!a.causal) nl += static_cast<float>(__popcll(M));
             if (jp + 1 < j1) {
@@ -230,26 +240,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     if (!a.causal) nl = (g == 0 && rowok) ? nl : 0.f;
 
     // one value per row and wave to the partner wave (same rows, other half);
-    // the exchanges and the votes each alternate between two slots, so that
-    // one barrier per call suffices
-    int xp = 0, vp = 0;
-    auto exchange = [&](f32x4 v) -> f32x4 {
+    // the exchanges alternate between two slots, so that one barrier per
+    // call suffices.  With a vote: every wave also tells whether its flag
+    // was set, and all four waves learn whether any flag was.
+    int xp = 0;
+    auto exchange_vote = [&](f32x4 v, bool flag, bool* any) -> f32x4 {
         if (g == 0) xch[(xp * 4 + wv) * 16 + c] = v;
+        if (lane == 0) votes[xp * 4 + wv] = flag ? 1 : 0;
         __syncthreads();
         const f32x4 o = xch[(xp * 4 + (wv ^ 2)) * 16 + c];
+        *any = (votes[xp * 4] | votes[xp * 4 + 1] | votes[xp * 4 + 2] | votes[xp * 4 + 3]) != 0;
         xp ^= 1;
         return o;
     };
-    auto wg_any = [&](bool v) -> bool {
-        const int wave_any = __any(v) ? 1 : 0;   // the whole wave votes (outside the branch)
-        if (lane == 0) votes[vp * 4 + wv] = wave_any;
-        __syncthreads();
-        const bool r = (votes[vp * 4] | votes[vp * 4 + 1] | votes[vp * 4 + 2] | votes[vp * 4 + 3]) != 0;
-        vp ^= 1;
-        return r;
+    auto exchange = [&](f32x4 v) -> f32x4 {
+        bool unused;
+        return exchange_vote(v, false, &unused);
     };
 
     // ---- 2. the threshold ------------------------------------------------------------------
+    // V of the first pair is fetched now; its latency passes under the rounds
+    Pre prv;
+    prefetch(j0, vc, prv);
     const float c2 = 0.5f * a.scale;
     const f32x4 mw = {col4_max(mlane), col4_sum(nl), 0.f, 0.f};
     const f32x4 mp = exchange(mw);
@@ -258,51 +270,80 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     const bool empty = n == 0.f;
     const float mc2 = empty ? 0.f : mrow * c2;
     const float hi = -__builtin_amdgcn_rsqf(empty ? 1.f : n);
-    // root over this wave's four lane maxima, then the larger of the two halves'
-    const float lbw = fmaxf(col_lower_bound(fmaf(mlane, c2, -mc2)), -1.f);
+    // A lower bound of the root from a subset of the row: the root over this
+    // wave's four lane maxima, then Newton steps (as below, from the left)
+    // over its 32 pair maxima, which stay at or below that subset's root;
+    // the larger of the two halves' bounds starts the rounds.
+    float lbw = fmaxf(col_lower_bound(fmaf(mlane, c2, -mc2)), -1.f);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NP; ++jj) {
+            const float y = relu1(fmaf(mpair[jj], c2, -(mc2 + lbw)));
+            s1 += y;
+            s2 = fmaf(y, y, s2);
+        }
+        s1 = col4_sum(s1);
+        s2 = col4_sum(s2);
+        const float rg = __builtin_amdgcn_sqrtf(s2);
+        // s1 = 0 where this half holds nothing above the bound
+        lbw += s1 > 0.f ? fmaxf((rg - 1.f) * rg * __builtin_amdgcn_rcpf(s1), 0.f) : 0.f;
+    }
     const f32x4 lp = exchange(f32x4{lbw, 0.f, 0.f, 0.f});
     float t = fminf(fmaxf(lbw, lp[0]), hi);
-    bool done = empty || n <= 1.f;   // n = 1: the root is the lower end -1
-    bool go = wg_any(!done);
+    const bool trivial = empty || n <= 1.f;   // n = 1: the root is the lower end -1
+    const int nt = 4 * (j1 - j0);             // tiles holding keys (uniform)
+
+    // Newton step on sqrt(g) - 1 from the sums over both halves; the same
+    // value in both waves of the row group (addition commutes)
+    auto newton_step = [&](float s1, float s2, f32x4 pp) {
+        const float S1 = s1 + pp[0], S2 = s2 + pp[1];
+        const float rg = __builtin_amdgcn_sqrtf(S2);   // (sqrt(g))' = -S1 / sqrt(g)
+        return (rg - 1.f) * rg * __builtin_amdgcn_rcpf(S1);
+    };
+
+    // A round whose vote finds no wave with an open row ends the loop (every
+    // wave skipped its pass in it): one barrier per round.
+    bool done = trivial;
 #pragma unroll 1
-    for (int r = 0; r < C::kRounds && go; ++r) {
-        const float bias = -(mc2 + t);
+    for (int r = 0; r <= C::kRounds; ++r) {
+        const bool open = __any(!done);
         float s1 = 0.f, s2 = 0.f;
-        // a wave whose rows are all done skips the pass (its partner wave,
-        // with the same rows, skips it too)
-        if (__any(!done)) {
+        if (open && r < C::kRounds) {   // a wave whose rows are all done skips the pass (so does its partner)
+            const float bias = -(mc2 + t);
             float u1 = 0.f, u2 = 0.f;   // two chains each
 #pragma unroll
-            for (int k = 0; k < NT; ++k)
+            for (int k = 0; k < NT; ++k) {
+                if (k < nt) {   // uniform
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float y = relu1(fmaf(S[k][i], c2, bias));
-                    if (i & 1) {
-                        u1 += y;
-                        u2 = fmaf(y, y, u2);
-                    } else {
-                        s1 += y;
-                        s2 = fmaf(y, y, s2);
+                    for (int i = 0; i < 4; ++i) {
+                        const float y = relu1(fmaf(S[k][i], c2, bias));
+                        if (i & 1) {
+                            u1 += y;
+                            u2 = fmaf(y, y, u2);
+                        } else {
+                            s1 += y;
+                            s2 = fmaf(y, y, s2);
+                        }
                     }
                 }
+            }
             s1 = col4_sum(s1 + u1);
             s2 = col4_sum(s2 + u2);
         }
-        const f32x4 pp = exchange(f32x4{s1, s2, 0.f, 0.f});
+        bool any_open;
+        const f32x4 pp = exchange_vote(f32x4{s1, s2, 0.f, 0.f}, open, &any_open);
+        if (!any_open || r == C::kRounds) break;   // uniform
         if (!done) {
-            // the same sums in both waves of the row group (addition commutes)
-            const float S1 = s1 + pp[0], S2 = s2 + pp[1];
-            // Newton on sqrt(g) - 1: (sqrt(g))' = -S1 / sqrt(g)
-            const float rg = __builtin_amdgcn_sqrtf(S2);
-            const float step = (rg - 1.f) * rg * __builtin_amdgcn_rcpf(S1);
+            const float step = newton_step(s1, s2, pp);
             t = fminf(t + fmaxf(step, 0.f), hi);
-            done = step < 1e-5f;
+            done = step < C::kStop;
         }
-        go = wg_any(!done);
     }
     const float tx = t;
     float tf = -1.f;
-    if (!empty && n > 1.f) {
+    if (!trivial) {
         ColState st;
         st.lo = -1.f;
         st.hi = hi;
@@ -311,15 +352,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     }
     if (a.tau != nullptr && g == 0 && hf == 0 && rowok)
         a.tau[static_cast<size_t>(bh) * L + qrow] = empty ? kInf : 2.f * (mc2 + tf);
-    const float pb = -(mc2 + tf);   // p = relu(s c2 + pb)^2
+    // p = relu(s c2 + pb)^2; an empty row has no finite score and gets pb = -inf
+    const float pb = empty ? -kInf : -(mc2 + tf);
 
     // ---- 3. O = P V --------------------------------------------------------------------------
     f32x4 o[D / 16];
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        Pre pr;
-        prefetch(j0, vc, pr);
+        Pre& pr = prv;
         stage_v(0, pr);
         __syncthreads();
 #pragma unroll
@@ -327,29 +368,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             const int jp = j0 + jj;
             if (jp >= j1) continue;   // uniform
             if (jp + 1 < j1) prefetch(jp + 1, vc, pr);
-            f32x4 p[4];
+            float y[4][4];
             bool nz = false;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float y = empty ? 0.f : relu1(fmaf(S[4 * jj + t][i], c2, pb));
-                    p[t][i] = y * y;
-                    nz |= y > 0.f;
+                    y[t][i] = relu1(fmaf(S[4 * jj + t][i], c2, pb));
+                    nz |= y[t][i] > 0.f;
                 }
             if (__any(nz)) {   // uniform over the wave
                 const char* vb = buf + (jj & 1) * C::buf_bytes;
                 if constexpr (DT == DT_BF16) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
-                        bf16x8 phi, plo;
+                        float y8[8];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const float pv = i < 4 ? p[2 * h2][i] : p[2 * h2 + 1][i - 4];
-                            const __bf16 hb = static_cast<__bf16>(pv);
-                            phi[i] = hb;
-                            plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
+                        for (int i = 0; i < 4; ++i) {
+                            y8[i] = y[2 * h2][i];
+                            y8[4 + i] = y[2 * h2 + 1][i];
                         }
+                        bf16x8 phi, plo;
+                        split_sq_bf16(y8, phi, plo);
 #pragma unroll
                         for (int ct = 0; ct < D / 16; ++ct) {
                             // B operand through transpose loads: keys 64 hf + 32 h2 + slot
@@ -369,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
                         for (int ct = 0; ct < D / 16; ++ct) {
                             const f32x4 bv = *reinterpret_cast<const f32x4*>(vt + (16 * ct + c) * C::VSTR + 64 * hf + 16 * t + 4 * g);
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) o[ct] = mfma_f32(p[t][q], bv[q], o[ct]);
+                            for (int q = 0; q < 4; ++q) o[ct] = mfma_f32(y[t][q] * y[t][q], bv[q], o[ct]);
                         }
                 }
             }

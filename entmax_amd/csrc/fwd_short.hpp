@@ -350,17 +350,14 @@ __global__ __launch_bounds__(kThreads, (ShortCfg<DT, D, NKT, KC>::kOcc)) void fw
 #pragma unroll
         for (int h = 0; h < NT / 2; ++h) {
             if (2 * h + 1 < t0 || 2 * h >= t1) continue;   // uniform
-            f32x4 p0, p1;
-            probs(2 * h, p0);
-            probs(2 * h + 1, p1);
-            bf16x8 phi, plo;
+            float y8[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pv = i < 4 ? p0[i] : p1[i - 4];
-                const __bf16 hb = static_cast<__bf16>(pv);
-                phi[i] = hb;
-                plo[i] = static_cast<__bf16>(pv - static_cast<float>(hb));
+            for (int i = 0; i < 4; ++i) {
+                y8[i] = relu1(fmaf(sv[2 * h][i], c2, -sh));
+                y8[4 + i] = relu1(fmaf(sv[2 * h + 1][i], c2, -sh));
             }
+            bf16x8 phi, plo;
+            split_sq_bf16(y8, phi, plo);
 #pragma unroll
             for (int ct = 0; ct < D / 16; ++ct) {
                 // B operand: lane (g, c) needs V[key 32h + 4g + k][16ct + c]
