@@ -108,12 +108,13 @@ struct ChunkStream {
     __device__ __forceinline__ unsigned long long valid_bits(int ch, const Pre& p) const {
         return __ballot((ch * C::CK + lane < L) & (!hasm | (p.mb != 0)));
     }
-    // fn(ch, kbuf, vbuf, M) for every chunk of [ch0, ch1), in order.  Every
-    // thread of the workgroup must call this with the same arguments.  With a
-    // side array the staged values of a chunk sit at sideb + (kbuf - Kb) /
-    // k_bytes * 64 (the buffer index times 64).
-    template <typename F>
+    // fn(ch, kbuf, vbuf, M) for the chunks ch0, ch0 + STEP, ... below ch1,
+    // in order.  Every thread of the workgroup must call this with the same
+    // arguments.  With a side array the staged values of a chunk sit at
+    // sideb + (kbuf - Kb) / k_bytes * 64 (the buffer index times 64).
+    template <int STEP = 1, typename F>
     __device__ __forceinline__ void run(int ch0, int ch1, bool withv, F&& fn) const {
+        static_assert(STEP == 1 || (NBUF == 2 && NPRE == 1), "strided runs: two buffers, one chunk ahead");
         if (ch0 >= ch1) return;
         if constexpr (NBUF == 1 && NPRE == 1) {
             Pre pa;
@@ -160,15 +161,16 @@ struct ChunkStream {
             stage(0, withv, pa);
             unsigned long long Mc = valid_bits(ch0, pa);
             __syncthreads();
-            for (int ch = ch0; ch < ch1; ++ch) {
-                const int buf = (ch - ch0) & 1;
-                if (ch + 1 < ch1) prefetch(ch + 1, withv, pa);
+            int buf = 0;
+            for (int ch = ch0; ch < ch1; ch += STEP) {
+                if (ch + STEP < ch1) prefetch(ch + STEP, withv, pa);
                 fn(ch, Kb + buf * C::k_bytes, Vb + buf * C::v_bytes, Mc);
-                if (ch + 1 < ch1) {
+                if (ch + STEP < ch1) {
                     stage(buf ^ 1, withv, pa);
-                    Mc = valid_bits(ch + 1, pa);
+                    Mc = valid_bits(ch + STEP, pa);
                 }
                 __syncthreads();
+                buf ^= 1;
             }
             return;
         }

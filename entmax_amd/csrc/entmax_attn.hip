@@ -95,12 +95,12 @@ int launch_wide(ea::FwdArgs a, hipStream_t st) {
     typedef ea::LongCfg<DT, D> C;
     auto kw = ea::fwd_wide_kernel<DT, D>;
     auto kl = ea::fwd_long_kernel<DT, D>;
-    int rc = set_lds(kw, W::stream_lds_bytes);
+    int rc = set_lds(kw, W::fwd_lds_bytes);
     if (!rc) rc = set_lds(kl, C::lds_bytes);
     if (rc) return rc;
     a.nqt = (a.L + W::BR - 1) / W::BR;
     a.fixup = 0;
-    hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
+    hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::fwd_lds_bytes, st, a);
     a.nqt = (a.L + C::BM - 1) / C::BM;
     a.fixup = 1;
     hipLaunchKernelGGL(kl, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), C::lds_bytes, st, a);

@@ -6,34 +6,38 @@
 // products, so the four lanes c, c + 16, c + 32, c + 48 hold a row.  K
 // streams through LDS in chunks of 64 keys shared by the four waves
 // (wide.hpp); each LDS read of K feeds NF products.  The score row is never
-// stored whole; K is streamed twice:
-//   1. scores, the running maximum of each lane's share of the row and the
-//      allowed count;
-//   2. the row maximum m and a certified lower bound of tau: the larger of
-//      m - 2 ("DistilBERT SST-2 with AdaSplash Attention" model card,
-//      Mathematical Formulation 2: tau >= max - 2) and the root of
-//      sum_j ((s_j - t)/2)^2 = 1 over the four lanes' maxima ("ADASPLASH --
-//      ROBERTA Benchmark Result", section 2.2 Theorem 1: the root over a
-//      subset of a row is at most the row's).  The scores are recomputed and
-//      every score above that bound goes to the row's candidate list: the
+// stored whole; K is streamed one and a half times:
+//   1. every other chunk: scores and the running maximum of each lane's
+//      share of that sample of the row;
+//   2. a certified lower bound of tau per row from the sample: the larger
+//      of ms - 2, ms the sample's maximum ("DistilBERT SST-2 with AdaSplash
+//      Attention" model card, Mathematical Formulation 2: tau >= m - 2 >=
+//      ms - 2), and the root of sum_j ((s_j - t)/2)^2 = 1 over the four
+//      lanes' sampled maxima ("ADASPLASH -- ROBERTA Benchmark Result",
+//      section 2.2 Theorem 1: the root over a subset of a row is at most
+//      the row's);
+//   3. every chunk: the scores again, the row maximum m, the allowed count,
+//      and every score above that bound into the row's candidate list: the
 //      row's own O row in memory, still unwritten, holds D/2 entries of
-//      (score, key), D/8 per lane (lane-private, so an append is one store;
-//      entry e of lane group g at slot 4 e + g, so that the first entries of
-//      a row's four lanes share one 32-byte sector);
-//   3. tau is the 25-step bisection result on [m - 2, m - 2/sqrt(n)], found
+//      (score, key); the row's four lanes take slots from a counter of the
+//      row in LDS (one LDS atomic per lane and tile with candidates), and
+//      lane g later reads back the slots g, g + 4, ...;
+//   4. tau is the 25-step bisection result on [m - 2, m - 2/sqrt(n)], found
 //      as in the short-span kernel (exact root by Newton steps from the left
-//      and the closed form of Theorem 1 on the list, then the centre of the
-//      dyadic cell that holds it; col_solve.hpp), and
-//      O_i = sum_j p_ij V_j over the list entries with s > tau, gathering V
-//      rows (sparse aggregation, "RoBERTa Base with AdaSplash Attention" model
-//      card, Architecture Overview).
-// Two passes over K instead of one: a single pass must bound tau from the
-// keys seen so far, and a prefix of a row can have a far larger support than
-// the whole row (a flat top that a later, larger score dwarfs), so its lists
-// would have to be much longer.  A row with more than D/8 scores above its
-// bound in one lane is marked (kOMarker in O[row][0]); the long-span kernel
-// (fwd_long.hpp) then recomputes the marked 64-row tiles in fix-up mode, with
-// S recomputed from the K tiles pass by pass.
+//      and the closed form of Theorem 1 on the list entries above the bound
+//      from all of m and the lanes' maxima, then the centre of the dyadic
+//      cell that holds it; col_solve.hpp), and O_i = sum_j p_ij V_j over the
+//      list entries with s > tau, gathering V rows (sparse aggregation,
+//      "RoBERTa Base with AdaSplash Attention" model card, Architecture
+//      Overview).
+// Not a single pass: a pass must bound tau from the keys seen so far, and a
+// prefix of a row can have a far larger support than the whole row (a flat
+// top that a later, larger score dwarfs), so its lists would have to be much
+// longer; the sample of every other chunk bounds tau nearly as tightly as
+// the whole row.  A row with more than D/2 scores above its bound is
+// marked (kOMarker in O[row][0]); the long-span kernel
+// (fwd_long.hpp) then recomputes the marked 64-row tiles in fix-up mode,
+// with S recomputed from the K tiles pass by pass.
 #pragma once
 
 #include <type_traits>
@@ -57,8 +61,10 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     typedef WideCfg<DT, D> C;
     constexpr int NF = C::NF, CK = C::CK, DQ = C::DQ, NB = C::NB;
     constexpr int SUB = D / 8;     // list entries per lane (8 bytes each in the row's O)
+    constexpr int kSampleStep = 2; // the first pass reads every other chunk
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
+    int* rowcnt = reinterpret_cast<int*>(Kb + 2 * C::k_bytes);   // list length of each of the workgroup's rows
 
     const int total = a.B * a.H * a.nqt;
     const int wi = xcd_swizzle(blockIdx.x, total);
@@ -90,28 +96,28 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     const float scale = a.scale;
     QFrag<DT, D> qf[NF];
     float LM[NF];      // running maximum of this lane's share of the row (raw accumulator units)
-    float thrr[NF];    // the row's candidate threshold (raw, pass 2)
+    float thrr[NF];    // the row's candidate threshold (raw)
     float lbs[NF];     // its certified lower bound of tau (scaled units)
     float m[NF];       // row maximum (raw)
-    int cnt[NF];       // entries in the row's list
     bool ovf[NF];
     float nl[NF];      // allowed keys seen by this lane (causal rows)
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         qf[f].load(qh, rbase + 16 * f + c, L, g);
         LM[f] = -kInf;
-        cnt[f] = 0;
         ovf[f] = false;
         nl[f] = 0.f;
     }
     float npop = 0.f;   // valid keys of the span (rows without a causal mask; uniform)
     const bool allrows = rbase + NF * 16 <= L;
-    // this lane's list of row f: entries (score scaled, key bits) in the row's O,
-    // entry e at [4 e]
+    // the list of row f: entries (score scaled, key bits) in the row's O,
+    // slots taken by the row's four lanes from the row's counter in LDS; lane
+    // g reads back the slots g, g + 4, ... (its share), the k-th at [4 k]
     float* outh = a.out + head_off;
     auto lst = [&](int f, int lane_g) {
         return reinterpret_cast<f32x2*>(outh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g;
     };
+    int* const rc = rowcnt + wv * NF * 16 + c;   // row f's counter at rc[16 f]
 
     ChunkStream<DT, D, 2, 1> cs;
     cs.Kb = Kb;
@@ -166,7 +172,43 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         return M == ~0ull && !cross && allrows;
     };
 
-    // ---- 1. row maxima and allowed counts ------------------------------------------------
+    // ---- 1. a lower bound of each row's maximum from every other chunk -----------------------
+    cs.template run<kSampleStep>(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
+        const int cb = chn * CK;
+        if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
+        f32x4 s[NF][4];
+        if (clean_chunk(cb, M)) scores(std::true_type{}, cb, kb, M, s);
+        else scores(std::false_type{}, cb, kb, M, s);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            float mx = LM[f];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mx = fmaxf(fmaxf(mx, s[f][t][0]), fmaxf(fmaxf(s[f][t][1], s[f][t][2]), s[f][t][3]));
+            LM[f] = mx;
+        }
+    });
+
+    // ---- 2. candidate thresholds: a certified lower bound of tau from the sampled maxima ----
+    // The larger of ms - 2 and the root of sum_j ((s_j - t)/2)^2 = 1 over the
+    // four lanes' sampled maxima, ms their maximum: the root over a subset of
+    // a row is at most the row's, and ms - 2 <= m - 2 <= tau.  A row with no
+    // allowed key among the sampled chunks keeps every allowed score.
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const float msr = col4_max(LM[f]);
+        const bool none = !(msr > -1e29f);
+        const float ms = none ? 0.f : msr * scale;
+        const float xl = LM[f] > -1e29f ? fmaf(LM[f], 0.5f * scale, -0.5f * ms) : -2.f;
+        const float lbx = fmaxf(col_lower_bound(xl), -1.f);
+        const float tr = fmaf(2.f, lbx, ms) / scale;
+        thrr[f] = none ? -1e29f : tr - 1e-6f * fabsf(tr) - 1e-30f;   // a little low: rounding keeps more
+        LM[f] = -kInf;   // the exact maxima come from the second pass
+    }
+
+    // ---- 3. every chunk: scores, maxima, allowed counts and the candidate lists ------------
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+        if (g == 0) rc[16 * f] = 0;   // the wave's own counters: its later atomics follow in order
     cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
         const int cb = chn * CK;
         npop += static_cast<float>(__popcll(M));
@@ -193,61 +235,67 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            float mx = LM[f];
+            float tm[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) mx = fmaxf(fmaxf(mx, s[f][t][0]), fmaxf(fmaxf(s[f][t][1], s[f][t][2]), s[f][t][3]));
-            LM[f] = mx;
+            for (int t = 0; t < 4; ++t) tm[t] = fmaxf(fmaxf(s[f][t][0], s[f][t][1]), fmaxf(s[f][t][2], s[f][t][3]));
+            const float cm = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+            LM[f] = fmaxf(LM[f], cm);
+            if (!__any(cm > thrr[f])) continue;   // uniform
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!__any(tm[t] > thrr[f])) continue;   // uniform: no candidate in this tile
+                int k = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) k += s[f][t][i] > thrr[f] ? 1 : 0;
+                if (k > 0) {
+                    int slot = atomicAdd(rc + 16 * f, k);   // this lane's k slots at once
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (s[f][t][i] > thrr[f]) {
+                            if (slot < 4 * SUB) {
+                                // a 32-bit byte offset from the head's O (a head holds at most 2^32 bytes)
+                                const unsigned off = (static_cast<unsigned>(clamp_row(rbase + 16 * f + c, L)) * D + 2u * slot) * 4u;
+                                *reinterpret_cast<f32x2*>(reinterpret_cast<char*>(outh) + off) =
+                                    f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
+                            }
+                            else
+                                ovf[f] = true;
+                            ++slot;
+                        }
+                    }
+                }
+            }
+        }
+        // every 16 chunks: the bound from the lane maxima seen so far in this
+        // pass (again a subset of the row) may exceed the sampled one
+        if (((chn - ch0) & 15) == 15) {   // uniform
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const float mr = col4_max(LM[f]);
+                if (mr > -1e29f) {
+                    const float ms = mr * scale;
+                    const float xl = LM[f] > -1e29f ? fmaf(LM[f], 0.5f * scale, -0.5f * ms) : -2.f;
+                    const float tr = fmaf(2.f, fmaxf(col_lower_bound(xl), -1.f), ms) / scale;
+                    thrr[f] = fmaxf(thrr[f], tr - 1e-6f * fabsf(tr) - 1e-30f);
+                }
+            }
         }
     });
-
-    // ---- 2. thresholds, then the candidate lists ------------------------------------------
+    // the row maximum m and the lower bound of tau from all lanes' maxima
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         m[f] = col4_max(LM[f]);
         const bool none = !(m[f] > -kInf);   // a row without an allowed key
         const float ms = none ? 0.f : m[f] * scale;
-        // the root over the four lanes' maxima, in the half-scaled shifted
-        // domain x = (s - m)/2 (at least -1: tau >= m - 2; lanes without a
-        // key hold -inf, below every root)
         const float xl = LM[f] > -kInf ? fmaf(LM[f], 0.5f * scale, -0.5f * ms) : -2.f;
         const float lbx = fmaxf(col_lower_bound(xl), -1.f);
         lbs[f] = none ? -kInf : fmaf(2.f, lbx, ms);
-        const float tr = lbs[f] / scale;
-        thrr[f] = none ? kInf : tr - 1e-6f * fabsf(tr) - 1e-30f;   // a little low: rounding keeps more
     }
-    cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
-        const int cb = chn * CK;
-        if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
-        f32x4 s[NF][4];
-        if (clean_chunk(cb, M)) scores(std::true_type{}, cb, kb, M, s);
-        else scores(std::false_type{}, cb, kb, M, s);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            float tm[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) tm[t] = fmaxf(fmaxf(s[f][t][0], s[f][t][1]), fmaxf(s[f][t][2], s[f][t][3]));
-            if (!__any(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])) > thrr[f])) continue;   // uniform
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (!__any(tm[t] > thrr[f])) continue;   // uniform: no candidate in this tile
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (s[f][t][i] > thrr[f]) {
-                        if (cnt[f] < SUB)
-                            lst(f, g)[4 * cnt[f]] = f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
-                        else
-                            ovf[f] = true;
-                        ++cnt[f];
-                    }
-                }
-            }
-        }
-    });
     // the lists written by the row's four lanes are visible to all of them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
-    // ---- tau, then O over the support, row by row ---------------------------------------
+    // ---- 4. tau, then O over the support, row by row ---------------------------------------
 #pragma unroll 1
     for (int f = 0; f < NF; ++f) {
         const int row = rbase + 16 * f + c;
@@ -264,8 +312,9 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         st.cnt = 0.f;
         st.a1 = 0.f;
         st.a2 = 0.f;
-        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // some lane's list overflowed
-        const int len = rovf ? 0 : min(cnt[f], SUB);
+        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // the row's list overflowed
+        const int nrow = min(rc[16 * f], 4 * SUB);
+        const int len = rovf ? 0 : max((nrow - g + 3) >> 2, 0);   // this lane's share: slots g, g + 4, ...
         const f32x2* mine = lst(f, g);
         float sl[SUB];
 #pragma unroll

@@ -30,6 +30,8 @@ struct WideCfg : ChunkCfg<DT, D> {
     // the kernels whose lists live in their output rows need the two
     // buffers only
     static constexpr size_t stream_lds_bytes = 2 * static_cast<size_t>(S::k_bytes);
+    // the forward adds one list counter per stationary row
+    static constexpr size_t fwd_lds_bytes = stream_lds_bytes + BR * sizeof(int);
     // two bf16 workgroups per CU (the registers allow two waves per SIMD)
     static constexpr int kOcc = DT == DT_BF16 ? 2 : 1;
 };
