@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
     typedef WideCfg<DT, D> C;
     constexpr int NF = C::NF, CK = C::CK, DQ = C::DQ, NB = C::NB;
     constexpr int SUB = D / 8;     // list entries per lane (8 bytes each in the row's dQ)
+    constexpr int NBQ = DT == DT_BF16 ? (D == 128 ? 3 : 4) : 2;   // support entries gathered per batch (registers)
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
 
@@ -228,49 +229,58 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
         float X[DQ], Y[DQ], sw = 0.f, swdp = 0.f;
 #pragma unroll
         for (int d = 0; d < DQ; ++d) { X[d] = 0.f; Y[d] = 0.f; }
+        // the four lanes' lists in one index space, in lane-group order: lane
+        // group g2's k-th entry is number P[g2] + k of the row, so that one
+        // batch of gathers spans the lists (the summation order is the
+        // lists' order)
+        int P[4];
+        P[0] = 0;
+#pragma unroll
+        for (int g2 = 0; g2 < 3; ++g2) P[g2 + 1] = P[g2] + __shfl(len, 16 * g2 + c, kWave);
+        const int T = P[3] + __shfl(len, 48 + c, kWave);
+        const int Tmax = wave_max_int<kWave>(T);
 #pragma unroll 1
-        for (int g2 = 0; g2 < 4; ++g2) {
-            const int n2 = __shfl(len, 16 * g2 + c, kWave);   // entries of lane (g2, c)
-            const int nmax = wave_max_int<kWave>(n2);
-            const f32x2* other = lst(f, g2);
-            for (int e0 = 0; e0 < nmax; e0 += NB) {
-                int key[NB];
-                float w[NB];
-                RowSlice<DT, DQ> vr[NB], kr[NB];
+        for (int e0 = 0; e0 < Tmax; e0 += NBQ) {
+            int key[NBQ], own[NBQ];
+            float w[NBQ];
+            RowSlice<DT, DQ> vr[NBQ], kr[NBQ];
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const bool in = e0 + j < n2;
-                    const f32x2 en = other[4 * (in ? e0 + j : 0)];
-                    key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
-                    w[j] = in ? en[0] : 0.f;
+            for (int j = 0; j < NBQ; ++j) {
+                const int e = e0 + j;
+                const bool in = e < T;
+                const int g2 = (e >= P[1] ? 1 : 0) + (e >= P[2] ? 1 : 0) + (e >= P[3] ? 1 : 0);
+                const int k = e - (g2 == 0 ? 0 : g2 == 1 ? P[1] : g2 == 2 ? P[2] : P[3]);
+                const f32x2 en = lst(f, in ? g2 : 0)[4 * (in ? k : 0)];
+                key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
+                w[j] = in ? en[0] : 0.f;
+                own[j] = in ? g2 : -1;   // the lane group whose list holds the entry
+            }
+#pragma unroll
+            for (int j = 0; j < NBQ; ++j) {
+                vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
+                kr[j].load(kh + static_cast<size_t>(key[j]) * D + g * DQ);
+            }
+#pragma unroll
+            for (int j = 0; j < NBQ; ++j) {
+                float part = 0.f;
+#pragma unroll
+                for (int d = 0; d < DQ; ++d) part = fmaf(dor[d], vr[j].at(d), part);
+                const float dp = col4_sum(part);
+                sw += w[j];
+                swdp = fmaf(w[j], dp, swdp);
+                const float wdp = w[j] * dp;
+#pragma unroll
+                for (int d = 0; d < DQ; ++d) {
+                    X[d] = fmaf(wdp, kr[j].at(d), X[d]);
+                    Y[d] = fmaf(w[j], kr[j].at(d), Y[d]);
                 }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
-                    kr[j].load(kh + static_cast<size_t>(key[j]) * D + g * DQ);
-                }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    float part = 0.f;
-#pragma unroll
-                    for (int d = 0; d < DQ; ++d) part = fmaf(dor[d], vr[j].at(d), part);
-                    const float dp = col4_sum(part);
-                    sw += w[j];
-                    swdp = fmaf(w[j], dp, swdp);
-                    const float wdp = w[j] * dp;
-#pragma unroll
-                    for (int d = 0; d < DQ; ++d) {
-                        X[d] = fmaf(wdp, kr[j].at(d), X[d]);
-                        Y[d] = fmaf(w[j], kr[j].at(d), Y[d]);
-                    }
-                    // the list's own lane hands the entry to key j's bucket
-                    if (kch != nullptr && g == g2 && e0 + j < n2 && w[j] > 0.f) {
-                        const int slot = atomicAdd(kch + key[j], 1);
-                        if (slot < D / 2) {
-                            float* dst = (slot < D / 4 ? dkb : dvb) + static_cast<size_t>(key[j]) * D + 4 * (slot % (D / 4));
-                            *reinterpret_cast<u32x4*>(dst) =
-                                u32x4{hq16 | static_cast<unsigned>(row), __float_as_uint(w[j]), __float_as_uint(wdp), 0u};
-                        }
+                // the list's own lane hands the entry to key j's bucket
+                if (kch != nullptr && g == own[j] && w[j] > 0.f) {
+                    const int slot = atomicAdd(kch + key[j], 1);
+                    if (slot < D / 2) {
+                        float* dst = (slot < D / 4 ? dkb : dvb) + static_cast<size_t>(key[j]) * D + 4 * (slot % (D / 4));
+                        *reinterpret_cast<u32x4*>(dst) =
+                            u32x4{hq16 | static_cast<unsigned>(row), __float_as_uint(w[j]), __float_as_uint(wdp), 0u};
                     }
                 }
             }

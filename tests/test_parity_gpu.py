@@ -200,6 +200,19 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(t1, t2)
 
 
+@pytest.mark.parametrize("gain", [2.0, 0.4])
+def test_wide_forward_is_deterministic(gain):
+    # spans beyond 2048 keys: a row's lanes take list slots from a shared
+    # counter, in a fixed order; gain 0.4 also overflows lists (the fix-up)
+    from entmax_amd import entmax_attn_fwd
+    from tests.parity_util import to_gpu
+    g = to_gpu(random_inputs(1, 2, 2304, 128, "bf16", seed=21, qk_gain=gain))
+    o1, t1 = entmax_attn_fwd(g["q"], g["k"], g["v"])
+    o2, t2 = entmax_attn_fwd(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(t1, t2)
+
+
 def test_runs_on_a_side_stream():
     from entmax_amd import entmax_attn_fwd
     inp = random_inputs(2, 2, 256, 64, "bf16", seed=10)
