@@ -59,9 +59,10 @@ template <int DT, int D>
 __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef WideCfg<DT, D> C;
-    constexpr int NF = C::NF, CK = C::CK, DQ = C::DQ, NB = C::NB;
-    constexpr int SUB = D / 8;     // list entries per lane (8 bytes each in the row's O)
+    constexpr int NF = C::NF, CK = C::CK, DQ = C::DQ;
+    constexpr int SUB = D / 8;     // list slots per lane: D/2 per row (8 bytes each in the row's O)
     constexpr int kSampleStep = 2; // the first pass reads every other chunk
+    constexpr int NBO = 4;         // list entries gathered per batch
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
     int* rowcnt = reinterpret_cast<int*>(Kb + 2 * C::k_bytes);   // list length of each of the workgroup's rows
@@ -324,34 +325,33 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         }
         const float ts = col_exact<SUB>(sl, st, SUB * 4 + 3);
         const float t = col_dyadic(st, ts);
-        // O = sum p V over the list entries above tau (all four lanes' lists)
+        // O = sum p V over the list entries above tau
         float o[DQ];
 #pragma unroll
         for (int d = 0; d < DQ; ++d) o[d] = 0.f;
+        // the row's list in slot order, NBO entries per batch of gathers
+        const int nr = rovf ? 0 : nrow;
+        const int nmax = wave_max_int<kWave>(nr);
+        const f32x2* rl = lst(f, 0);
 #pragma unroll 1
-        for (int g2 = 0; g2 < 4; ++g2) {
-            const int n2 = __shfl(len, 16 * g2 + c, kWave);   // entries of lane (g2, c)
-            const int nmax = wave_max_int<kWave>(n2);
-            const f32x2* other = lst(f, g2);
-            for (int e0 = 0; e0 < nmax; e0 += NB) {
-                int key[NB];
-                float p[NB];
-                RowSlice<DT, DQ> vr[NB];
+        for (int e0 = 0; e0 < nmax; e0 += NBO) {
+            int key[NBO];
+            float p[NBO];
+            RowSlice<DT, DQ> vr[NBO];
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const bool in = e0 + j < n2;
-                    const f32x2 en = other[4 * (in ? e0 + j : 0)];
-                    const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
-                    p[j] = in && !empty ? y * y : 0.f;
-                    key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
-                }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-#pragma unroll
-                    for (int d = 0; d < DQ; ++d) o[d] = fmaf(p[j], vr[j].at(d), o[d]);
+            for (int j = 0; j < NBO; ++j) {
+                const bool in = e0 + j < nr;
+                const f32x2 en = rl[in ? e0 + j : 0];
+                const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
+                p[j] = in && !empty ? y * y : 0.f;
+                key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
             }
+#pragma unroll
+            for (int j = 0; j < NBO; ++j) vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
+#pragma unroll
+            for (int j = 0; j < NBO; ++j)
+#pragma unroll
+                for (int d = 0; d < DQ; ++d) o[d] = fmaf(p[j], vr[j].at(d), o[d]);
         }
         // every lane of the wave has read the row's lists before any is overwritten
         __builtin_amdgcn_wave_barrier();
