@@ -259,7 +259,8 @@ def time_workload(name, steps, warmup, copy_gbs):
     result dict (ms per step, effective TFLOP/s, roofline of its longest call,
     zero fraction)."""
     import torch
-    from entmax_amd import bwd_workspace_bytes, entmax_attn_bwd, entmax_attn_fwd, entmax_attn_probs
+    from entmax_amd import (bwd_workspace_bytes, entmax_attn_bwd_saved, entmax_attn_fwd, entmax_attn_fwd_save,
+                            entmax_attn_probs, saved_bytes)
     from entmax_amd.workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[name]
@@ -273,10 +274,11 @@ def time_workload(name, steps, warmup, copy_gbs):
     esz = 4 if w.dtype == "f32" else 2
     n_el = w.B * w.H * w.L * w.d
     set_bytes = n_el * (3 * esz + 4) + w.B * w.H * w.L * 4
-    if w.backward:
-        set_bytes += n_el * (esz + 12)
-    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes)))
     ws_bytes = bwd_workspace_bytes(w.B, w.H, w.L, w.d) if w.backward else 0
+    sv_bytes = saved_bytes(w.B, w.H, w.L, w.d) if w.backward else 0
+    if w.backward:
+        set_bytes += n_el * (esz + 12) + ws_bytes + sv_bytes
+    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes)))
     sets = []
     for _ in range(nsets):
         s = {x: inp[x].to(dev) for x in ("q", "k", "v")}
@@ -287,16 +289,23 @@ def time_workload(name, steps, warmup, copy_gbs):
             s["dout"] = inp["dout"].to(dev)
             s["grads"] = [torch.empty((w.B, w.H, w.L, w.d), dtype=torch.float32, device=dev) for _ in range(3)]
             s["ws"] = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+            s["saved"] = torch.empty((max(sv_bytes, 1),), dtype=torch.uint8, device=dev)
         sets.append(s)
     torch.cuda.synchronize()
 
+    # With a backward the forward keeps each row's support for it (as a
+    # training step keeps what its backward needs) and the backward reads it.
     def step(s, mid=None):
-        entmax_attn_fwd(s["q"], s["k"], s["v"], s["key_mask"], w.causal, w.window, out=s["out"], tau_out=s["tau"])
-        if w.backward:
-            if mid is not None:
-                mid.record()   # between the forward and the backward call, same stream
-            entmax_attn_bwd(s["q"], s["k"], s["v"], s["tau"], s["dout"], s["key_mask"], w.causal, w.window,
-                            dq=s["grads"][0], dk=s["grads"][1], dv=s["grads"][2], workspace=s["ws"])
+        if not w.backward:
+            entmax_attn_fwd(s["q"], s["k"], s["v"], s["key_mask"], w.causal, w.window, out=s["out"],
+                            tau_out=s["tau"])
+            return
+        entmax_attn_fwd_save(s["q"], s["k"], s["v"], s["key_mask"], w.causal, w.window, out=s["out"],
+                             tau_out=s["tau"], saved=s["saved"])
+        if mid is not None:
+            mid.record()   # between the forward and the backward call, same stream
+        entmax_attn_bwd_saved(s["q"], s["k"], s["v"], s["tau"], s["dout"], s["saved"], s["key_mask"], w.causal,
+                              w.window, dq=s["grads"][0], dk=s["grads"][1], dv=s["grads"][2], workspace=s["ws"])
 
     for i in range(warmup):
         step(sets[i % nsets])

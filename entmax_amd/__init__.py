@@ -15,13 +15,16 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     entmax_attn_bwd,
     entmax_attn_bwd_noalloc,
+    entmax_attn_bwd_saved,
     entmax_attn_decode,
     entmax_attn_decode_bwd,
     entmax_attn_fwd,
+    entmax_attn_fwd_save,
     entmax_attn_probs,
     entmax15_rows,
     entmax15_rows_bwd,
     entmax_bisect_rows,
     entmax_bisect_rows_bwd,
     load_library,
+    saved_bytes,
 )

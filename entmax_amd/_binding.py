@@ -26,6 +26,7 @@ EXPORTS = (
     "entmax_attn_bwd",
     "entmax_attn_bwd_gqa",
     "entmax_attn_bwd_noalloc",
+    "entmax_attn_bwd_saved",
     "entmax_attn_bwd_workspace_bytes",
     "entmax_attn_decode",
     "entmax_attn_decode_bwd",
@@ -33,9 +34,11 @@ EXPORTS = (
     "entmax_attn_decode_workspace_size",
     "entmax_attn_fwd",
     "entmax_attn_fwd_gqa",
+    "entmax_attn_fwd_save",
     "entmax_attn_last_error",
     "entmax_attn_probs",
     "entmax_attn_probs_gqa",
+    "entmax_attn_saved_bytes",
     "entmax_attn_status_string",
     "entmax_attn_version",
     "entmax_bisect_rows_bwd",
@@ -82,6 +85,13 @@ def load_library(path=LIB_PATH):
     lib.entmax_attn_bwd_noalloc.restype = i32
     lib.entmax_attn_probs_gqa.argtypes = [vp, vp, u8p, i32, i32, fp, fp, i32, i32, i32, i32, i32, i32, vp]
     lib.entmax_attn_probs_gqa.restype = i32
+    lib.entmax_attn_saved_bytes.argtypes = [i32, i32, i32, i32]
+    lib.entmax_attn_saved_bytes.restype = sz
+    lib.entmax_attn_fwd_save.argtypes = [vp, vp, vp, u8p, i32, i32, fp, fp, vp, sz, i32, i32, i32, i32, i32, i32, vp]
+    lib.entmax_attn_fwd_save.restype = i32
+    lib.entmax_attn_bwd_saved.argtypes = [vp, vp, vp, u8p, i32, i32, fp, vp, vp, sz, fp, fp, fp, i32, i32, i32, i32,
+                                          i32, i32, vp, sz, vp]
+    lib.entmax_attn_bwd_saved.restype = i32
     lib.entmax15_rows_fwd.argtypes = [vp, u8p, fp, fp, i32, i32, i32, vp]
     lib.entmax15_rows_fwd.restype = i32
     lib.entmax15_rows_bwd.argtypes = [fp, fp, fp, i32, i32, vp]
@@ -202,6 +212,68 @@ def entmax_attn_fwd(q, k, v, key_mask=None, causal=False, window=0, out=None, ta
                                  _ptr(out), _ptr(tau_out), B, H, hkv, L, d, _dtype_code(q), _stream(q))
     _check(lib, rc)
     return out, tau_out
+
+
+def saved_bytes(B, H, L, d):
+    """Bytes of device memory ``entmax_attn_fwd_save`` keeps the support in
+    (a count and d/2 entries per query row)."""
+    return int(load_library().entmax_attn_saved_bytes(B, H, L, d))
+
+
+def entmax_attn_fwd_save(q, k, v, key_mask=None, causal=False, window=0, out=None, tau_out=None, saved=None):
+    """``entmax_attn_fwd`` that also keeps each query row's support for
+    ``entmax_attn_bwd_saved`` (spans above 2048 keys; elsewhere the buffer is
+    not touched and the backward recomputes as usual).
+
+    saved: a uint8 GPU tensor of at least ``saved_bytes`` bytes, or None to
+    allocate one.  Returns (out, tau, saved)."""
+    lib = load_library()
+    hkv = _check_qkv(q, k, v)
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    out = _out(out, (B, H, L, d), q, "out")
+    tau_out = _out(tau_out, (B, H, L), q, "tau_out")
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    if tau_out is None:
+        tau_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    saved = _workspace(saved, saved_bytes(B, H, L, d), q, "saved")
+    rc = lib.entmax_attn_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window),
+                                  _ptr(out), _ptr(tau_out), _ptr(saved), saved.numel(), B, H, hkv, L, d,
+                                  _dtype_code(q), _stream(q))
+    _check(lib, rc)
+    return out, tau_out, saved
+
+
+def entmax_attn_bwd_saved(q, k, v, tau, dout, saved, key_mask=None, causal=False, window=0, dq=None, dk=None,
+                          dv=None, workspace=None):
+    """``entmax_attn_bwd`` on the support kept by ``entmax_attn_fwd_save``
+    (same inputs and masks): the query side reads each row's support instead
+    of recomputing the scores.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    hkv = _check_qkv(q, k, v)
+    _check_qkv(q, dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    km = _check_mask(key_mask, q)
+    B, H, L, d = q.shape
+    if tau is None or saved is None:
+        raise ValueError("tau and saved are required")
+    _out(tau, (B, H, L), q, "tau")
+    saved = _workspace(saved, saved_bytes(B, H, L, d), q, "saved")
+    dq = _out(dq, (B, H, L, d), q, "dq")
+    dk = _out(dk, (B, hkv, L, d), q, "dk")
+    dv = _out(dv, (B, hkv, L, d), q, "dv")
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, L, d), q)
+    mk = lambda h: torch.empty((B, h, L, d), dtype=torch.float32, device=q.device)  # noqa: E731
+    dq = mk(H) if dq is None else dq
+    dk = mk(hkv) if dk is None else dk
+    dv = mk(hkv) if dv is None else dv
+    rc = lib.entmax_attn_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(km), int(bool(causal)), int(window), _ptr(tau),
+                                   _ptr(dout), _ptr(saved), saved.numel(), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv,
+                                   L, d, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(q))
+    _check(lib, rc)
+    return dq, dk, dv
 
 
 def bwd_workspace_bytes(B, H, L, d):

@@ -60,6 +60,10 @@ struct BwdArgs {
     float scale;
     int nqt;
     int fixup;     // run only for tiles holding an overflow marker in c_i
+    // the support saved by the forward (long spans; see FwdArgs), read by
+    // the query side instead of recomputing the scores
+    const int* scount;
+    const float* sent;
 };
 
 template <int DT, int D>

@@ -190,6 +190,11 @@ struct FwdArgs {
     float scale;
     int nqt;   // query tiles per head
     int fixup; // long-span kernel: only tiles with a row marked by the wide kernel
+    // the support of every query row for the backward (the wide kernel; null
+    // otherwise): scount [B, H, L] its size (-1: not saved), sent [B, H, L,
+    // D/2] its entries (w = sqrt(p), key bits)
+    int* scount;
+    float* sent;
 };
 
 // Key/value head serving query head bh = b H + h when Hkv heads serve the H

@@ -161,9 +161,9 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
         if (a.causal && a.window > 0 && a.window <= 32) return launch_short<DT, D, 2, 16>(a, st);
         return launch_short<DT, D, 2>(a, st);
     }
-    // spans beyond 2048 keys: one pass over K with candidate lists and a
-    // gather over the support (the multi-pass long-span kernel re-reads K
-    // and V more than it saves there)
+    // spans beyond 2048 keys: a sampled pass and a pass over K with
+    // candidate lists, then a gather over the support (the multi-pass
+    // long-span kernel re-reads K and V more than it saves there)
     if (s64 > 2048) return launch_wide<DT, D>(a, st);
     // (float32 at d = 128 would not keep its scores in registers)
     if constexpr (!(DT == ea::DT_F32 && D == 128))
@@ -172,8 +172,9 @@ int dispatch_fwd(ea::FwdArgs a, hipStream_t st) {
 }
 
 // Backward: query side (dQ, c) then key side (dK, dV), all on one stream.
-// Spans beyond 2048 keys take the wide query-side kernel, which also fills
-// the support buckets of the key side; its rows with an overflowing support
+// Spans beyond 2048 keys take the wide query-side kernel (on the forward's
+// saved support when given, else with a pass over the keys), which also
+// fills the support buckets of the key side; its rows with an overflowing support
 // are finished by the tile kernel in fix-up mode, and keys whose bucket
 // overflowed by the key-side recompute kernel in fix-up mode.  Shorter spans
 // take the tile kernel and the key-side recompute kernel.
@@ -182,6 +183,7 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
     typedef ea::WideCfg<DT, D> W;
     auto kq = ea::bwd_kernel<DT, D>;
     auto kw = ea::bwd_q_kernel<DT, D>;
+    auto ks = ea::bwd_q_kernel<DT, D, true>;
     auto kv = ea::bwd_kv_kernel<DT, D>;
     constexpr size_t lds_q = ea::BwdCfg<DT, D>::lds_bytes;
     int rc = set_lds(kq, lds_q);
@@ -199,7 +201,10 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
                            dim3(ea::kThreads), 0, st, reinterpret_cast<float*>(a.kcnt), nz);
         a.nqt = (L + W::BR - 1) / W::BR;
         a.fixup = 0;
-        hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
+        if (a.scount != nullptr)   // the forward's saved support: no pass over the keys
+            hipLaunchKernelGGL(ks, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
         a.fixup = 1;
     } else {
         a.kcnt = nullptr;
@@ -257,6 +262,26 @@ int scratch_addr(void** out) {
     }
     *out = g_scratch_ptr[dev];
     return ENTMAX_OK;
+}
+
+// Forward after the argument checks.
+int fwd_run(ea::FwdArgs a, int d, int dtype, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == ENTMAX_BF16)
+        return d == 64 ? dispatch_fwd<ea::DT_BF16, 64>(a, st) : dispatch_fwd<ea::DT_BF16, 128>(a, st);
+    return d == 64 ? dispatch_fwd<ea::DT_F32, 64>(a, st) : dispatch_fwd<ea::DT_F32, 128>(a, st);
+}
+
+// The saved support of the forward (spans beyond 2048 keys, where the wide
+// kernels run): a count per query row, then d/2 entries of 8 bytes per row;
+// the count part 256-byte aligned.
+bool saves_support(int L, int causal, int window) { return max_span(L, 64, causal, window) > 2048; }
+size_t saved_part(int B, int H, int L) {
+    const size_t n = static_cast<size_t>(B) * H * L * sizeof(int);
+    return (n + 255) & ~static_cast<size_t>(255);
+}
+size_t saved_bytes(int B, int H, int L, int d) {
+    return saved_part(B, H, L) + static_cast<size_t>(B) * H * L * (d / 2) * 8;
 }
 
 }  // namespace
@@ -434,10 +459,9 @@ int entmax_attn_fwd_gqa(const void* q, const void* k, const void* v, const uint8
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
     a.nqt = 0;
     a.fixup = 0;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dtype == ENTMAX_BF16)
-        return d == 64 ? dispatch_fwd<ea::DT_BF16, 64>(a, st) : dispatch_fwd<ea::DT_BF16, 128>(a, st);
-    return d == 64 ? dispatch_fwd<ea::DT_F32, 64>(a, st) : dispatch_fwd<ea::DT_F32, 128>(a, st);
+    a.scount = nullptr;
+    a.sent = nullptr;
+    return fwd_run(a, d, dtype, stream);
 }
 
 int entmax_attn_probs_gqa(const void* q, const void* k, const uint8_t* key_mask, int causal, int window,
@@ -479,8 +503,15 @@ namespace {
 // Backward after the workspace checks: ws is a workspace of bwd_ws_bytes.
 int bwd_run(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,
             const float* tau, const void* dout, float* dq, float* dk, float* dv,
-            int B, int H, int Hkv, int L, int d, int dtype, void* ws, void* stream) {
+            int B, int H, int Hkv, int L, int d, int dtype, void* ws, void* stream,
+            const void* saved = nullptr) {
     ea::BwdArgs a;
+    a.scount = nullptr;
+    a.sent = nullptr;
+    if (saved != nullptr) {
+        a.scount = static_cast<const int*>(saved);
+        a.sent = reinterpret_cast<const float*>(static_cast<const char*>(saved) + saved_part(B, H, L));
+    }
     a.q = q; a.k = k; a.v = v; a.key_mask = key_mask; a.tau = tau; a.dout = dout;
     a.dq = dq; a.dk = dk; a.dv = dv;
     char* w = static_cast<char*>(ws);
@@ -541,6 +572,60 @@ int entmax_attn_bwd_noalloc(const void* q, const void* k, const void* v, const u
     // c_i of every query row is written before it is read, and the bucket
     // counters are cleared by the call itself (a fill kernel)
     return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype, ws, stream);
+}
+
+size_t entmax_attn_saved_bytes(int B, int H, int L, int d) {
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0) return 0;
+    return saved_bytes(B, H, L, d);
+}
+
+int entmax_attn_fwd_save(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal,
+                         int window, float* out, float* tau_out, void* saved, size_t saved_bytes_given,
+                         int B, int H, int Hkv, int L, int d, int dtype, void* stream) {
+    if (!q || !k || !v || !out || !tau_out || !saved)
+        return fail(ENTMAX_ERR_INVALID_ARG, "q, k, v, out, tau_out and saved must not be NULL");
+    if (misaligned({q, k, v, out}, 16) || misaligned({tau_out}, 4) || misaligned({saved}, 256))
+        return fail(ENTMAX_ERR_INVALID_ARG,
+                    "q, k, v and out must be 16-byte aligned, tau_out 4-byte aligned, saved 256-byte aligned");
+    int rc = check_common(B, H, Hkv, L, d, dtype, causal, window);
+    if (rc) return rc;
+    const size_t need = saved_bytes(B, H, L, d);
+    if (saved_bytes_given < need)
+        return fail(ENTMAX_ERR_INVALID_ARG, "saved buffer of %zu bytes, %zu needed", saved_bytes_given, need);
+    ea::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.key_mask = key_mask;
+    a.out = out; a.tau = tau_out;
+    a.B = B; a.H = H; a.L = L; a.Hkv = Hkv;
+    a.causal = causal ? 1 : 0; a.window = window;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    a.nqt = 0;
+    a.fixup = 0;
+    a.scount = nullptr;
+    a.sent = nullptr;
+    if (saves_support(L, causal, window)) {
+        a.scount = static_cast<int*>(saved);
+        a.sent = reinterpret_cast<float*>(static_cast<char*>(saved) + saved_part(B, H, L));
+    }
+    return fwd_run(a, d, dtype, stream);
+}
+
+int entmax_attn_bwd_saved(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal,
+                          int window, const float* tau, const void* dout, const void* saved,
+                          size_t saved_bytes_given, float* dq, float* dk, float* dv, int B, int H, int Hkv, int L,
+                          int d, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = bwd_check(q, k, v, tau, dout, dq, dk, dv, causal, window, B, H, Hkv, L, d, dtype);
+    if (rc) return rc;
+    if (!workspace || !saved) return fail(ENTMAX_ERR_INVALID_ARG, "workspace and saved must not be NULL");
+    if (misaligned({workspace, saved}, 256))
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace and saved must be 256-byte aligned");
+    const size_t need = bwd_ws_bytes(B, H, L);
+    if (workspace_bytes < need)
+        return fail(ENTMAX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const size_t sneed = saved_bytes(B, H, L, d);
+    if (saved_bytes_given < sneed)
+        return fail(ENTMAX_ERR_INVALID_ARG, "saved buffer of %zu bytes, %zu needed", saved_bytes_given, sneed);
+    return bwd_run(q, k, v, key_mask, causal, window, tau, dout, dq, dk, dv, B, H, Hkv, L, d, dtype, workspace,
+                   stream, saves_support(L, causal, window) ? saved : nullptr);
 }
 
 int entmax_attn_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int causal, int window,

@@ -333,10 +333,15 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         const int nr = rovf ? 0 : nrow;
         const int nmax = wave_max_int<kWave>(nr);
         const f32x2* rl = lst(f, 0);
+        // the support, kept for the backward when asked: entries with p > 0
+        // in list order (the same in the row's four lanes; lane group 0 writes)
+        const size_t srow = static_cast<size_t>(bh) * L + clamp_row(row, L);
+        f32x2* se = a.sent != nullptr ? reinterpret_cast<f32x2*>(a.sent) + srow * (D / 2) : nullptr;
+        int ns = 0;
 #pragma unroll 1
         for (int e0 = 0; e0 < nmax; e0 += NBO) {
             int key[NBO];
-            float p[NBO];
+            float p[NBO], yv[NBO];
             RowSlice<DT, DQ> vr[NBO];
 #pragma unroll
             for (int j = 0; j < NBO; ++j) {
@@ -344,15 +349,26 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
                 const f32x2 en = rl[in ? e0 + j : 0];
                 const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
                 p[j] = in && !empty ? y * y : 0.f;
+                yv[j] = y;
                 key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
             }
 #pragma unroll
             for (int j = 0; j < NBO; ++j) vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
+            if (se != nullptr) {
+#pragma unroll
+                for (int j = 0; j < NBO; ++j) {
+                    if (p[j] > 0.f) {
+                        if (g == 0 && row < L) se[ns] = f32x2{yv[j], __uint_as_float(static_cast<unsigned>(key[j]))};
+                        ++ns;
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < NBO; ++j)
 #pragma unroll
                 for (int d = 0; d < DQ; ++d) o[d] = fmaf(p[j], vr[j].at(d), o[d]);
         }
+        if (a.scount != nullptr && g == 0 && row < L) a.scount[srow] = rovf ? -1 : ns;   // -1: recomputed, not saved
         // every lane of the wave has read the row's lists before any is overwritten
         __builtin_amdgcn_wave_barrier();
         if (row < L) {

@@ -138,6 +138,50 @@ int entmax_attn_probs_gqa(const void *q, const void *k,
                           const float *tau, float *probs,
                           int B, int H, int H_kv, int L, int d, int dtype, void *stream);
 
+/*
+ * Forward that also keeps each query row's support for the backward (the
+ * keys with p_ij > 0: the sparse aggregation of the "RoBERTa Base with
+ * AdaSplash Attention" model card, Architecture Overview), so that
+ * entmax_attn_bwd_saved finds them without recomputing the scores.  Same
+ * arguments and results as entmax_attn_fwd_gqa, plus:
+ *  - tau_out is required.
+ *  - saved: caller-owned DEVICE memory, 256-byte aligned, of at least
+ *    entmax_attn_saved_bytes(B, H, L, d) bytes: per query row a count
+ *    (int32, -1 where the row was finished by the recompute fix-up and is
+ *    not kept; the counts first, 256-byte aligned), then d/2 entries per
+ *    row of 8 bytes each (float w_ij = sqrt(p_ij), uint32 key index), in
+ *    the order the forward summed them.  Written only where the key span
+ *    exceeds 2048 keys (the wide kernels); elsewhere left untouched.  No
+ *    initialisation needed; it must stay unchanged until the matching
+ *    entmax_attn_bwd_saved.  A too small or misaligned buffer returns
+ *    ENTMAX_ERR_INVALID_ARG.
+ * entmax_attn_saved_bytes returns 0 for non-positive sizes.
+ */
+size_t entmax_attn_saved_bytes(int B, int H, int L, int d);
+int entmax_attn_fwd_save(const void *q, const void *k, const void *v,
+                         const uint8_t *key_mask, int causal, int window,
+                         float *out, float *tau_out, void *saved, size_t saved_bytes,
+                         int B, int H, int H_kv, int L, int d, int dtype, void *stream);
+
+/*
+ * entmax_attn_bwd_gqa on the support kept by entmax_attn_fwd_save, called
+ * with the same q, k, v, key_mask, causal, window and tau: the query side
+ * reads each row's support instead of recomputing the scores (rows without
+ * a kept support are recomputed, as the rows whose support overflows in
+ * entmax_attn_bwd_gqa).  Where the key span is at most 2048 keys it is
+ * entmax_attn_bwd_gqa.  Arguments, workspace, results and determinism as
+ * entmax_attn_bwd_gqa (w comes from the forward's own arithmetic, so the
+ * results agree with entmax_attn_bwd_gqa's to rounding, not bit for bit);
+ * saved and saved_bytes as above.
+ */
+int entmax_attn_bwd_saved(const void *q, const void *k, const void *v,
+                          const uint8_t *key_mask, int causal, int window,
+                          const float *tau, const void *dout,
+                          const void *saved, size_t saved_bytes,
+                          float *dq, float *dk, float *dv,
+                          int B, int H, int H_kv, int L, int d, int dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* entmax_attn_bwd_noalloc: entmax_attn_bwd_gqa for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  Same arguments, results and

@@ -104,17 +104,23 @@ def check_forward(inp, heads=None, rows=None, check_probs=True, label="", band=N
     return errs, out, tau
 
 
-def check_backward(inp, heads=None, label="", tau=None):
-    from entmax_amd import entmax_attn_bwd, entmax_attn_fwd
+def check_backward(inp, heads=None, label="", tau=None, saved=False):
+    """With saved: the forward keeps the support (entmax_attn_fwd_save) and
+    the backward reads it (entmax_attn_bwd_saved)."""
+    from entmax_amd import entmax_attn_bwd, entmax_attn_bwd_saved, entmax_attn_fwd, entmax_attn_fwd_save
     g = to_gpu(inp)
     q, k, v, do, km = g["q"], g["k"], g["v"], g["dout"], g["key_mask"]
     causal, window = bool(inp["causal"]), int(inp["window"])
     B, H, L, d = q.shape
     tol = TOL[dtype_name(q)]
-    log(f"[parity] bwd {label} B{B} H{H} L{L} d{d} {dtype_name(q)} causal={causal} window={window}")
-    if tau is None:
-        _, tau = entmax_attn_fwd(q, k, v, km, causal, window)
-    dq, dk, dv = entmax_attn_bwd(q, k, v, tau, do, km, causal, window)
+    log(f"[parity] bwd {label} B{B} H{H} L{L} d{d} {dtype_name(q)} causal={causal} window={window} saved={saved}")
+    if saved:
+        _, tau, sv = entmax_attn_fwd_save(q, k, v, km, causal, window)
+        dq, dk, dv = entmax_attn_bwd_saved(q, k, v, tau, do, sv, km, causal, window)
+    else:
+        if tau is None:
+            _, tau = entmax_attn_fwd(q, k, v, km, causal, window)
+        dq, dk, dv = entmax_attn_bwd(q, k, v, tau, do, km, causal, window)
     torch.cuda.synchronize()
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]

@@ -107,6 +107,45 @@ def test_bwd_and_probs_reject_null(lib):
     assert lib.entmax_attn_probs(P, P, None, 0, 0, P, P, 1, 1, 8, 32, 1, None) == 2
 
 
+def test_saved_support_size_and_arguments(lib):
+    # a count per query row (rounded up to 256 bytes), then d/2 entries of
+    # 8 bytes per row
+    assert lib.entmax_attn_saved_bytes(1, 32, 8192, 128) == 32 * 8192 * 4 + 32 * 8192 * 64 * 8
+    assert lib.entmax_attn_saved_bytes(2, 3, 7, 64) == 256 + 42 * 32 * 8
+    assert lib.entmax_attn_saved_bytes(0, 3, 7, 64) == 0
+    sb = lib.entmax_attn_saved_bytes(1, 1, 8, 64)
+    # q, k, v, mask, causal, window, out, tau, saved, saved_bytes, B, H, Hkv, L, d, dtype, stream
+    fargs = [P, P, P, None, 0, 0, P, P, W256, sb, 1, 1, 1, 8, 64, 1, None]
+    for i in (0, 1, 2, 6, 7, 8):
+        a = list(fargs)
+        a[i] = None
+        assert lib.entmax_attn_fwd_save(*a) == 1, i
+    a = list(fargs)
+    a[9] = sb - 1                                                        # saved buffer too small
+    assert lib.entmax_attn_fwd_save(*a) == 1
+    assert b"saved" in lib.entmax_attn_last_error()
+    a = list(fargs)
+    a[8] = ctypes.c_void_p(272)                                          # not 256-byte aligned
+    assert lib.entmax_attn_fwd_save(*a) == 1
+    ws = lib.entmax_attn_bwd_workspace_bytes(1, 1, 8, 64)
+    # q, k, v, mask, causal, window, tau, dout, saved, saved_bytes, dq, dk, dv, B, H, Hkv, L, d, dtype, ws,
+    # ws_bytes, stream
+    bargs = [P, P, P, None, 0, 0, P, P, W256, sb, P, P, P, 1, 1, 1, 8, 64, 1, W256, ws, None]
+    for i in (0, 1, 2, 6, 7, 8, 10, 11, 12, 19):
+        a = list(bargs)
+        a[i] = None
+        assert lib.entmax_attn_bwd_saved(*a) == 1, i
+    a = list(bargs)
+    a[9] = sb - 1
+    assert lib.entmax_attn_bwd_saved(*a) == 1
+    a = list(bargs)
+    a[20] = ws - 1
+    assert lib.entmax_attn_bwd_saved(*a) == 1
+    a = list(bargs)
+    a[17] = 96                                                           # unsupported d
+    assert lib.entmax_attn_bwd_saved(*a) == 2
+
+
 def test_binding_validates_before_calling():
     import torch
     from entmax_amd import entmax_attn_fwd

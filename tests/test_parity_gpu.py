@@ -262,6 +262,37 @@ def test_backward_long_span_f32_masked_window():
     check_backward(inp, label="long span f32 masked window")
 
 
+# ---- backward on the support the forward kept ------------------------------------
+
+@pytest.mark.parametrize("L,d,dtype,gain,causal,window,lengths", [
+    (2304, 128, "bf16", 2.0, False, 0, None),       # wide: every row kept
+    (2400, 128, "bf16", 0.4, False, 0, None),       # supports of hundreds: rows not kept, fix-up
+    (3000, 128, "bf16", 1.0, True, 0, None),        # causal, ragged tail of rows
+    (2600, 64, "f32", 1.0, True, 2200, [2600, 2311]),   # window, key padding, float32
+    (300, 64, "bf16", 1.5, False, 0, None),         # short span: the buffer is not used
+])
+def test_backward_on_saved_support(L, d, dtype, gain, causal, window, lengths):
+    B = 1 if lengths is None else len(lengths)
+    inp = random_inputs(B, 2, L, d, dtype, seed=L + 31, qk_gain=gain, key_lengths=lengths)
+    inp["causal"], inp["window"] = causal, window
+    check_backward(inp, label=f"saved support gain{gain}", saved=True)
+
+
+def test_backward_on_saved_support_grouped_and_repeatable():
+    from entmax_amd import entmax_attn_bwd_saved, entmax_attn_fwd_save
+    from tests.parity_util import to_gpu
+    inp = random_inputs(1, 4, 2304, 64, "bf16", seed=41, qk_gain=2.0)
+    inp["k"], inp["v"] = inp["k"][:, :2].contiguous(), inp["v"][:, :2].contiguous()   # two key/value heads
+    check_backward(inp, label="saved support grouped", saved=True)
+    g = to_gpu(inp)
+    _, tau, sv = entmax_attn_fwd_save(g["q"], g["k"], g["v"])
+    a = entmax_attn_bwd_saved(g["q"], g["k"], g["v"], tau, g["dout"], sv)
+    b = entmax_attn_bwd_saved(g["q"], g["k"], g["v"], tau, g["dout"], sv)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("L,d,gain", [(300, 64, 1.5), (2304, 128, 2.0), (2200, 64, 0.3)])
 def test_backward_is_deterministic(L, d, gain):
     # query rows and key rows each have one owner and a fixed summation
