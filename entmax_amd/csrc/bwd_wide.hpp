@@ -25,14 +25,14 @@
 //    dQ_i = scale (sum w dp K - c_i sum w K).  A row whose support outgrows
 //    its lists gets the overflow marker in c_i, and the tile-wise kernel of
 //    bwd.hpp finishes it in fix-up mode.
-//    In the saved mode the support comes from the forward instead (the wide
-//    forward kept each row's entries with p > 0 as (w, key) in a caller's
-//    buffer), and the kernel skips the pass over the keys; a row the
-//    forward did not save goes to the fix-up as an overflowing one does.
 //    With support buckets (kcnt non-null), every entry (i, j) with w > 0
 //    also goes to key j's bucket: (query, w, w dp), 16 bytes, at a slot
 //    taken with an integer atomic on kcnt_j, stored in j's dK and dV rows
 //    (still unwritten: KCAP = D/2 slots).
+//  * bwd_q_saved_kernel: the same per-row work on the support the wide
+//    forward kept (entries with p > 0 as (w, key) in a caller's buffer), so
+//    no score is formed: D/8 lanes per row, 8 columns each; a row the
+//    forward did not keep goes to the fix-up as an overflowing row does.
 //  * bwd_kv_gather_kernel: per key, the bucket is put in query order and
 //    summed: dK_j = scale sum (w dp - w c_i) Q_i, dV_j = sum w^2 dO_i.  The
 //    order is fixed by the entries themselves, not by the atomics, so
@@ -64,9 +64,7 @@ namespace ea {
 // ============================================================================
 // Query side: dQ and c for rows of long key spans
 // ============================================================================
-// SAVED: the support of every row comes from the forward (a.scount, a.sent)
-// instead of a pass over the keys.
-template <int DT, int D, bool SAVED = false>
+template <int DT, int D>
 __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel(BwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef WideCfg<DT, D> C;
@@ -106,13 +104,23 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
     int wlo, whi;   // keys the wave's rows may attend
     key_range(rbase, NF * 16, L, a.causal, a.window, &wlo, &whi);
 
+    QFrag<DT, D> qf[NF];
+    float tau[NF], traw[NF];
     int cnt[NF];        // entries in this lane's list of the row
     bool ovf[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
+        const int row = rbase + 16 * f + c;
+        qf[f].load(qh, row, L, g);
+        tau[f] = row < L ? a.tau[static_cast<size_t>(bh) * L + clamp_row(row, L)] : kInf;
+        // raw-accumulator threshold, a little low (the exact test is the fma
+        // below); +inf for rows without an allowed key
+        const float tr = tau[f] / a.scale;
+        traw[f] = tau[f] < kInf ? tr - 1e-6f * fabsf(tr) - 1e-30f : kInf;
         cnt[f] = 0;
         ovf[f] = false;
     }
+    const bool allrows = rbase + NF * 16 <= L;
     // support buckets of the key side: query head within its group, and the
     // key/value head's dK, dV rows and counters
     const unsigned hq16 = static_cast<unsigned>((bh - b * a.H) % (a.H / a.Hkv)) << 16;
@@ -125,131 +133,101 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
         return reinterpret_cast<f32x2*>(dqh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g;
     };
 
-    if constexpr (!SAVED) {   // the support from a pass over the keys
-        QFrag<DT, D> qf[NF];
-        float tau[NF], traw[NF];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            const int row = rbase + 16 * f + c;
-            qf[f].load(qh, row, L, g);
-            tau[f] = row < L ? a.tau[static_cast<size_t>(bh) * L + clamp_row(row, L)] : kInf;
-            // raw-accumulator threshold, a little low (the exact test is the fma
-            // below); +inf for rows without an allowed key
-            const float tr = tau[f] / a.scale;
-            traw[f] = tau[f] < kInf ? tr - 1e-6f * fabsf(tr) - 1e-30f : kInf;
-        }
-        const bool allrows = rbase + NF * 16 <= L;
+    ChunkStream<DT, D, 2, 1> cs;
+    cs.Kb = Kb;
+    cs.Vb = nullptr;
+    cs.kh = kh;
+    cs.vh = vh;
+    cs.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+    cs.hasm = hasm;
+    cs.L = L;
+    cs.tid = tid;
+    cs.lane = lane;
+    constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
+    const int klane = c * C::KSTR + 16 * g;
 
-        ChunkStream<DT, D, 2, 1> cs;
-        cs.Kb = Kb;
-        cs.Vb = nullptr;
-        cs.kh = kh;
-        cs.vh = vh;
-        cs.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
-        cs.hasm = hasm;
-        cs.L = L;
-        cs.tid = tid;
-        cs.lane = lane;
-        constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
-        const int klane = c * C::KSTR + 16 * g;
-
-        // ---- support lists ----------------------------------------------------------------
-        // A chunk of valid keys that no causal / window bound crosses and whose
-        // rows are all query rows ("clean", uniform) takes plain products and no
-        // masking; the support test itself only runs for a fragment whose
-        // running maximum clears one of its rows' thresholds.
-        auto body = [&](auto clean_tag, int cb, const char* kb, unsigned long long M) {
-            constexpr bool CLEAN = decltype(clean_tag)::value;
-            f32x4 s[NF][4];
+    // ---- support lists ----------------------------------------------------------------
+    // A chunk of valid keys that no causal / window bound crosses and whose
+    // rows are all query rows ("clean", uniform) takes plain products and no
+    // masking; the support test itself only runs for a fragment whose
+    // running maximum clears one of its rows' thresholds.
+    auto body = [&](auto clean_tag, int cb, const char* kb, unsigned long long M) {
+        constexpr bool CLEAN = decltype(clean_tag)::value;
+        f32x4 s[NF][4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if constexpr (CLEAN) {
-                    f32x4 o[NF];
-                    tile_products<DT, D, NF>(kb + klane + 16 * t * C::KSTR, qf, o);
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (CLEAN) {
+                f32x4 o[NF];
+                tile_products<DT, D, NF>(kb + klane + 16 * t * C::KSTR, qf, o);
 #pragma unroll
-                    for (int f = 0; f < NF; ++f) s[f][t] = o[f];
-                } else {
-                    const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
-                    const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
-                    if (!ok) {
+                for (int f = 0; f < NF; ++f) s[f][t] = o[f];
+            } else {
+                const unsigned mb = static_cast<unsigned>((M >> (16 * t)) & 0xFFFFull);
+                const bool ok = mb != 0u && cb + 16 * t < whi && cb + 16 * t + 16 > wlo;   // uniform
+                if (!ok) {
 #pragma unroll
-                        for (int f = 0; f < NF; ++f) s[f][t] = f32x4{-kInf, -kInf, -kInf, -kInf};
-                        continue;
-                    }
-                    const unsigned bias = ((mb >> c) & 1u) ? 0u : kMaskedBits;
-                    f32x4 o[NF];
-                    tile_products<DT, D, NF, true>(kb + klane + 16 * t * C::KSTR, qf, o, bias, g);
-#pragma unroll
-                    for (int f = 0; f < NF; ++f) s[f][t] = o[f];
-#pragma unroll
-                    for (int f = 0; f < NF; ++f) {
-                        const int row = rbase + 16 * f + c;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = cb + 16 * t + 4 * g + i;
-                            const bool okk = row < L && (!a.causal || allowed_ij(row, key, 1, a.window));
-                            s[f][t][i] = okk ? s[f][t][i] : -kInf;
-                        }
-                    }
+                    for (int f = 0; f < NF; ++f) s[f][t] = f32x4{-kInf, -kInf, -kInf, -kInf};
+                    continue;
                 }
-            }
+                const unsigned bias = ((mb >> c) & 1u) ? 0u : kMaskedBits;
+                f32x4 o[NF];
+                tile_products<DT, D, NF, true>(kb + klane + 16 * t * C::KSTR, qf, o, bias, g);
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                float tm[4];
+                for (int f = 0; f < NF; ++f) s[f][t] = o[f];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) tm[t] = fmaxf(fmaxf(s[f][t][0], s[f][t][1]), fmaxf(s[f][t][2], s[f][t][3]));
-                if (!__any(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])) > traw[f])) continue;   // uniform: no support entry here
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (!__any(tm[t] > traw[f])) continue;   // uniform: none in this tile
+                for (int f = 0; f < NF; ++f) {
+                    const int row = rbase + 16 * f + c;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (s[f][t][i] > traw[f]) {
-                            // w = (s - tau)/2; an entry the low raw threshold let in
-                            // by rounding gets w = 0 and contributes nothing
-                            if (cnt[f] < SUB)
-                                lst(f, g)[4 * cnt[f]] = f32x2{fmaxf(0.5f * fmaf(s[f][t][i], a.scale, -tau[f]), 0.f),
-                                                          __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
-                            else
-                                ovf[f] = true;
-                            ++cnt[f];
-                        }
+                        const int key = cb + 16 * t + 4 * g + i;
+                        const bool okk = row < L && (!a.causal || allowed_ij(row, key, 1, a.window));
+                        s[f][t][i] = okk ? s[f][t][i] : -kInf;
                     }
                 }
             }
-        };
-        cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
-            const int cb = chn * CK;
-            if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
-            const bool cross = a.causal && (cb + CK - 1 > rbase || (a.window > 0 && cb <= rbase + NF * 16 - 1 - a.window));
-            if (M == ~0ull && !cross && allrows) body(std::true_type{}, cb, kb, M);
-            else body(std::false_type{}, cb, kb, M);
-        });
-        // the lists written by the row's four lanes are visible to all of them
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            float tm[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tm[t] = fmaxf(fmaxf(s[f][t][0], s[f][t][1]), fmaxf(s[f][t][2], s[f][t][3]));
+            if (!__any(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3])) > traw[f])) continue;   // uniform: no support entry here
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!__any(tm[t] > traw[f])) continue;   // uniform: none in this tile
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (s[f][t][i] > traw[f]) {
+                        // w = (s - tau)/2; an entry the low raw threshold let in
+                        // by rounding gets w = 0 and contributes nothing
+                        if (cnt[f] < SUB)
+                            lst(f, g)[4 * cnt[f]] = f32x2{fmaxf(0.5f * fmaf(s[f][t][i], a.scale, -tau[f]), 0.f),
+                                                      __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
+                        else
+                            ovf[f] = true;
+                        ++cnt[f];
+                    }
+                }
+            }
+        }
+    };
+    cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
+        const int cb = chn * CK;
+        if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
+        const bool cross = a.causal && (cb + CK - 1 > rbase || (a.window > 0 && cb <= rbase + NF * 16 - 1 - a.window));
+        if (M == ~0ull && !cross && allrows) body(std::true_type{}, cb, kb, M);
+        else body(std::false_type{}, cb, kb, M);
+    });
+    // the lists written by the row's four lanes are visible to all of them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
     // ---- c and dQ per row ---------------------------------------------------------------
 #pragma unroll 1
     for (int f = 0; f < NF; ++f) {
         const int row = rbase + 16 * f + c;
-        bool rovf;
-        int len = 0;
-        int T;   // the row's entries (the same in its four lanes)
-        const f32x2* se = nullptr;
-        if constexpr (SAVED) {
-            // the forward's support of the row: entries (w, key) in key order of
-            // its list; a negative count: not saved (recomputed by the fix-up)
-            const size_t srow = static_cast<size_t>(bh) * L + clamp_row(row, L);
-            const int ns = row < L ? a.scount[srow] : 0;
-            rovf = ns < 0;
-            T = rovf ? 0 : ns;
-            se = reinterpret_cast<const f32x2*>(a.sent) + srow * (D / 2);
-        } else {
-            rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // some lane's list overflowed
-            len = rovf ? 0 : min(cnt[f], SUB);
-        }
+        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // some lane's list overflowed
+        const int len = rovf ? 0 : min(cnt[f], SUB);
         float dor[DQ];
         load_cols<DT, DQ>(doh + static_cast<size_t>(clamp_row(row, L)) * D + g * DQ, dor);
         float X[DQ], Y[DQ], sw = 0.f, swdp = 0.f;
@@ -259,12 +237,11 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
         // group g2's k-th entry is number P[g2] + k of the row, so that one
         // batch of gathers spans the lists (the summation order is the
         // lists' order)
-        int P[4] = {0, 0, 0, 0};
-        if constexpr (!SAVED) {
+        int P[4];
+        P[0] = 0;
 #pragma unroll
-            for (int g2 = 0; g2 < 3; ++g2) P[g2 + 1] = P[g2] + __shfl(len, 16 * g2 + c, kWave);
-            T = P[3] + __shfl(len, 48 + c, kWave);
-        }
+        for (int g2 = 0; g2 < 3; ++g2) P[g2 + 1] = P[g2] + __shfl(len, 16 * g2 + c, kWave);
+        const int T = P[3] + __shfl(len, 48 + c, kWave);
         const int Tmax = wave_max_int<kWave>(T);
 #pragma unroll 1
         for (int e0 = 0; e0 < Tmax; e0 += NBQ) {
@@ -275,18 +252,12 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
             for (int j = 0; j < NBQ; ++j) {
                 const int e = e0 + j;
                 const bool in = e < T;
-                f32x2 en;
-                if constexpr (SAVED) {
-                    en = se[in ? e : 0];
-                    own[j] = in ? (e & 3) : -1;   // the lane group that hands it to its bucket
-                } else {
-                    const int g2 = (e >= P[1] ? 1 : 0) + (e >= P[2] ? 1 : 0) + (e >= P[3] ? 1 : 0);
-                    const int k = e - (g2 == 0 ? 0 : g2 == 1 ? P[1] : g2 == 2 ? P[2] : P[3]);
-                    en = lst(f, in ? g2 : 0)[4 * (in ? k : 0)];
-                    own[j] = in ? g2 : -1;   // the lane group whose list holds the entry
-                }
+                const int g2 = (e >= P[1] ? 1 : 0) + (e >= P[2] ? 1 : 0) + (e >= P[3] ? 1 : 0);
+                const int k = e - (g2 == 0 ? 0 : g2 == 1 ? P[1] : g2 == 2 ? P[2] : P[3]);
+                const f32x2 en = lst(f, in ? g2 : 0)[4 * (in ? k : 0)];
                 key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
                 w[j] = in ? en[0] : 0.f;
+                own[j] = in ? g2 : -1;   // the lane group whose list holds the entry
             }
 #pragma unroll
             for (int j = 0; j < NBQ; ++j) {
@@ -338,6 +309,107 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
             }
         }
     }
+}
+
+// ============================================================================
+// Query side on the forward's saved support
+// ============================================================================
+// D/8 lanes per query row (8 columns each), 256/(D/8) rows per workgroup;
+// grid: ceil(B H L / rows per workgroup).  Entries are taken in the order
+// the forward kept them; per entry the row's lanes gather V_j and K_j.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void bwd_q_saved_kernel(BwdArgs a) {
+    typedef typename InT<DT>::type T;
+    constexpr int LPR = D / 8;          // lanes per row
+    constexpr int CPL = 8;              // columns per lane
+    constexpr int NBS = 4;              // entries gathered per batch
+    const int tid = threadIdx.x;
+    const int l = tid % LPR;            // the lane's column group
+    const long long rows = static_cast<long long>(a.B) * a.H * a.L;
+    const long long gr = static_cast<long long>(blockIdx.x) * (kThreads / LPR) + tid / LPR;
+    const bool valid = gr < rows;       // the same in a row's lanes
+    const long long r = valid ? gr : 0;
+    const int bh = static_cast<int>(r / a.L);
+    const int row = static_cast<int>(r - static_cast<long long>(bh) * a.L);
+    const int b = bh / a.H;
+    const int L = a.L;
+    const size_t kv_off = static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L * D;
+    const T* kh = static_cast<const T*>(a.k) + kv_off;
+    const T* vh = static_cast<const T*>(a.v) + kv_off;
+    // support buckets of the key side (query head within its group, row)
+    const unsigned code = (static_cast<unsigned>((bh - b * a.H) % (a.H / a.Hkv)) << 16) | static_cast<unsigned>(row);
+    int* kch = a.kcnt + static_cast<size_t>(kv_head(bh, a.H, a.Hkv)) * L;
+    float* dkb = a.dk + kv_off;
+    float* dvb = a.dv + kv_off;
+
+    const int ns = valid ? a.scount[r] : 0;
+    const bool rovf = ns < 0;           // not kept by the forward: the fix-up finishes the row
+    const int tn = rovf ? 0 : ns;
+    const f32x2* se = reinterpret_cast<const f32x2*>(a.sent) + static_cast<size_t>(r) * (D / 2);
+    float dor[CPL];
+    load_cols<DT, CPL>(static_cast<const T*>(a.dout) + static_cast<size_t>(r) * D + l * CPL, dor);
+    float X[CPL], Y[CPL], sw = 0.f, swdp = 0.f;
+#pragma unroll
+    for (int d = 0; d < CPL; ++d) { X[d] = 0.f; Y[d] = 0.f; }
+    const int tmax = wave_max_int<kWave>(tn);
+#pragma unroll 1
+    for (int e0 = 0; e0 < tmax; e0 += NBS) {
+        int key[NBS];
+        float w[NBS];
+        RowSlice<DT, CPL> vr[NBS], kr[NBS];
+#pragma unroll
+        for (int j = 0; j < NBS; ++j) {
+            const bool in = e0 + j < tn;
+            const f32x2 en = se[in ? e0 + j : 0];
+            key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
+            w[j] = in ? en[0] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < NBS; ++j) {
+            vr[j].load(vh + static_cast<size_t>(key[j]) * D + l * CPL);
+            kr[j].load(kh + static_cast<size_t>(key[j]) * D + l * CPL);
+        }
+#pragma unroll
+        for (int j = 0; j < NBS; ++j) {
+            float part = 0.f;
+#pragma unroll
+            for (int d = 0; d < CPL; ++d) part = fmaf(dor[d], vr[j].at(d), part);
+            const float dp = group_sum<LPR>(part);
+            sw += w[j];
+            swdp = fmaf(w[j], dp, swdp);
+            const float wdp = w[j] * dp;
+#pragma unroll
+            for (int d = 0; d < CPL; ++d) {
+                X[d] = fmaf(wdp, kr[j].at(d), X[d]);
+                Y[d] = fmaf(w[j], kr[j].at(d), Y[d]);
+            }
+            // one lane of the row hands the entry to key j's bucket
+            if (l == (e0 + j) % LPR && w[j] > 0.f) {
+                const int slot = atomicAdd(kch + key[j], 1);
+                if (slot < D / 2) {
+                    float* dst = (slot < D / 4 ? dkb : dvb) + static_cast<size_t>(key[j]) * D + 4 * (slot % (D / 4));
+                    *reinterpret_cast<u32x4*>(dst) = u32x4{code, __float_as_uint(w[j]), __float_as_uint(wdp), 0u};
+                }
+            }
+        }
+    }
+    if (!valid) return;
+    float* ch = a.cbuf + static_cast<size_t>(bh) * L;
+    if (rovf) {
+        if (l == 0) {
+            reinterpret_cast<unsigned*>(ch)[row] = kCMarker;   // finished by the fix-up pass
+            *a.kflag = 1;                                     // its entries are in no bucket
+        }
+        return;
+    }
+    const float cc = sw > 0.f ? swdp / sw : 0.f;
+    float* dst = a.dq + static_cast<size_t>(r) * D + l * CPL;
+#pragma unroll
+    for (int d = 0; d < CPL; d += 4)
+        *reinterpret_cast<f32x4*>(dst + d) =
+            f32x4{a.scale * fmaf(-cc, Y[d], X[d]), a.scale * fmaf(-cc, Y[d + 1], X[d + 1]),
+                  a.scale * fmaf(-cc, Y[d + 2], X[d + 2]), a.scale * fmaf(-cc, Y[d + 3], X[d + 3])};
+    if (l == 0) ch[row] = cc;
 }
 
 // ============================================================================

@@ -183,7 +183,7 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
     typedef ea::WideCfg<DT, D> W;
     auto kq = ea::bwd_kernel<DT, D>;
     auto kw = ea::bwd_q_kernel<DT, D>;
-    auto ks = ea::bwd_q_kernel<DT, D, true>;
+
     auto kv = ea::bwd_kv_kernel<DT, D>;
     constexpr size_t lds_q = ea::BwdCfg<DT, D>::lds_bytes;
     int rc = set_lds(kq, lds_q);
@@ -201,10 +201,14 @@ int launch_bwd(ea::BwdArgs a, hipStream_t st) {
                            dim3(ea::kThreads), 0, st, reinterpret_cast<float*>(a.kcnt), nz);
         a.nqt = (L + W::BR - 1) / W::BR;
         a.fixup = 0;
-        if (a.scount != nullptr)   // the forward's saved support: no pass over the keys
-            hipLaunchKernelGGL(ks, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), 0, st, a);
-        else
+        if (a.scount != nullptr) {   // the forward's saved support: no pass over the keys
+            constexpr int rpb = ea::kThreads / (D / 8);   // rows per workgroup
+            const long long rows = static_cast<long long>(a.B) * a.H * L;
+            hipLaunchKernelGGL((ea::bwd_q_saved_kernel<DT, D>), dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)),
+                               dim3(ea::kThreads), 0, st, a);
+        } else {
             hipLaunchKernelGGL(kw, dim3(a.B * a.H * a.nqt), dim3(ea::kThreads), W::stream_lds_bytes, st, a);
+        }
         a.fixup = 1;
     } else {
         a.kcnt = nullptr;
