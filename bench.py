@@ -95,6 +95,16 @@ def algorithmic_bytes(w, key_mask):
     return q + 2 * kv_rows * row + o + tau + mask
 
 
+def saved_bwd_bytes(w, nnz):
+    """HBM bytes the backward on the saved support must move at least: Q, K,
+    V and dO read once, tau and the support (a count per row, 8 bytes per
+    entry) read, dQ, dK and dV written in fp32.  It forms no score, so it is
+    priced against HBM, not the MFMA peak."""
+    esz = 4 if w.dtype == "f32" else 2
+    rows = w.B * w.H * w.L
+    return 4 * rows * w.d * esz + 2 * rows * 4 + 8 * nnz + 3 * rows * w.d * 4
+
+
 def kernel_source_sha():
     """SHA-256 over the HIP sources; measured counters are tied to it."""
     import hashlib
@@ -376,17 +386,20 @@ def time_workload(name, steps, warmup, copy_gbs):
                            "launch_ms": fwd_ms}
     else:
         fwd_flop = 2.0 * w.d * pairs + 2.0 * w.d * nnz
-        bwd_flop = 2.0 * w.d * pairs + 8.0 * w.d * nnz
         fwd_roof = {"bound": "mfma", "kernel": "fwd", "achieved": fwd_flop / (fwd_ms * 1e-3) / 1e12,
                     "peak": peak, "unit": "TFLOP/s", "flop_per_launch": fwd_flop, "launch_ms": fwd_ms,
                     "launch_ms_median": fwd_med, "traffic": measured_traffic(name)}
         fwd_roof["frac"] = fwd_roof["achieved"] / peak
         res["roofline"] = fwd_roof
         if w.backward:
-            bwd_roof = {"bound": "mfma", "kernel": "bwd", "achieved": bwd_flop / (bwd_ms * 1e-3) / 1e12,
-                        "peak": peak, "unit": "TFLOP/s", "flop_per_launch": bwd_flop, "launch_ms": bwd_ms,
+            # the backward reads the forward's saved support: gathers of the
+            # kept entries' rows, no score recomputed, no MFMA
+            bwd_bytes = saved_bwd_bytes(w, nnz)
+            bwd_roof = {"bound": "hbm", "kernel": "bwd", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": bwd_bytes, "launch_ms": bwd_ms,
                         "launch_ms_median": bwd_med, "traffic": measured_traffic(name, "bwd")}
-            bwd_roof["frac"] = bwd_roof["achieved"] / peak
+            bwd_roof["frac"] = bwd_roof["achieved"] / HBM_PEAK_GBS
+            bwd_roof["frac_of_measured_copy"] = None if copy_gbs is None else bwd_roof["achieved"] / copy_gbs
             res["fwd_ms"], res["bwd_ms"] = fwd_ms, bwd_ms
             res["fwd_effective_tflops"] = FWD_EFF * w.d * pairs / (fwd_ms * 1e-3) / 1e12
             res["bwd_effective_tflops"] = BWD_EFF * w.d * pairs / (bwd_ms * 1e-3) / 1e12
@@ -437,7 +450,9 @@ def main_attention(args):
         "roofline": h["roofline"],
         "cpu_baseline": None if cpu is None else cpu[head],
         "flop_convention": {"effective_per_pair": {"fwd": f"{FWD_EFF} d", "bwd": f"{BWD_EFF} d"},
-                            "algorithmic": {"fwd": "2 d pairs + 2 d nnz", "bwd": "2 d pairs + 8 d nnz"}},
+                            "algorithmic": {"fwd": "2 d pairs + 2 d nnz",
+                                            "bwd": "bytes: Q, K, V, dO read, tau and the saved support read, "
+                                                   "dQ, dK, dV written (no score recomputed)"}},
         "measured_copy_gbs": copy_gbs,
     }
     for k in ("fwd_ms", "bwd_ms", "fwd_effective_tflops", "bwd_effective_tflops", "fwd_roofline", "bwd_roofline"):
