@@ -18,24 +18,25 @@
 //      the row's);
 //   3. every chunk: the scores again, the row maximum m, the allowed count,
 //      and every score above that bound into the row's candidate list: the
-//      row's own O row in memory, still unwritten, holds D/2 entries of
-//      (score, key); the row's four lanes take slots from a counter of the
-//      row in LDS (one LDS atomic per lane and tile with candidates), and
-//      lane g later reads back the slots g, g + 4, ...;
+//      lane keeps its first PL candidates (score, key) in LDS and the next
+//      D/8 - PL in the row's own O row in memory, still unwritten (slot
+//      4 k + g for the lane's k-th entry there): no counter is shared
+//      between lanes, and few stores to memory hold up the chunk loads;
 //   4. tau is the 25-step bisection result on [m - 2, m - 2/sqrt(n)], found
 //      as in the short-span kernel (exact root by Newton steps from the left
 //      and the closed form of Theorem 1 on the list entries above the bound
 //      from all of m and the lanes' maxima, then the centre of the dyadic
-//      cell that holds it; col_solve.hpp), and O_i = sum_j p_ij V_j over the
-//      list entries with s > tau, gathering V rows (sparse aggregation,
+//      cell that holds it; col_solve.hpp); the entries with s > tau go to
+//      a per-row list in LDS (the row's four lanes in order), and O_i =
+//      sum_j p_ij V_j over it, gathering V rows (sparse aggregation,
 //      "RoBERTa Base with AdaSplash Attention" model card, Architecture
 //      Overview).
 // Not a single pass: a pass must bound tau from the keys seen so far, and a
 // prefix of a row can have a far larger support than the whole row (a flat
 // top that a later, larger score dwarfs), so its lists would have to be much
 // longer; the sample of every other chunk bounds tau nearly as tightly as
-// the whole row.  A row with more than D/2 scores above its bound is
-// marked (kOMarker in O[row][0]); the long-span kernel
+// the whole row.  A row with more than D/8 scores above its bound in one
+// lane is marked (kOMarker in O[row][0]); the long-span kernel
 // (fwd_long.hpp) then recomputes the marked 64-row tiles in fix-up mode,
 // with S recomputed from the K tiles pass by pass.
 #pragma once
@@ -63,9 +64,12 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     constexpr int SUB = D / 8;     // list slots per lane: D/2 per row (8 bytes each in the row's O)
     constexpr int kSampleStep = 2; // the first pass reads every other chunk
     constexpr int NBO = 4;         // list entries gathered per batch
+    constexpr int PL = C::PL;      // candidates per lane in LDS
+    static_assert(PL < SUB, "the lists in memory take the rest");
     extern __shared__ float lds[];
     char* Kb = reinterpret_cast<char*>(lds);
-    int* rowcnt = reinterpret_cast<int*>(Kb + 2 * C::k_bytes);   // list length of each of the workgroup's rows
+    // the LDS candidates: entry k of lane group g of the workgroup's row r at [(4 k + g) BR + r]
+    f32x2* const cand = reinterpret_cast<f32x2*>(Kb + 2 * C::k_bytes);
 
     const int total = a.B * a.H * a.nqt;
     const int wi = xcd_swizzle(blockIdx.x, total);
@@ -111,14 +115,14 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     }
     float npop = 0.f;   // valid keys of the span (rows without a causal mask; uniform)
     const bool allrows = rbase + NF * 16 <= L;
-    // the list of row f: entries (score scaled, key bits) in the row's O,
-    // slots taken by the row's four lanes from the row's counter in LDS; lane
-    // g reads back the slots g, g + 4, ... (its share), the k-th at [4 k]
+    // the list of row f in memory: entries (score scaled, key bits) in the
+    // row's O; lane g of the row owns the slots g, g + 4, ..., its k-th
+    // entry there at [4 k]
     float* outh = a.out + head_off;
     auto lst = [&](int f, int lane_g) {
         return reinterpret_cast<f32x2*>(outh + static_cast<size_t>(clamp_row(rbase + 16 * f + c, L)) * D) + lane_g;
     };
-    int* const rc = rowcnt + wv * NF * 16 + c;   // row f's counter at rc[16 f]
+    int pc[NF];   // this lane's candidates of row f so far
 
     ChunkStream<DT, D, 2, 1> cs;
     cs.Kb = Kb;
@@ -208,8 +212,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
 
     // ---- 3. every chunk: scores, maxima, allowed counts and the candidate lists ------------
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-        if (g == 0) rc[16 * f] = 0;   // the wave's own counters: its later atomics follow in order
+    for (int f = 0; f < NF; ++f) pc[f] = 0;
     cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
         const int cb = chn * CK;
         npop += static_cast<float>(__popcll(M));
@@ -245,24 +248,21 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 if (!__any(tm[t] > thrr[f])) continue;   // uniform: no candidate in this tile
-                int k = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) k += s[f][t][i] > thrr[f] ? 1 : 0;
-                if (k > 0) {
-                    int slot = atomicAdd(rc + 16 * f, k);   // this lane's k slots at once
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (s[f][t][i] > thrr[f]) {
-                            if (slot < 4 * SUB) {
-                                // a 32-bit byte offset from the head's O (a head holds at most 2^32 bytes)
-                                const unsigned off = (static_cast<unsigned>(clamp_row(rbase + 16 * f + c, L)) * D + 2u * slot) * 4u;
-                                *reinterpret_cast<f32x2*>(reinterpret_cast<char*>(outh) + off) =
-                                    f32x2{s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
-                            }
-                            else
-                                ovf[f] = true;
-                            ++slot;
+                for (int i = 0; i < 4; ++i) {
+                    if (s[f][t][i] > thrr[f]) {
+                        const f32x2 en = {s[f][t][i] * scale, __uint_as_float(static_cast<unsigned>(cb + 16 * t + 4 * g + i))};
+                        if (pc[f] < PL) {
+                            cand[(4 * pc[f] + g) * C::BR + wv * NF * 16 + 16 * f + c] = en;
+                        } else if (pc[f] < SUB) {
+                            // slot 4 (pc - PL) + g; a 32-bit byte offset from the head's O (a head holds at most 2^32 bytes)
+                            const unsigned off = (static_cast<unsigned>(clamp_row(rbase + 16 * f + c, L)) * D +
+                                                  2u * static_cast<unsigned>(4 * (pc[f] - PL) + g)) * 4u;
+                            *reinterpret_cast<f32x2*>(reinterpret_cast<char*>(outh) + off) = en;
+                        } else {
+                            ovf[f] = true;
                         }
+                        ++pc[f];
                     }
                 }
             }
@@ -292,9 +292,14 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         const float lbx = fmaxf(col_lower_bound(xl), -1.f);
         lbs[f] = none ? -kInf : fmaf(2.f, lbx, ms);
     }
-    // the lists written by the row's four lanes are visible to all of them
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // the lists written by the row's four lanes are visible to all of them,
+    // and every wave is done with the K buffers, which take the support lists
+    __syncthreads();
+    // the support of the wave's row c of the fragment in hand: (y, key)
+    // entries, the row's four lanes in lane-group order, each in its list
+    // order
+    f32x2* const sup = reinterpret_cast<f32x2*>(Kb) + (wv * 16 + c) * (4 * SUB);
+    static_assert(4 * 16 * 4 * SUB * sizeof(f32x2) <= 2 * static_cast<size_t>(C::k_bytes), "support lists fit the K buffers");
 
     // ---- 4. tau, then O over the support, row by row ---------------------------------------
 #pragma unroll 1
@@ -313,64 +318,68 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         st.cnt = 0.f;
         st.a1 = 0.f;
         st.a2 = 0.f;
-        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // the row's list overflowed
-        const int nrow = min(rc[16 * f], 4 * SUB);
-        const int len = rovf ? 0 : max((nrow - g + 3) >> 2, 0);   // this lane's share: slots g, g + 4, ...
+        const bool rovf = col4_sum_int(ovf[f] ? 1 : 0) != 0;   // a lane of the row ran out of slots
+        const int len = rovf ? 0 : min(pc[f], SUB);             // this lane's entries: PL in LDS, then memory
         const f32x2* mine = lst(f, g);
+        const f32x2* minel = cand + g * C::BR + wv * NF * 16 + 16 * f + c;
         float sl[SUB];
+        unsigned kl[SUB];
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const float v = mine[4 * (k < len ? k : 0)][0];
-            sl[k] = k < len ? fmaf(v, 0.5f, -hs) : -kInf;
+            const f32x2 v = k < PL ? minel[4 * k * C::BR] : mine[4 * (k < len ? k - PL : 0)];
+            sl[k] = k < len ? fmaf(v[0], 0.5f, -hs) : -kInf;
+            kl[k] = __float_as_uint(v[1]);
         }
         const float ts = col_exact<SUB>(sl, st, SUB * 4 + 3);
         const float t = col_dyadic(st, ts);
-        // O = sum p V over the list entries above tau
+        // the support (p > 0) into the row's list in LDS: this lane's entries
+        // after those of the row's lane groups below g
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) cnt += (!empty && sl[k] - t > 0.f) ? 1 : 0;
+        int nsup;
+        int at = col4_scan_int(cnt, g, &nsup);
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) {
+            const float y = sl[k] - t;
+            if (!empty && y > 0.f) sup[at++] = f32x2{y, __uint_as_float(kl[k])};
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // O = sum p V over the support, NBO entries per batch of gathers
         float o[DQ];
 #pragma unroll
         for (int d = 0; d < DQ; ++d) o[d] = 0.f;
-        // the row's list in slot order, NBO entries per batch of gathers
-        const int nr = rovf ? 0 : nrow;
-        const int nmax = wave_max_int<kWave>(nr);
-        const f32x2* rl = lst(f, 0);
-        // the support, kept for the backward when asked: entries with p > 0
-        // in list order (the same in the row's four lanes; lane group 0 writes)
+        const int nmax = wave_max_int<kWave>(nsup);
+        // the support, kept for the backward when asked, in the same order
         const size_t srow = static_cast<size_t>(bh) * L + clamp_row(row, L);
         f32x2* se = a.sent != nullptr ? reinterpret_cast<f32x2*>(a.sent) + srow * (D / 2) : nullptr;
-        int ns = 0;
 #pragma unroll 1
         for (int e0 = 0; e0 < nmax; e0 += NBO) {
             int key[NBO];
-            float p[NBO], yv[NBO];
+            float p[NBO];
             RowSlice<DT, DQ> vr[NBO];
 #pragma unroll
             for (int j = 0; j < NBO; ++j) {
-                const bool in = e0 + j < nr;
-                const f32x2 en = rl[in ? e0 + j : 0];
-                const float y = fmaxf(fmaf(en[0], 0.5f, -hs) - t, 0.f);
-                p[j] = in && !empty ? y * y : 0.f;
-                yv[j] = y;
-                key[j] = (in && p[j] > 0.f) ? static_cast<int>(__float_as_uint(en[1])) : 0;
+                const bool in = e0 + j < nsup;
+                const f32x2 en = sup[in ? e0 + j : 0];
+                p[j] = in ? en[0] * en[0] : 0.f;
+                key[j] = in ? static_cast<int>(__float_as_uint(en[1])) : 0;
+                // lane group j % 4 keeps entry e0 + j
+                if (se != nullptr && in && g == (j & 3) && row < L) se[e0 + j] = en;
             }
 #pragma unroll
             for (int j = 0; j < NBO; ++j) vr[j].load(vh + static_cast<size_t>(key[j]) * D + g * DQ);
-            if (se != nullptr) {
-#pragma unroll
-                for (int j = 0; j < NBO; ++j) {
-                    if (p[j] > 0.f) {
-                        if (g == 0 && row < L) se[ns] = f32x2{yv[j], __uint_as_float(static_cast<unsigned>(key[j]))};
-                        ++ns;
-                    }
-                }
-            }
 #pragma unroll
             for (int j = 0; j < NBO; ++j)
 #pragma unroll
                 for (int d = 0; d < DQ; ++d) o[d] = fmaf(p[j], vr[j].at(d), o[d]);
         }
-        if (a.scount != nullptr && g == 0 && row < L) a.scount[srow] = rovf ? -1 : ns;   // -1: recomputed, not saved
-        // every lane of the wave has read the row's lists before any is overwritten
-        __builtin_amdgcn_wave_barrier();
+        if (a.scount != nullptr && g == 0 && row < L) a.scount[srow] = rovf ? -1 : nsup;   // -1: recomputed, not saved
+        // every lane of the wave has read the row's lists (in its O row and
+        // in LDS) before any is overwritten
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         if (row < L) {
             float* orow = outh + static_cast<size_t>(row) * D + g * DQ;
 #pragma unroll

@@ -30,8 +30,11 @@ struct WideCfg : ChunkCfg<DT, D> {
     // the kernels whose lists live in their output rows need the two
     // buffers only
     static constexpr size_t stream_lds_bytes = 2 * static_cast<size_t>(S::k_bytes);
-    // the forward adds one list counter per stationary row
-    static constexpr size_t fwd_lds_bytes = stream_lds_bytes + BR * sizeof(int);
+    // the forward keeps each lane's first PL candidates in LDS (8 bytes
+    // each) and the rest in the row's output row: stores to memory share the
+    // wait counter of the chunk loads, so every chunk would wait for them
+    static constexpr int PL = 5;
+    static constexpr size_t fwd_lds_bytes = stream_lds_bytes + static_cast<size_t>(BR) * 4 * PL * 8;
     // two bf16 workgroups per CU (the registers allow two waves per SIMD)
     static constexpr int kOcc = DT == DT_BF16 ? 2 : 1;
 };
