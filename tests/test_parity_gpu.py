@@ -188,6 +188,35 @@ def test_stream_overflow_fallback():
     check_forward(inp, label="stream overflow")
 
 
+def _one_lane_flat_top(seed):
+    """Rows of 2304 keys whose top is 576 near-equal scores, all on keys j
+    with j % 16 < 4: the keys a single lane of a row holds in the wide
+    forward, so that lane's list overflows while the row's other lanes hold
+    few candidates."""
+    inp = random_inputs(1, 1, 2304, 128, "bf16", seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1)
+    u = torch.randn(128, generator=gen)
+    u = u * (8.0 / u.norm())
+    q = (u + 0.3 * torch.randn(1, 1, 2304, 128, generator=gen)).to(torch.bfloat16)
+    k = inp["k"].float()
+    sel = (torch.arange(2304) % 16) < 4
+    k[:, :, sel] = u + 0.05 * torch.randn(1, 1, int(sel.sum()), 128, generator=gen)
+    return dict(inp, q=q, k=k.to(torch.bfloat16))
+
+
+def test_wide_one_lane_overflow():
+    from entmax_amd import entmax_attn_fwd_save
+    from tests.parity_util import to_gpu
+    inp = _one_lane_flat_top(41)
+    g = to_gpu(inp)
+    _, _, saved = entmax_attn_fwd_save(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    counts = saved[: 2304 * 4].view(torch.int32).cpu()
+    assert int((counts < 0).sum()) > 0, "no row took the overflow path"
+    check_forward(inp, rows=np.arange(0, 2304, 37), label="one-lane overflow")
+    check_backward(inp, label="one-lane overflow", saved=True)
+
+
 # ---- determinism and streams ----------------------------------------------------
 
 def test_forward_is_deterministic():
@@ -202,8 +231,8 @@ def test_forward_is_deterministic():
 
 @pytest.mark.parametrize("gain", [2.0, 0.4])
 def test_wide_forward_is_deterministic(gain):
-    # spans beyond 2048 keys: a row's lanes take list slots from a shared
-    # counter, in a fixed order; gain 0.4 also overflows lists (the fix-up)
+    # spans beyond 2048 keys: each lane of a row keeps its own candidates,
+    # in a fixed order; gain 0.4 also overflows lists (the fix-up)
     from entmax_amd import entmax_attn_fwd
     from tests.parity_util import to_gpu
     g = to_gpu(random_inputs(1, 2, 2304, 128, "bf16", seed=21, qk_gain=gain))
