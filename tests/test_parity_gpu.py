@@ -188,26 +188,27 @@ def test_stream_overflow_fallback():
     check_forward(inp, label="stream overflow")
 
 
-def _one_lane_flat_top(seed):
+def _one_lane_flat_top(seed, d):
     """Rows of 2304 keys whose top is 576 near-equal scores, all on keys j
     with j % 16 < 4: the keys a single lane of a row holds in the wide
     forward, so that lane's list overflows while the row's other lanes hold
     few candidates."""
-    inp = random_inputs(1, 1, 2304, 128, "bf16", seed=seed)
+    inp = random_inputs(1, 1, 2304, d, "bf16", seed=seed)
     gen = torch.Generator().manual_seed(seed + 1)
-    u = torch.randn(128, generator=gen)
+    u = torch.randn(d, generator=gen)
     u = u * (8.0 / u.norm())
-    q = (u + 0.3 * torch.randn(1, 1, 2304, 128, generator=gen)).to(torch.bfloat16)
+    q = (u + 0.3 * torch.randn(1, 1, 2304, d, generator=gen)).to(torch.bfloat16)
     k = inp["k"].float()
     sel = (torch.arange(2304) % 16) < 4
-    k[:, :, sel] = u + 0.05 * torch.randn(1, 1, int(sel.sum()), 128, generator=gen)
+    k[:, :, sel] = u + 0.05 * torch.randn(1, 1, int(sel.sum()), d, generator=gen)
     return dict(inp, q=q, k=k.to(torch.bfloat16))
 
 
-def test_wide_one_lane_overflow():
+@pytest.mark.parametrize("d", [64, 128])
+def test_wide_one_lane_overflow(d):
     from entmax_amd import entmax_attn_fwd_save
     from tests.parity_util import to_gpu
-    inp = _one_lane_flat_top(41)
+    inp = _one_lane_flat_top(41, d)
     g = to_gpu(inp)
     _, _, saved = entmax_attn_fwd_save(g["q"], g["k"], g["v"])
     torch.cuda.synchronize()
@@ -215,6 +216,30 @@ def test_wide_one_lane_overflow():
     assert int((counts < 0).sum()) > 0, "no row took the overflow path"
     check_forward(inp, rows=np.arange(0, 2304, 37), label="one-lane overflow")
     check_backward(inp, label="one-lane overflow", saved=True)
+
+
+def test_wide_lists_past_lds():
+    # a flat top of 40 near-equal scores on keys spread over a row's lanes:
+    # about ten candidates per lane, more than a lane keeps in LDS (the rest
+    # go to the row's output row) and fewer than its list holds (no fix-up)
+    from entmax_amd import entmax_attn_fwd_save
+    from tests.parity_util import to_gpu
+    inp = random_inputs(1, 1, 2304, 128, "bf16", seed=43)
+    gen = torch.Generator().manual_seed(44)
+    u = torch.randn(128, generator=gen)
+    u = u * (8.0 / u.norm())
+    q = (u + 0.3 * torch.randn(1, 1, 2304, 128, generator=gen)).to(torch.bfloat16)
+    k = inp["k"].float()
+    top = torch.randperm(2304, generator=gen)[:40]
+    k[:, :, top] = u + 0.05 * torch.randn(1, 1, 40, 128, generator=gen)
+    inp = dict(inp, q=q, k=k.to(torch.bfloat16))
+    g = to_gpu(inp)
+    _, _, saved = entmax_attn_fwd_save(g["q"], g["k"], g["v"])
+    torch.cuda.synchronize()
+    counts = saved[: 2304 * 4].view(torch.int32).cpu()
+    assert int((counts < 0).sum()) == 0 and int(counts.max()) > 20, (int(counts.min()), int(counts.max()))
+    check_forward(inp, rows=np.arange(0, 2304, 37), label="lists past LDS")
+    check_backward(inp, label="lists past LDS", saved=True)
 
 
 # ---- determinism and streams ----------------------------------------------------
