@@ -208,6 +208,9 @@ __global__ __launch_bounds__(kThreads) void dec_pv_kernel(DecArgs a) {
     for (int ct = 0; ct < NF; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
+        // a step whose four keys have p = 0 in every row of the group adds
+        // nothing: its V rows are not read (sparse rows leave most steps so)
+        if (!__any(p[s] > 0.f)) continue;   // uniform
         const int r = r0 + 16 * g + s;
         VRow<DT, D> vr;
         vr.load(vh + static_cast<size_t>(r < span ? lo + r : n - 1) * D, c);   // past the span: p = 0
