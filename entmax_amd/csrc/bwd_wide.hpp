@@ -317,8 +317,11 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void bwd_q_kernel
 // D/8 lanes per query row (8 columns each), 256/(D/8) rows per workgroup;
 // grid: ceil(B H L / rows per workgroup).  Entries are taken in the order
 // the forward kept them; per entry the row's lanes gather V_j and K_j.
+// bf16: five waves per SIMD (96 registers, a few bytes spilled) hide more
+// of the gather latency than four (110 registers): 424 -> 413 us on the
+// long-context backward; six spill heavily.
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void bwd_q_saved_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 5 : 1)) void bwd_q_saved_kernel(BwdArgs a) {
     typedef typename InT<DT>::type T;
     constexpr int LPR = D / 8;          // lanes per row
     constexpr int CPL = 8;              // columns per lane
