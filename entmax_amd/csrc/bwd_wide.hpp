@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads, (DT == DT_BF16 ? 5 : 1)) void bwd_q_saved
     typedef typename InT<DT>::type T;
     constexpr int LPR = D / 8;          // lanes per row
     constexpr int CPL = 8;              // columns per lane
-    constexpr int NBS = 4;              // entries gathered per batch
+    constexpr int NBS = 2;              // entries gathered per batch (long-context backward: 404 us at 2, 413 at 4; 8 spills)
     const int tid = threadIdx.x;
     const int l = tid % LPR;            // the lane's column group
     const long long rows = static_cast<long long>(a.B) * a.H * a.L;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_gather_kernel(BwdArgs a) {
     constexpr int FPL = 8;           // features per lane
     constexpr int EPL = KCAP / LPK;  // bucket slots per lane while ordering
     constexpr int KPB = kThreads / LPK;
-    constexpr int UB = 4;            // entries gathered per batch
+    constexpr int UB = 2;            // entries gathered per batch (59 registers at 2; 82 at 4, 32 us slower)
     __shared__ u32x4 srt[KPB][KCAP];
     if (*a.kflag != 0) return;       // uniform: the recompute kernel does every key
 
