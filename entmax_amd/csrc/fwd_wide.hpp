@@ -225,9 +225,9 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
         if (!MASKED || clean_chunk(cb, M)) {
             scores(std::true_type{}, cb, kb, M, s);
             if (a.causal) {
-                const float pc = g == 0 ? static_cast<float>(kWave) : 0.f;   // every key of the chunk allowed
+                const float nc = g == 0 ? static_cast<float>(kWave) : 0.f;   // every key of the chunk allowed
 #pragma unroll
-                for (int f = 0; f < NF; ++f) nl[f] += pc;
+                for (int f = 0; f < NF; ++f) nl[f] += nc;
             }
         } else {
             scores(std::false_type{}, cb, kb, M, s);
