@@ -157,9 +157,11 @@ def chain_rows_ok(s64, tau_gpu, tau_ref, alpha, ok=None, slope_err=1e-6):
     exceeds slope_err; at alpha = 2 (w an indicator) it is twice the error;
     never below 1e-6 max(1, |tau|), the float32 resolution of the scores."""
     s64 = np.atleast_2d(s64)
-    eps = np.abs(np.asarray(tau_gpu, np.float64) - np.asarray(tau_ref, np.float64))
-    fin = np.isfinite(tau_ref)
-    eps = np.where(fin, eps, 0.0)
+    tg = np.asarray(tau_gpu, np.float64)
+    tr = np.asarray(tau_ref, np.float64)
+    fin = np.isfinite(tr)
+    # rows with no allowed entry carry tau = +inf on both sides: no error there
+    eps = np.where(fin, np.abs(np.where(fin, tg, 0.0) - np.where(fin, tr, 0.0)), 0.0)
     if alpha <= 1.5:
         return np.ones(s64.shape[0], bool), np.zeros(s64.shape[0])
     k = (2.0 - alpha) / (alpha - 1.0)
