@@ -21,9 +21,9 @@
 //     itself it is nearly linear far from the root: one entry is solved in
 //     one step);
 //   * the start is a lower bound from subsets of the row (the root of a
-//     subset is at most the row's): the exact root over a wave's four lane
-//     maxima, raised by two Newton steps over its 32 pair maxima (each lane's
-//     maximum of every 128-key pair); the larger of the two halves' bounds;
+//     subset is at most the row's): the larger of the exact roots over each
+//     wave's four lane maxima, raised by two Newton steps over the row's 64
+//     pair maxima (each lane's maximum of every 128-key pair, both halves);
 //   * a row stops once its step is below 1e-5 (the error then is of the
 //     order of the step squared over the mean excess);
 //   * the 25-step bisection's final midpoint is the centre of the dyadic
@@ -270,28 +270,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     const bool empty = n == 0.f;
     const float mc2 = empty ? 0.f : mrow * c2;
     const float hi = -__builtin_amdgcn_rsqf(empty ? 1.f : n);
-    // A lower bound of the root from a subset of the row: the root over this
-    // wave's four lane maxima, then Newton steps (as below, from the left)
-    // over its 32 pair maxima, which stay at or below that subset's root;
-    // the larger of the two halves' bounds starts the rounds.
-    float lbw = fmaxf(col_lower_bound(fmaf(mlane, c2, -mc2)), -1.f);
+    // A lower bound of the root from a subset of the row: the larger of the
+    // two halves' roots over their four lane maxima (each at or below the
+    // root over the row's eight), then two Newton steps (as below, from the
+    // left) over the row's 64 pair maxima, the halves adding their sums
+    // through LDS; the iterates stay at or below that subset's root.  (Each
+    // half stepping on its own 32 maxima left one round more per row group
+    // in a float64 simulation of the long workload: 4.0 against 3.3.)
+    const float lbw = fmaxf(col_lower_bound(fmaf(mlane, c2, -mc2)), -1.f);
+    const f32x4 lp = exchange(f32x4{lbw, 0.f, 0.f, 0.f});
+    float t = fmaxf(lbw, lp[0]);   // the same in both halves
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int jj = 0; jj < NP; ++jj) {
-            const float y = relu1(fmaf(mpair[jj], c2, -(mc2 + lbw)));
+            const float y = relu1(fmaf(mpair[jj], c2, -(mc2 + t)));
             s1 += y;
             s2 = fmaf(y, y, s2);
         }
         s1 = col4_sum(s1);
         s2 = col4_sum(s2);
-        const float rg = __builtin_amdgcn_sqrtf(s2);
-        // s1 = 0 where this half holds nothing above the bound
-        lbw += s1 > 0.f ? fmaxf((rg - 1.f) * rg * __builtin_amdgcn_rcpf(s1), 0.f) : 0.f;
+        const f32x4 pq = exchange(f32x4{s1, s2, 0.f, 0.f});
+        const float S1 = s1 + pq[0], S2 = s2 + pq[1];   // addition commutes: both halves agree
+        const float rg = __builtin_amdgcn_sqrtf(S2);
+        // S1 = 0 where the row holds nothing above the bound
+        t += S1 > 0.f ? fmaxf((rg - 1.f) * rg * __builtin_amdgcn_rcpf(S1), 0.f) : 0.f;
     }
-    const f32x4 lp = exchange(f32x4{lbw, 0.f, 0.f, 0.f});
-    float t = fminf(fmaxf(lbw, lp[0]), hi);
+    t = fminf(t, hi);
     const bool trivial = empty || n <= 1.f;   // n = 1: the root is the lower end -1
     const int nt = 4 * (j1 - j0);             // tiles holding keys (uniform)
 
