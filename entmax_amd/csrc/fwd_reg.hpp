@@ -75,6 +75,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     typedef typename InT<DT>::type T;
     typedef RegCfg<DT, D> C;
     constexpr int PK = C::PK, NP = C::NP, NT = C::NT;
+    // register sets for K and V pairs in flight: two at d = 64 (the loads run
+    // two pairs ahead of the products); at d = 128 a second set would spill
+    constexpr int NS = D == 64 ? 2 : 1;
     extern __shared__ float lds[];
     char* buf = reinterpret_cast<char*>(lds);                                // 2 staging buffers
     f32x4* xch = reinterpret_cast<f32x4*>(buf + 2 * C::buf_bytes);          // row exchange
@@ -166,10 +169,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     float mlane = -kInf, nl = 0.f;
     float mpair[NP];   // this lane's maximum of each pair
     {
-        Pre pr;
-        prefetch(j0, kc, pr);
-        stage_k(0, pr);
-        unsigned long long M = bits(j0, pr);
+        // NS register sets: pairs are fetched NS ahead of the products
+        Pre pr[NS];
+        prefetch(j0, kc, pr[0]);
+        if (NS == 2 && j0 + 1 < j1) prefetch(j0 + 1, kc, pr[NS - 1]);
+        stage_k(0, pr[0]);
+        unsigned long long M = bits(j0, pr[0]);
         __syncthreads();
 #pragma unroll
         for (int jj = 0; jj < NP; ++jj) {
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
                 mpair[jj] = -kInf;
                 continue;
             }
-            if (jp + 1 < j1) prefetch(jp + 1, kc, pr);
+            if (jp + NS < j1) prefetch(jp + NS, kc, pr[jj % NS]);   // this set was staged last step
             const char* kb = buf + (jj & 1) * C::buf_bytes + (64 * hf + c) * C::KSTR + 16 * g;
             const int cb = jp * PK + 64 * hf;
             // a clean chunk (every key valid, no causal / window bound
@@ -231,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
             if (a.causal && M == ~0ull && !cross && allrows) nl += 16.f;   // four clean tiles: 16 keys of this lane
             if (!a.causal) nl += static_cast<float>(__popcll(M));
             if (jp + 1 < j1) {
-                stage_k((jj + 1) & 1, pr);
-                M = bits(jp + 1, pr);
+                stage_k((jj + 1) & 1, pr[(jj + 1) % NS]);
+                M = bits(jp + 1, pr[(jj + 1) % NS]);
             }
             __syncthreads();
         }
@@ -260,8 +265,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
 
     // ---- 2. the threshold ------------------------------------------------------------------
     // V of the first pair is fetched now; its latency passes under the rounds
-    Pre prv;
-    prefetch(j0, vc, prv);
+    Pre prv[NS];   // as for K, NS pairs ahead
+    prefetch(j0, vc, prv[0]);
+    if (NS == 2 && j0 + 1 < j1) prefetch(j0 + 1, vc, prv[NS - 1]);
     const float c2 = 0.5f * a.scale;
     const f32x4 mw = {col4_max(mlane), col4_sum(nl), 0.f, 0.f};
     const f32x4 mp = exchange(mw);
@@ -319,21 +325,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
         if (open && r < C::kRounds) {   // a wave whose rows are all done skips the pass (so does its partner)
             const float bias = -(mc2 + t);
             float u1 = 0.f, u2 = 0.f;   // two chains each
+            auto tile = [&](int k) {
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                if (k < nt) {   // uniform
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float y = relu1(fmaf(S[k][i], c2, bias));
-                        if (i & 1) {
-                            u1 += y;
-                            u2 = fmaf(y, y, u2);
-                        } else {
-                            s1 += y;
-                            s2 = fmaf(y, y, s2);
-                        }
+                for (int i = 0; i < 4; ++i) {
+                    const float y = relu1(fmaf(S[k][i], c2, bias));
+                    if (i & 1) {
+                        u1 += y;
+                        u2 = fmaf(y, y, u2);
+                    } else {
+                        s1 += y;
+                        s2 = fmaf(y, y, s2);
                     }
                 }
+            };
+            if (nt == NT) {   // uniform: every tile holds keys, one straight block
+#pragma unroll
+                for (int k = 0; k < NT; ++k) tile(k);
+            } else {
+                // tiles past the span hold -inf (y = 0): skipped, a pair at a time
+#pragma unroll
+                for (int k = 0; k < NT; k += 4)
+                    if (k < nt) {   // uniform
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) tile(k + kk);
+                    }
             }
             s1 = col4_sum(s1 + u1);
             s2 = col4_sum(s2 + u2);
@@ -366,24 +381,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        Pre& pr = prv;
-        stage_v(0, pr);
+        stage_v(0, prv[0]);
         __syncthreads();
 #pragma unroll
         for (int jj = 0; jj < NP; ++jj) {
             const int jp = j0 + jj;
             if (jp >= j1) continue;   // uniform
-            if (jp + 1 < j1) prefetch(jp + 1, vc, pr);
-            float y[4][4];
-            bool nz = false;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    y[t][i] = relu1(fmaf(S[4 * jj + t][i], c2, pb));
-                    nz |= y[t][i] > 0.f;
-                }
+            if (jp + NS < j1) prefetch(jp + NS, vc, prv[jj % NS]);   // this set was staged last step
+            // the lane's largest score of the pair decides whether any of its
+            // p is nonzero (fma with c2 > 0 is monotone in the score)
+            const bool nz = fmaf(mpair[jj], c2, pb) > 0.f;
             if (__any(nz)) {   // uniform over the wave
+                float y[4][4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[t][i] = relu1(fmaf(S[4 * jj + t][i], c2, pb));
                 const char* vb = buf + (jj & 1) * C::buf_bytes;
                 if constexpr (DT == DT_BF16) {
 #pragma unroll
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
                         }
                 }
             }
-            if (jp + 1 < j1) stage_v((jj + 1) & 1, pr);
+            if (jp + 1 < j1) stage_v((jj + 1) & 1, prv[(jj + 1) % NS]);
             __syncthreads();
         }
     }
