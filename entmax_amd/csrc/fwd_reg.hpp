@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     constexpr int PK = C::PK, NP = C::NP, NT = C::NT;
     // register sets for K and V pairs in flight: two at d = 64 (the loads run
     // two pairs ahead of the products); at d = 128 a second set would spill
-    constexpr int NS = D == 64 ? 2 : 1;
+    constexpr int NS = D == 64 ? (DT == DT_BF16 ? 3 : 2) : 1;
     extern __shared__ float lds[];
     char* buf = reinterpret_cast<char*>(lds);                                // 2 staging buffers
     f32x4* xch = reinterpret_cast<f32x4*>(buf + 2 * C::buf_bytes);          // row exchange
@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
         // NS register sets: pairs are fetched NS ahead of the products
         Pre pr[NS];
         prefetch(j0, kc, pr[0]);
-        if (NS == 2 && j0 + 1 < j1) prefetch(j0 + 1, kc, pr[NS - 1]);
+        if (NS >= 2 && j0 + 1 < j1) prefetch(j0 + 1, kc, pr[1 % NS]);
+        if (NS >= 3 && j0 + 2 < j1) prefetch(j0 + 2, kc, pr[2 % NS]);
         stage_k(0, pr[0]);
         unsigned long long M = bits(j0, pr[0]);
         __syncthreads();
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_reg_kernel(FwdArgs a) {
     // V of the first pair is fetched now; its latency passes under the rounds
     Pre prv[NS];   // as for K, NS pairs ahead
     prefetch(j0, vc, prv[0]);
-    if (NS == 2 && j0 + 1 < j1) prefetch(j0 + 1, vc, prv[NS - 1]);
+    if (NS >= 2 && j0 + 1 < j1) prefetch(j0 + 1, vc, prv[1 % NS]);
+    if (NS >= 3 && j0 + 2 < j1) prefetch(j0 + 2, vc, prv[2 % NS]);
     const float c2 = 0.5f * a.scale;
     const f32x4 mw = {col4_max(mlane), col4_sum(nl), 0.f, 0.f};
     const f32x4 mp = exchange(mw);
