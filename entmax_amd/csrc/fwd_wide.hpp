@@ -128,16 +128,23 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     };
     int pc[NF];   // this lane's candidates of row f so far
 
+    // pass 1 (every other chunk) fetches one chunk ahead; pass 2 (every
+    // chunk) two ahead, in two register sets
     ChunkStream<DT, D, 2, 1> cs;
-    cs.Kb = Kb;
-    cs.Vb = nullptr;
-    cs.kh = kh;
-    cs.vh = vh;
-    cs.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
-    cs.hasm = hasm;
-    cs.L = L;
-    cs.tid = tid;
-    cs.lane = lane;
+    ChunkStream<DT, D, 2, 2> cs2;
+    auto init_stream = [&](auto& st) {
+        st.Kb = Kb;
+        st.Vb = nullptr;
+        st.kh = kh;
+        st.vh = vh;
+        st.kmp = hasm ? km : reinterpret_cast<const uint8_t*>(qh);
+        st.hasm = hasm;
+        st.L = L;
+        st.tid = tid;
+        st.lane = lane;
+    };
+    init_stream(cs);
+    init_stream(cs2);
     constexpr unsigned kMaskedBits = DT == DT_BF16 ? 0xF149u : 0xF149F2CAu;   // -1e30
     const int klane = c * C::KSTR + 16 * g;
 
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
     // ---- 3. every chunk: scores, maxima, allowed counts and the candidate lists ------------
 #pragma unroll
     for (int f = 0; f < NF; ++f) pc[f] = 0;
-    cs.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
+    cs2.run(ch0, ch1, false, [&](int chn, const char* kb, const char*, unsigned long long M) {
         const int cb = chn * CK;
         npop += static_cast<float>(__popcll(M));
         if (cb >= whi || cb + CK <= wlo) return;   // uniform: none of the wave's keys
