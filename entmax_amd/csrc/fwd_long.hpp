@@ -76,13 +76,17 @@ __global__ __launch_bounds__(kThreads, (LongCfg<DT, D>::kOcc)) void fwd_long_ker
     const size_t head_off = static_cast<size_t>(bh) * L * D;
     if (a.fixup) {
         // fix-up mode: run only for a tile holding a row the wide kernel
-        // could not finish (kOMarker in O[row][0]), and then for all its rows
+        // could not finish (kOMarker in its tau word when tau is written,
+        // else in O[row][0]), and then for all its rows
         const int t = threadIdx.x;
         if (t == 0) *flag = 0;
         __syncthreads();
-        if (t < BM && q0 + t < L &&
-            reinterpret_cast<const unsigned*>(a.out)[head_off + static_cast<size_t>(q0 + t) * D] == kOMarker)
-            atomicOr(flag, 1);
+        if (t < BM && q0 + t < L) {
+            const unsigned mk = a.tau != nullptr
+                                    ? reinterpret_cast<const unsigned*>(a.tau)[static_cast<size_t>(bh) * L + q0 + t]
+                                    : reinterpret_cast<const unsigned*>(a.out)[head_off + static_cast<size_t>(q0 + t) * D];
+            if (mk == kOMarker) atomicOr(flag, 1);
+        }
         __syncthreads();
         const bool marked = *flag != 0;
         __syncthreads();

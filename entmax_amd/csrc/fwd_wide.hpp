@@ -36,7 +36,8 @@
 // top that a later, larger score dwarfs), so its lists would have to be much
 // longer; the sample of every other chunk bounds tau nearly as tightly as
 // the whole row.  A row with more than D/8 scores above its bound in one
-// lane is marked (kOMarker in O[row][0]); the long-span kernel
+// lane is marked (kOMarker in O[row][0], and in its tau word when tau is
+// written, so that the check reads tau rather than one O row per row); the long-span kernel
 // (fwd_long.hpp) then recomputes the marked 64-row tiles in fix-up mode,
 // with S recomputed from the K tiles pass by pass.
 #pragma once
@@ -396,7 +397,11 @@ __global__ __launch_bounds__(kThreads, (WideCfg<DT, D>::kOcc)) void fwd_wide_ker
 #pragma unroll
             for (int d = 0; d < DQ; d += 4) *reinterpret_cast<f32x4*>(orow + d) = f32x4{o[d], o[d + 1], o[d + 2], o[d + 3]};
             if (rovf && g == 0) reinterpret_cast<unsigned*>(orow)[0] = kOMarker;   // recomputed by the fix-up
-            if (a.tau != nullptr && g == 0) a.tau[static_cast<size_t>(bh) * L + row] = empty ? kInf : fmaf(2.f, t, ms);
+            // tau of a row left to the fix-up holds the marker too (bits, not a
+            // float value), so that the fix-up reads one word per row from tau
+            if (a.tau != nullptr && g == 0)
+                reinterpret_cast<unsigned*>(a.tau)[static_cast<size_t>(bh) * L + row] =
+                    rovf ? kOMarker : __float_as_uint(empty ? kInf : fmaf(2.f, t, ms));
         }
     }
 }
